@@ -1,0 +1,149 @@
+/*
+ * ld.h - C ABI of libld.so: the small-batch decode step of a dense
+ * Llama-style decoder on one MI355X (gfx950), with stages that hand work to
+ * each other through per-tile readiness counters instead of whole-kernel
+ * waits.
+ *
+ * What the step computes (per sequence): embedding row; per layer RMSNorm,
+ * the Q/K/V projection with rotary position embedding and K/V append,
+ * grouped-query attention over the cache, the output projection with
+ * residual, RMSNorm, the fused SwiGLU first stage and the Down projection
+ * with residual; then the final RMSNorm, the LM head (fp32 logits) and a
+ * greedy argmax.  The workload is batch-1 Llama-3.2-1B decode, which is
+ * memory-bound (Hazy Research, "Look Ma, No Bubbles! Designing a
+ * Low-Latency Megakernel for Llama-1B", introduction); the MLP is split into
+ * a fused Up/Gate/SiLU/product stage and a separate Down projection ("Deep
+ * Kernel Fusion for Transformers", Key points, "Fusion scope").
+ *
+ * Execution modes (all share the same stage code and give bitwise-equal
+ * results):
+ *   LD_MODE_WAIT  - one kernel per stage on one stream; each kernel starts
+ *                   when the previous one has finished (the conventional
+ *                   whole-kernel wait of the MegaOps summary, "In plain
+ *                   words").
+ *   LD_MODE_FLAGS - the same kernels on two alternating streams; a consumer's
+ *                   workgroups start as soon as the tiles they read are
+ *                   signalled ready (MegaOps summary, "Keep kernels
+ *                   separate"; multi-streaming and prefetch, "What the
+ *                   control can show").
+ *   LD_MODE_MEGA  - one persistent cooperative kernel per step whose
+ *                   workgroups walk the stages in order, synchronising on the
+ *                   same counters (the megakernel of the Hazy post).
+ *
+ * Conventions.
+ *  - Every pointer documented "dev" is device memory on the current HIP
+ *    device; "host" is host memory.  `stream` is a hipStream_t (NULL = the
+ *    legacy default stream), passed as void* so this header needs no HIP
+ *    include.
+ *  - Buffers handed in belong to the caller and must outlive the model; the
+ *    library frees only memory it allocated itself.
+ *  - Host-visible argument errors return LD_EINVAL before anything is
+ *    enqueued; ld_last_error() describes the latest error of a model.
+ *  - ld_decode_step does no host synchronisation: it is asynchronous on
+ *    `stream`.  Device-side input errors (token outside [0, vocab), position
+ *    outside [0, max_seq)) and watchdog timeouts set a device error word and
+ *    the step completes with unspecified outputs; read the word with
+ *    ld_device_error().
+ *  - A model is not thread-safe; use one model per host thread.
+ */
+#ifndef LD_H
+#define LD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ld_model ld_model;
+
+typedef enum {
+  LD_OK = 0,
+  LD_EINVAL = -1,   /* bad argument (host-side check) */
+  LD_ENOMEM = -2,   /* allocation failed or caller buffer too small */
+  LD_EHIP = -3,     /* a HIP runtime call failed */
+  LD_ETIMEOUT = -4, /* a device-side wait exceeded the watchdog */
+  LD_ESTATE = -5,   /* call out of order (e.g. decode before ld_alloc_kv) */
+  LD_EDEVICE = -6   /* device input error (bad token or position) */
+} ld_status;
+
+typedef enum { LD_MODE_WAIT = 0, LD_MODE_FLAGS = 1, LD_MODE_MEGA = 2 } ld_mode;
+
+/* Model shape.  Weights are bf16 row-major [out, in]; norm gains bf16. */
+typedef struct {
+  int32_t n_layers, hidden, n_q_heads, n_kv_heads, head_dim, intermediate, vocab, tied;
+  float rms_eps, rope_theta;
+} ld_config;
+
+/* Bytes of the weight arena for `cfg` (0 if the shape is unsupported).
+ * Requirements: hidden, intermediate and n_q_heads*head_dim multiples of 8;
+ * head_dim even and <= 256; n_q_heads a multiple of n_kv_heads. */
+size_t ld_weights_bytes(const ld_config* cfg);
+
+/* Create a model and fill its weights on the device from the seeded
+ * generator: matrices ~N(0, w_std) (Irwin-Hall(4) approximation, keyed by
+ * (seed, tensor, logical index)), norm gains 1.0.  dev_buf: dev arena of at
+ * least ld_weights_bytes(cfg) bytes, or NULL to let the library allocate it.
+ * Work is enqueued on `stream`; *out is valid on return. */
+ld_status ld_init_weights(ld_model** out, const ld_config* cfg, void* dev_buf, size_t bytes,
+                          uint64_t seed, float w_std, void* stream);
+
+/* Bytes of the KV-cache + workspace arena for max_batch sequences of up to
+ * max_seq positions each. */
+size_t ld_kv_bytes(const ld_config* cfg, int32_t max_batch, int32_t max_seq);
+
+/* Carve the bf16 KV cache [layer][seq][kv_head][pos][head_dim], the fp32
+ * workspaces and the readiness counters; zero the counters and the device
+ * error word.  dev_buf: dev arena of >= ld_kv_bytes() bytes or NULL.
+ * Synchronous. */
+ld_status ld_alloc_kv(ld_model* m, void* dev_buf, size_t bytes, int32_t max_batch,
+                      int32_t max_seq);
+
+/* Fill positions [0, prefill_len[b]) of every (layer, seq b, kv head) with
+ * seeded ~N(0, kv_std) bf16 values (treated as already-rotated keys).
+ * prefill_len: host [max_batch]. */
+ld_status ld_fill_kv(ld_model* m, uint64_t seed, float kv_std, const int32_t* prefill_len,
+                     void* stream);
+
+ld_status ld_set_mode(ld_model* m, ld_mode mode);
+
+/* One decode step for `batch` sequences (1 <= batch <= max_batch).
+ *   tokens      dev int32 [batch]: input token of each sequence
+ *   positions   dev int32 [batch]: slot the new K/V is written to (= tokens
+ *               already in the cache); attention covers 0..positions[b]
+ *   logits      dev fp32 [batch, vocab] (out)
+ *   next_tokens dev int32 [batch] greedy argmax, lowest index on ties (out,
+ *               may be NULL)
+ * The KV cache of slot positions[b] is overwritten. */
+ld_status ld_decode_step(ld_model* m, const int32_t* tokens, int32_t batch,
+                         const int32_t* positions, float* logits, int32_t* next_tokens,
+                         void* stream);
+
+/* Offline choice of the SwiGLU tiling ("Deep Kernel Fusion for Transformers",
+ * Summary: a profiler benchmarks the tiling variants on the target before
+ * inference and keeps the fastest; Key points: no runtime dispatch cost).
+ * Times the row-major and column-major variants for each batch size in
+ * batches[0..n) (each <= max_batch) and records the faster in the model's
+ * table; writes the table as JSON to table_path unless NULL.  Synchronous;
+ * needs ld_alloc_kv.  Overwrites workspace contents (not the KV cache). */
+ld_status ld_tune(ld_model* m, const int32_t* batches, int32_t n, const char* table_path);
+
+/* Load a table written by ld_tune (same shape required). */
+ld_status ld_load_tuning(ld_model* m, const char* table_path);
+
+/* Synchronise the device, return LD_OK / LD_ETIMEOUT / LD_EDEVICE from the
+ * device error word, and clear it. */
+ld_status ld_device_error(ld_model* m);
+
+/* Message of the latest error on `m` (or of the latest failed
+ * ld_init_weights when m is NULL). Never NULL. */
+const char* ld_last_error(const ld_model* m);
+
+/* Free the model and any memory the library allocated. */
+void ld_free(ld_model* m);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -252,7 +252,12 @@ uint16_t* lo_kv_v(lo_kv* kv, int layer, int seq, int h) {
 }
 
 int lo_kv_synth(lo_kv* kv, uint64_t seed, float kv_std, const int32_t* prefill_len) {
-  if (!kv || !prefill_len) return -1;
+  return lo_kv_synth_from(kv, seed, kv_std, prefill_len, 0);
+}
+
+int lo_kv_synth_from(lo_kv* kv, uint64_t seed, float kv_std, const int32_t* prefill_len,
+                     int32_t seq0) {
+  if (!kv || !prefill_len || seq0 < 0) return -1;
   const lo_config* c = &kv->cfg;
   const float kappa = ls_kappa(kv_std);
   const int d = c->head_dim;
@@ -267,7 +272,7 @@ int lo_kv_synth(lo_kv* kv, uint64_t seed, float kv_std, const int32_t* prefill_l
         uint16_t* V = lo_kv_v(kv, l, b, h);
         for (int p = 0; p < prefill_len[b]; ++p)
           for (int i = 0; i < d; ++i) {
-            const uint64_t idx = ls_kv_index((uint64_t)b, (uint64_t)c->n_kv_heads, (uint64_t)h,
+            const uint64_t idx = ls_kv_index((uint64_t)(b + seq0), (uint64_t)c->n_kv_heads, (uint64_t)h,
                                              (uint64_t)p, (uint64_t)d, (uint64_t)i);
             K[(size_t)p * d + i] = ls_normal_bf16(kk, idx, kappa);
             V[(size_t)p * d + i] = ls_normal_bf16(kvk, idx, kappa);
@@ -377,16 +382,12 @@ static void copy_real(lo_real* dst, const lo_real* src, int64_t n) {
   if (dst) memcpy(dst, src, (size_t)n * sizeof(lo_real));
 }
 
-int lo_decode_step(const lo_model* m, lo_kv* kv, const int32_t* tokens, int32_t B,
-                   const int32_t* pos, float* logits, int32_t* next, lo_trace* trace) {
-  if (!m || !kv || !tokens || !pos || !logits || B < 1 || B > kv->max_batch) return -1;
+/* One sequence: the whole layer stack and the LM head for cache slot b. */
+static int decode_seq(const lo_model* m, lo_kv* kv, int32_t b, int32_t tok, int32_t p,
+                      float* logits_b, int32_t* next_b, lo_trace* trace) {
   const lo_config* c = &m->cfg;
-  if (memcmp(c, &kv->cfg, sizeof(lo_config)) != 0) return -1;
   const int32_t H = c->hidden, d = c->head_dim, nq = c->n_q_heads, nkv = c->n_kv_heads;
   const int32_t I = c->intermediate, V = c->vocab, group = nq / nkv;
-  for (int32_t b = 0; b < B; ++b)
-    if (tokens[b] < 0 || tokens[b] >= V || pos[b] < 0 || pos[b] >= kv->max_seq) return -1;
-
   const int64_t nbuf = (int64_t)H + 2 * (int64_t)nq * d + 2 * (int64_t)nkv * d + I + V + H + H;
   lo_real* buf = (lo_real*)malloc((size_t)nbuf * sizeof(lo_real));
   if (!buf) return -1;
@@ -400,60 +401,80 @@ int lo_decode_step(const lo_model* m, lo_kv* kv, const int32_t* tokens, int32_t 
   lo_real* lg = hh + I;
   lo_real* tmp = lg + V;
 
-  for (int32_t b = 0; b < B; ++b) {
-    const int32_t tok = tokens[b], p = pos[b];
-    /* embedding row, widened */
-    for (int32_t j = 0; j < H; ++j) x[j] = (lo_real)lo_bf16_widen(m->embed[(int64_t)tok * H + j]);
+  /* embedding row, widened */
+  for (int32_t j = 0; j < H; ++j) x[j] = (lo_real)lo_bf16_widen(m->embed[(int64_t)tok * H + j]);
 
-    for (int32_t l = 0; l < c->n_layers; ++l) {
-      const lo_layer* L = &m->layers[l];
-      const int tr = trace && trace->seq == b && trace->layer == l;
-      /* attention block: x += Wo . attn(rope(Wq n(x)), cache + rope(Wk n(x)), cache + Wv n(x)) */
-      lo_rmsnorm(x, L->attn_norm, H, c->rms_eps, xn);
-      if (tr) copy_real(trace->xn, xn, H);
-      lo_matvec(L->wq, (int64_t)nq * d, H, xn, q);
-      lo_matvec(L->wk, (int64_t)nkv * d, H, xn, k);
-      lo_matvec(L->wv, (int64_t)nkv * d, H, xn, v);
-      for (int32_t hq = 0; hq < nq; ++hq) lo_rope(q + (int64_t)hq * d, d, p, c->rope_theta);
-      for (int32_t hk = 0; hk < nkv; ++hk) lo_rope(k + (int64_t)hk * d, d, p, c->rope_theta);
-      if (tr) {
-        copy_real(trace->q, q, (int64_t)nq * d);
-        copy_real(trace->k, k, (int64_t)nkv * d);
-        copy_real(trace->v, v, (int64_t)nkv * d);
-      }
-      for (int32_t hk = 0; hk < nkv; ++hk) {
-        uint16_t* Kc = lo_kv_k(kv, l, b, hk);
-        uint16_t* Vc = lo_kv_v(kv, l, b, hk);
-        for (int32_t i = 0; i < d; ++i) {
-          Kc[(size_t)p * d + i] = lo_bf16_round((float)k[(int64_t)hk * d + i]);
-          Vc[(size_t)p * d + i] = lo_bf16_round((float)v[(int64_t)hk * d + i]);
-        }
-      }
-      for (int32_t hq = 0; hq < nq; ++hq) {
-        const int32_t hk = hq / group;
-        lo_attention_head(q + (int64_t)hq * d, lo_kv_k(kv, l, b, hk), lo_kv_v(kv, l, b, hk), p + 1,
-                          d, o + (int64_t)hq * d);
-      }
-      if (tr) copy_real(trace->o, o, (int64_t)nq * d);
-      lo_matvec(L->wo, H, (int64_t)nq * d, o, tmp);
-      for (int32_t j = 0; j < H; ++j) x[j] = x[j] + tmp[j];
-      if (tr) copy_real(trace->x_attn, x, H);
-
-      /* MLP block: x += Wd . (silu(Wg n(x)) * (Wu n(x))) */
-      lo_rmsnorm(x, L->mlp_norm, H, c->rms_eps, xn);
-      if (tr) copy_real(trace->xn2, xn, H);
-      lo_swiglu(L->wg, L->wu, I, H, xn, hh);
-      if (tr) copy_real(trace->hh, hh, I);
-      lo_matvec(L->wd, H, I, hh, tmp);
-      for (int32_t j = 0; j < H; ++j) x[j] = x[j] + tmp[j];
-      if (tr) copy_real(trace->x_out, x, H);
+  for (int32_t l = 0; l < c->n_layers; ++l) {
+    const lo_layer* L = &m->layers[l];
+    const int tr = trace && trace->seq == b && trace->layer == l;
+    /* attention block: x += Wo . attn(rope(Wq n(x)), cache + rope(Wk n(x)), cache + Wv n(x)) */
+    lo_rmsnorm(x, L->attn_norm, H, c->rms_eps, xn);
+    if (tr) copy_real(trace->xn, xn, H);
+    lo_matvec(L->wq, (int64_t)nq * d, H, xn, q);
+    lo_matvec(L->wk, (int64_t)nkv * d, H, xn, k);
+    lo_matvec(L->wv, (int64_t)nkv * d, H, xn, v);
+    for (int32_t hq = 0; hq < nq; ++hq) lo_rope(q + (int64_t)hq * d, d, p, c->rope_theta);
+    for (int32_t hk = 0; hk < nkv; ++hk) lo_rope(k + (int64_t)hk * d, d, p, c->rope_theta);
+    if (tr) {
+      copy_real(trace->q, q, (int64_t)nq * d);
+      copy_real(trace->k, k, (int64_t)nkv * d);
+      copy_real(trace->v, v, (int64_t)nkv * d);
     }
+    for (int32_t hk = 0; hk < nkv; ++hk) {
+      uint16_t* Kc = lo_kv_k(kv, l, b, hk);
+      uint16_t* Vc = lo_kv_v(kv, l, b, hk);
+      for (int32_t i = 0; i < d; ++i) {
+        Kc[(size_t)p * d + i] = lo_bf16_round((float)k[(int64_t)hk * d + i]);
+        Vc[(size_t)p * d + i] = lo_bf16_round((float)v[(int64_t)hk * d + i]);
+      }
+    }
+    for (int32_t hq = 0; hq < nq; ++hq) {
+      const int32_t hk = hq / group;
+      lo_attention_head(q + (int64_t)hq * d, lo_kv_k(kv, l, b, hk), lo_kv_v(kv, l, b, hk), p + 1,
+                        d, o + (int64_t)hq * d);
+    }
+    if (tr) copy_real(trace->o, o, (int64_t)nq * d);
+    lo_matvec(L->wo, H, (int64_t)nq * d, o, tmp);
+    for (int32_t j = 0; j < H; ++j) x[j] = x[j] + tmp[j];
+    if (tr) copy_real(trace->x_attn, x, H);
 
-    lo_rmsnorm(x, m->final_norm, H, c->rms_eps, xn);
-    lo_matvec(m->lm_head, V, H, xn, lg);
-    for (int32_t vv = 0; vv < V; ++vv) logits[(int64_t)b * V + vv] = (float)lg[vv];
-    if (next) next[b] = lo_argmax(lg, V);
+    /* MLP block: x += Wd . (silu(Wg n(x)) * (Wu n(x))) */
+    lo_rmsnorm(x, L->mlp_norm, H, c->rms_eps, xn);
+    if (tr) copy_real(trace->xn2, xn, H);
+    lo_swiglu(L->wg, L->wu, I, H, xn, hh);
+    if (tr) copy_real(trace->hh, hh, I);
+    lo_matvec(L->wd, H, I, hh, tmp);
+    for (int32_t j = 0; j < H; ++j) x[j] = x[j] + tmp[j];
+    if (tr) copy_real(trace->x_out, x, H);
   }
+
+  lo_rmsnorm(x, m->final_norm, H, c->rms_eps, xn);
+  lo_matvec(m->lm_head, V, H, xn, lg);
+  for (int32_t vv = 0; vv < V; ++vv) logits_b[vv] = (float)lg[vv];
+  if (next_b) *next_b = lo_argmax(lg, V);
   free(buf);
   return 0;
+}
+
+int lo_decode_step(const lo_model* m, lo_kv* kv, const int32_t* tokens, int32_t B,
+                   const int32_t* pos, float* logits, int32_t* next, lo_trace* trace) {
+  if (!m || !kv || !tokens || !pos || !logits || B < 1 || B > kv->max_batch) return -1;
+  const lo_config* c = &m->cfg;
+  if (memcmp(c, &kv->cfg, sizeof(lo_config)) != 0) return -1;
+  for (int32_t b = 0; b < B; ++b)
+    if (tokens[b] < 0 || tokens[b] >= c->vocab || pos[b] < 0 || pos[b] >= kv->max_seq) return -1;
+  for (int32_t b = 0; b < B; ++b)
+    if (decode_seq(m, kv, b, tokens[b], pos[b], logits + (int64_t)b * c->vocab,
+                   next ? next + b : NULL, trace) != 0)
+      return -1;
+  return 0;
+}
+
+int lo_decode_one(const lo_model* m, lo_kv* kv, int32_t seq, int32_t token, int32_t pos,
+                  float* logits, int32_t* next) {
+  if (!m || !kv || !logits || seq < 0 || seq >= kv->max_batch) return -1;
+  const lo_config* c = &m->cfg;
+  if (memcmp(c, &kv->cfg, sizeof(lo_config)) != 0) return -1;
+  if (token < 0 || token >= c->vocab || pos < 0 || pos >= kv->max_seq) return -1;
+  return decode_seq(m, kv, seq, token, pos, logits, next, NULL);
 }

@@ -88,6 +88,10 @@ void lo_kv_free(lo_kv* kv);
 /* Positions 0..prefill_len[b]-1 of every (layer, seq, kv head) from the
  * seeded generator, ~N(0, kv_std). */
 int lo_kv_synth(lo_kv* kv, uint64_t seed, float kv_std, const int32_t* prefill_len);
+/* As lo_kv_synth, but cache slot s holds logical sequence seq0 + s (so a
+ * small cache can stand for chosen sequences of a large batch). */
+int lo_kv_synth_from(lo_kv* kv, uint64_t seed, float kv_std, const int32_t* prefill_len,
+                     int32_t seq0);
 uint16_t* lo_kv_k(lo_kv* kv, int layer, int seq, int kv_head); /* [max_seq][d] */
 uint16_t* lo_kv_v(lo_kv* kv, int layer, int seq, int kv_head);
 
@@ -124,6 +128,11 @@ typedef struct {
  * trace may be NULL.  Returns 0, or -1 on bad arguments. */
 int lo_decode_step(const lo_model* m, lo_kv* kv, const int32_t* tokens, int32_t B,
                    const int32_t* pos, float* logits, int32_t* next, lo_trace* trace);
+
+/* One sequence only: cache slot `seq` decodes `token` at position `pos`.
+ * logits [vocab]; next may be NULL. */
+int lo_decode_one(const lo_model* m, lo_kv* kv, int32_t seq, int32_t token, int32_t pos,
+                  float* logits, int32_t* next);
 
 /* Bytes of lo_real in this build (4 or 8), so callers can tell the builds apart. */
 int32_t lo_real_bytes(void);

@@ -56,6 +56,8 @@ def _load(kind):
         "lo_kv_create": (P, [ctypes.POINTER(LoConfig), I32, I32]),
         "lo_kv_free": (None, [P]),
         "lo_kv_synth": (ctypes.c_int, [P, U64, F, P]),
+        "lo_kv_synth_from": (ctypes.c_int, [P, U64, F, P, I32]),
+        "lo_decode_one": (ctypes.c_int, [P, P, I32, I32, I32, P, P]),
         "lo_kv_k": (P, [P, ctypes.c_int, ctypes.c_int, ctypes.c_int]),
         "lo_kv_v": (P, [P, ctypes.c_int, ctypes.c_int, ctypes.c_int]),
         "lo_silu": (R, [R]),
@@ -156,8 +158,18 @@ class Oracle:
     def model(self, shape, seed=None, w_std=0.02):
         return OracleModel(self, shape, seed, w_std)
 
-    def kv(self, shape, max_batch, max_seq, seed=None, kv_std=1.0, prefill=None):
-        return OracleKV(self, shape, max_batch, max_seq, seed, kv_std, prefill)
+    def kv(self, shape, max_batch, max_seq, seed=None, kv_std=1.0, prefill=None, seq0=0):
+        return OracleKV(self, shape, max_batch, max_seq, seed, kv_std, prefill, seq0)
+
+    def decode_one(self, model, kv, seq, token, pos):
+        """Decode one cache slot only; returns (logits [vocab] float32, next token)."""
+        logits = np.empty(model.shape["vocab"], dtype=np.float32)
+        nxt = np.empty(1, dtype=np.int32)
+        rc = self.lib.lo_decode_one(model.h, kv.h, seq, int(token), int(pos), _ptr(logits),
+                                    _ptr(nxt))
+        if rc != 0:
+            raise ValueError("lo_decode_one rejected its arguments")
+        return logits, int(nxt[0])
 
     def decode_step(self, model, kv, tokens, pos, trace=None):
         tokens = np.ascontiguousarray(tokens, dtype=np.int32)
@@ -217,7 +229,7 @@ class OracleModel:
 
 
 class OracleKV:
-    def __init__(self, orc, shape, max_batch, max_seq, seed, kv_std, prefill):
+    def __init__(self, orc, shape, max_batch, max_seq, seed, kv_std, prefill, seq0=0):
         self.orc, self.shape = orc, dict(shape)
         self.max_batch, self.max_seq = max_batch, max_seq
         self.cfg = make_config(shape)
@@ -227,7 +239,7 @@ class OracleKV:
         if seed is not None:
             pf = np.ascontiguousarray(prefill, dtype=np.int32)
             assert pf.size == max_batch
-            if orc.lib.lo_kv_synth(self.h, seed, kv_std, _ptr(pf)) != 0:
+            if orc.lib.lo_kv_synth_from(self.h, seed, kv_std, _ptr(pf), seq0) != 0:
                 raise ValueError("lo_kv_synth rejected prefill lengths")
 
     def _view(self, fn, layer, seq, head):

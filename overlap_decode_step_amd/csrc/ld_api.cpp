@@ -1,0 +1,780 @@
+// ld_api.cpp - host runtime behind the C ABI of include/ld.h: arena
+// layout, argument validation, cumulative readiness-counter targets, the
+// three launch schedules (whole-kernel wait, tile flags on two streams, one
+// persistent kernel) and the offline SwiGLU tiling choice.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/ld.h"
+#include "../../include/ld_ops.h"
+#include "../../synth/ld_synth.h"
+#include "ld_launch.h"
+#include "ld_params.hpp"
+
+using namespace ld;
+
+struct ld_model {
+  ld_config cfg{};
+  Dims D{};
+  Weights W{};
+  Work K{};
+  void* warena = nullptr;
+  bool own_w = false;
+  size_t wbytes = 0;
+  void* karena = nullptr;
+  bool own_k = false;
+  size_t kbytes = 0;
+  bool kv_ready = false;
+  ld_mode mode = LD_MODE_MEGA;
+  int device = 0;
+  int n_cu = 0;
+  hipStream_t s1 = nullptr;
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+  // cumulative counter totals (what every layer's counter will read once all
+  // enqueued steps have finished)
+  uint32_t tot_qkv = 0, tot_attn = 0, tot_o = 0, tot_gu = 0, tot_d = 0, tot_lm = 0;
+  int gu_variant[65];
+  bool gu_tuned[65];
+  int grid_wait = 0, grid_flags = 0, grid_mega[9] = {0};  // grid_mega indexed by nb
+  int grid_attn_flags = 0;
+  size_t smem_attn = 0, smem_mega = 0;
+  uint64_t watchdog_ticks = 0;
+  double wall_khz = 100000.0;
+  uint32_t inject_next = 0;
+  uint32_t* tune_ctr = nullptr;  // counter slots for standalone tuning launches
+  std::string err;
+};
+
+static std::string g_err;
+
+static ld_status fail(ld_model* m, ld_status st, const std::string& msg) {
+  if (m)
+    m->err = msg;
+  else
+    g_err = msg;
+  return st;
+}
+
+#define HIPCHK(m, call)                                                                   \
+  do {                                                                                    \
+    hipError_t e_ = (call);                                                               \
+    if (e_ != hipSuccess)                                                                 \
+      return fail((m), LD_EHIP, std::string(#call) + ": " + hipGetErrorString(e_));       \
+  } while (0)
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static bool cfg_ok(const ld_config* c, std::string* why) {
+  if (!c) {
+    *why = "null config";
+    return false;
+  }
+  if (c->n_layers < 1 || c->hidden < 8 || c->n_q_heads < 1 || c->n_kv_heads < 1 ||
+      c->head_dim < 2 || c->intermediate < 8 || c->vocab < 1) {
+    *why = "non-positive dimension";
+    return false;
+  }
+  if (c->hidden % 8 || c->intermediate % 8 || (c->n_q_heads * c->head_dim) % 8) {
+    *why = "hidden, intermediate and n_q_heads*head_dim must be multiples of 8";
+    return false;
+  }
+  if (c->head_dim % 8 || c->head_dim > 256) {
+    *why = "head_dim must be a multiple of 8 and at most 256";
+    return false;
+  }
+  if (c->n_q_heads % c->n_kv_heads || c->n_q_heads / c->n_kv_heads > 8) {
+    *why = "n_q_heads must be a multiple of n_kv_heads, with at most 8 query heads per group";
+    return false;
+  }
+  if (!(c->rms_eps >= 0.f) || !(c->rope_theta > 0.f)) {
+    *why = "bad rms_eps or rope_theta";
+    return false;
+  }
+  return true;
+}
+
+// Weight arena layout (element offsets), every tensor 256-byte aligned.
+struct WLayout {
+  size_t embed, final_norm, lm, layer0, layer_stride;
+  size_t attn_norm, wqkv, wo, mlp_norm, wg, wu, wd;  // within a layer block
+  size_t total_bytes;
+};
+
+static WLayout wlayout(const ld_config* c) {
+  WLayout L{};
+  const size_t H = c->hidden, V = c->vocab, I = c->intermediate;
+  const size_t qd = (size_t)c->n_q_heads * c->head_dim, kvd = (size_t)c->n_kv_heads * c->head_dim;
+  size_t off = 0;  // bytes
+  auto take = [&](size_t elems) {
+    const size_t at = off;
+    off = align256(off + elems * 2);
+    return at / 2;
+  };
+  L.embed = take(V * H);
+  L.final_norm = take(H);
+  L.lm = c->tied ? L.embed : take(V * H);
+  // layer block
+  size_t lb = 0;
+  auto ltake = [&](size_t elems) {
+    const size_t at = lb;
+    lb = align256(lb + elems * 2);
+    return at / 2;
+  };
+  L.attn_norm = ltake(H);
+  L.wqkv = ltake((qd + 2 * kvd) * H);
+  L.wo = ltake(H * qd);
+  L.mlp_norm = ltake(H);
+  L.wg = ltake(I * H);
+  L.wu = ltake(I * H);
+  L.wd = ltake(H * I);
+  L.layer0 = off / 2;
+  L.layer_stride = lb / 2;
+  L.total_bytes = off + lb * (size_t)c->n_layers;
+  return L;
+}
+
+extern "C" size_t ld_weights_bytes(const ld_config* cfg) {
+  std::string why;
+  if (!cfg_ok(cfg, &why)) return 0;
+  return wlayout(cfg).total_bytes;
+}
+
+// KV + workspace arena layout (byte offsets).
+struct KLayout {
+  size_t kc, vc, xa, xb, qkv, ao, part, hbuf, lm_val, lm_idx, rope, ctr, err, tune_ctr, total;
+  int split_len, max_splits, max_wg;
+};
+
+static int split_len_for(const ld_config* c) { return c->head_dim > 64 ? 32 : 64; }
+
+static KLayout klayout(const ld_config* c, int maxB, int max_seq) {
+  KLayout K{};
+  const size_t H = c->hidden, I = c->intermediate, d = c->head_dim;
+  const size_t qd = (size_t)c->n_q_heads * d, kvd = (size_t)c->n_kv_heads * d;
+  K.split_len = split_len_for(c);
+  K.max_splits = (max_seq + K.split_len - 1) / K.split_len;
+  K.max_wg = 8192;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align256(off + bytes);
+    return at;
+  };
+  const size_t cache = (size_t)c->n_layers * maxB * c->n_kv_heads * (size_t)max_seq * d * 2;
+  K.kc = take(cache);
+  K.vc = take(cache);
+  K.xa = take((size_t)maxB * H * 4);
+  K.xb = take((size_t)maxB * H * 4);
+  K.qkv = take((size_t)maxB * (qd + 2 * kvd) * 4);
+  K.ao = take((size_t)maxB * qd * 4);
+  K.part = take((size_t)maxB * c->n_q_heads * K.max_splits * (d + 2) * 4);
+  K.hbuf = take((size_t)maxB * I * 4);
+  K.lm_val = take((size_t)K.max_wg * maxB * 4);
+  K.lm_idx = take((size_t)K.max_wg * maxB * 4);
+  K.rope = take((size_t)max_seq * (d / 2) * 2 * 4);
+  K.ctr = take(((size_t)c->n_layers * kCtrPerLayer + 8 + (size_t)c->n_layers * maxB * c->n_kv_heads) *
+               4);
+  K.err = take(256);
+  K.tune_ctr = take(((size_t)kCtrPerLayer * 2 + 8 + (size_t)maxB * c->n_kv_heads) * 4);
+  K.total = off;
+  return K;
+}
+
+extern "C" size_t ld_kv_bytes(const ld_config* cfg, int32_t max_batch, int32_t max_seq) {
+  std::string why;
+  if (!cfg_ok(cfg, &why) || max_batch < 1 || max_batch > 64 || max_seq < 1) return 0;
+  return klayout(cfg, max_batch, max_seq).total;
+}
+
+static ld_status setup_launch(ld_model* m) {
+  HIPCHK(m, hipGetDevice(&m->device));
+  HIPCHK(m, hipDeviceGetAttribute(&m->n_cu, hipDeviceAttributeMultiprocessorCount, m->device));
+  int khz = 0;
+  if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, m->device) == hipSuccess &&
+      khz > 0)
+    m->wall_khz = (double)khz;
+  m->watchdog_ticks = (uint64_t)(m->wall_khz * 1000.0 * 2.0);  // 2 s
+  HIPCHK(m, hipStreamCreateWithFlags(&m->s1, hipStreamNonBlocking));
+  HIPCHK(m, hipEventCreateWithFlags(&m->ev_fork, hipEventDisableTiming));
+  HIPCHK(m, hipEventCreateWithFlags(&m->ev_join, hipEventDisableTiming));
+  for (int b = 0; b <= 64; ++b) {
+    m->gu_variant[b] = kGuCol;
+    m->gu_tuned[b] = false;
+  }
+  return LD_OK;
+}
+
+extern "C" ld_status ld_init_weights(ld_model** out, const ld_config* cfg, void* dev_buf,
+                                     size_t bytes, uint64_t seed, float w_std, void* stream) {
+  std::string why;
+  if (!out) return fail(nullptr, LD_EINVAL, "null output pointer");
+  *out = nullptr;
+  if (!cfg_ok(cfg, &why)) return fail(nullptr, LD_EINVAL, "bad config: " + why);
+  if (!(w_std >= 0.f)) return fail(nullptr, LD_EINVAL, "bad w_std");
+  const WLayout L = wlayout(cfg);
+  if (dev_buf && bytes < L.total_bytes) return fail(nullptr, LD_ENOMEM, "weight buffer too small");
+  if (dev_buf && ((uintptr_t)dev_buf & 255)) return fail(nullptr, LD_EINVAL, "weight buffer not 256-byte aligned");
+  ld_model* m = new ld_model();
+  m->cfg = *cfg;
+  ld_status st = setup_launch(m);
+  if (st != LD_OK) {
+    g_err = m->err;
+    ld_free(m);
+    return st;
+  }
+  if (dev_buf) {
+    m->warena = dev_buf;
+  } else {
+    if (hipMalloc(&m->warena, L.total_bytes) != hipSuccess) {
+      g_err = "hipMalloc of the weight arena failed";
+      ld_free(m);
+      return LD_ENOMEM;
+    }
+    m->own_w = true;
+  }
+  m->wbytes = L.total_bytes;
+  uint16_t* base = static_cast<uint16_t*>(m->warena);
+  m->W.embed = base + L.embed;
+  m->W.final_norm = base + L.final_norm;
+  m->W.lm = base + L.lm;
+  m->W.layer0 = base + L.layer0;
+  m->W.layer_stride = (int64_t)L.layer_stride;
+  m->W.o_attn_norm = (int64_t)L.attn_norm;
+  m->W.o_wqkv = (int64_t)L.wqkv;
+  m->W.o_wo = (int64_t)L.wo;
+  m->W.o_mlp_norm = (int64_t)L.mlp_norm;
+  m->W.o_wg = (int64_t)L.wg;
+  m->W.o_wu = (int64_t)L.wu;
+  m->W.o_wd = (int64_t)L.wd;
+
+  Dims& D = m->D;
+  D.L = cfg->n_layers;
+  D.H = cfg->hidden;
+  D.nq = cfg->n_q_heads;
+  D.nkv = cfg->n_kv_heads;
+  D.d = cfg->head_dim;
+  D.I = cfg->intermediate;
+  D.V = cfg->vocab;
+  D.group = D.nq / D.nkv;
+  D.qd = D.nq * D.d;
+  D.kvd = D.nkv * D.d;
+  D.qkv_rows = D.qd + 2 * D.kvd;
+  D.tied = cfg->tied;
+  D.eps = cfg->rms_eps;
+  D.attn_scale = 1.0f / sqrtf((float)D.d);
+
+  // synthetic weights from the seeded generator (logical row-major index)
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const float kappa = ls_kappa(w_std);
+  const int64_t H = D.H, V = D.V, I = D.I, qd = D.qd, kvd = D.kvd;
+  auto gen = [&](const uint16_t* dst, int64_t n, uint64_t tensor) {
+    return launch_gen_normal(const_cast<uint16_t*>(dst), n, ls_key(seed, tensor), 0, kappa, s);
+  };
+  auto ones = [&](const uint16_t* dst, int64_t n) {
+    return launch_fill16(const_cast<uint16_t*>(dst), n, LS_BF16_ONE, s);
+  };
+  hipError_t e = hipSuccess;
+  auto chk = [&](hipError_t x) {
+    if (e == hipSuccess) e = x;
+  };
+  chk(gen(m->W.embed, V * H, LS_T_EMBED));
+  chk(ones(m->W.final_norm, H));
+  if (!cfg->tied) chk(gen(m->W.lm, V * H, LS_T_LM_HEAD));
+  for (int l = 0; l < D.L; ++l) {
+    const uint16_t* lb = m->W.layer0 + (int64_t)l * m->W.layer_stride;
+    chk(ones(lb + L.attn_norm, H));
+    chk(gen(lb + L.wqkv, qd * H, LS_T_LAYER(l, LS_K_WQ)));
+    chk(gen(lb + L.wqkv + qd * H, kvd * H, LS_T_LAYER(l, LS_K_WK)));
+    chk(gen(lb + L.wqkv + (qd + kvd) * H, kvd * H, LS_T_LAYER(l, LS_K_WV)));
+    chk(gen(lb + L.wo, H * qd, LS_T_LAYER(l, LS_K_WO)));
+    chk(ones(lb + L.mlp_norm, H));
+    chk(gen(lb + L.wg, I * H, LS_T_LAYER(l, LS_K_WG)));
+    chk(gen(lb + L.wu, I * H, LS_T_LAYER(l, LS_K_WU)));
+    chk(gen(lb + L.wd, H * I, LS_T_LAYER(l, LS_K_WD)));
+  }
+  if (e != hipSuccess) {
+    g_err = std::string("weight generation launch failed: ") + hipGetErrorString(e);
+    ld_free(m);
+    return LD_EHIP;
+  }
+  *out = m;
+  return LD_OK;
+}
+
+static ld_status compute_grids(ld_model* m) {
+  const int maxnb = nb_for_batch(m->D.max_batch);
+  m->smem_attn = attn_smem(m->D.group, m->D.d, m->D.split_len);
+  const size_t gs = gemv_smem_bytes();
+  m->smem_mega = std::max(m->smem_attn, gs);
+  if (m->smem_attn > 160 * 1024 || m->smem_mega > 160 * 1024)
+    return fail(m, LD_EINVAL, "attention tile does not fit in LDS");
+  HIPCHK(m, set_max_dynamic_smem(kSAttn, 1, m->smem_attn));
+  // per-stage kernels: the smallest occupancy over stages and batch tiles
+  int occ_min = 1 << 30;
+  for (int nb = 1; nb <= maxnb; nb *= 2) {
+    for (int st = kSQkv; st <= kSLm; ++st) {
+      int occ = 0;
+      const size_t sm = (st == kSAttn) ? m->smem_attn : 0;
+      HIPCHK(m, occupancy(st, nb, sm, &occ));
+      occ_min = std::min(occ_min, std::max(occ, 1));
+    }
+    int occm = 0;
+    HIPCHK(m, set_max_dynamic_smem(0, nb, m->smem_mega));
+    HIPCHK(m, occupancy(0, nb, m->smem_mega, &occm));
+    if (occm < 1) return fail(m, LD_EINVAL, "persistent kernel does not fit on a CU");
+    m->grid_mega[nb] = std::min(occm * m->n_cu, m->K.max_wg);
+  }
+  m->grid_wait = std::min(occ_min * m->n_cu, m->K.max_wg);
+  // tile-flag mode: two kernels in flight, each may hold at most half the machine
+  m->grid_flags = std::max(1, occ_min / 2) * m->n_cu;
+  m->grid_attn_flags = m->grid_flags;
+  return LD_OK;
+}
+
+extern "C" ld_status ld_alloc_kv(ld_model* m, void* dev_buf, size_t bytes, int32_t max_batch,
+                                 int32_t max_seq) {
+  if (!m) return fail(nullptr, LD_EINVAL, "null model");
+  if (m->kv_ready) return fail(m, LD_ESTATE, "KV arena already allocated");
+  if (max_batch < 1 || max_batch > 64) return fail(m, LD_EINVAL, "max_batch must be in [1, 64]");
+  if (max_seq < 1) return fail(m, LD_EINVAL, "max_seq must be >= 1");
+  const KLayout KL = klayout(&m->cfg, max_batch, max_seq);
+  if (dev_buf && bytes < KL.total) return fail(m, LD_ENOMEM, "KV buffer too small");
+  if (dev_buf && ((uintptr_t)dev_buf & 255)) return fail(m, LD_EINVAL, "KV buffer not 256-byte aligned");
+  HIPCHK(m, hipDeviceSynchronize());
+  if (dev_buf) {
+    m->karena = dev_buf;
+  } else {
+    if (hipMalloc(&m->karena, KL.total) != hipSuccess)
+      return fail(m, LD_ENOMEM, "hipMalloc of the KV arena failed");
+    m->own_k = true;
+  }
+  m->kbytes = KL.total;
+  char* base = static_cast<char*>(m->karena);
+  Work& K = m->K;
+  K.kc = reinterpret_cast<uint16_t*>(base + KL.kc);
+  K.vc = reinterpret_cast<uint16_t*>(base + KL.vc);
+  K.xa = reinterpret_cast<float*>(base + KL.xa);
+  K.xb = reinterpret_cast<float*>(base + KL.xb);
+  K.qkv = reinterpret_cast<float*>(base + KL.qkv);
+  K.ao = reinterpret_cast<float*>(base + KL.ao);
+  K.part = reinterpret_cast<float*>(base + KL.part);
+  K.hbuf = reinterpret_cast<float*>(base + KL.hbuf);
+  K.lm_val = reinterpret_cast<float*>(base + KL.lm_val);
+  K.lm_idx = reinterpret_cast<int*>(base + KL.lm_idx);
+  K.rope = reinterpret_cast<const float*>(base + KL.rope);
+  K.ctr = reinterpret_cast<uint32_t*>(base + KL.ctr);
+  K.err = reinterpret_cast<int*>(base + KL.err);
+  K.max_wg = KL.max_wg;
+  m->tune_ctr = reinterpret_cast<uint32_t*>(base + KL.tune_ctr);
+  m->D.max_batch = max_batch;
+  m->D.max_seq = max_seq;
+  m->D.split_len = KL.split_len;
+  m->D.max_splits = KL.max_splits;
+
+  // zero everything except the caches, then counters and error word
+  HIPCHK(m, hipMemset(base + KL.xa, 0, KL.total - KL.xa));
+  // RoPE table: angle p * theta^(-2i/d) in double, cos and sin rounded to fp32
+  const int half = m->D.d / 2;
+  std::vector<float> rope((size_t)max_seq * half * 2);
+  for (int p = 0; p < max_seq; ++p)
+    for (int i = 0; i < half; ++i) {
+      const double inv = std::pow((double)m->cfg.rope_theta, -2.0 * i / (double)m->D.d);
+      const double a = (double)p * inv;
+      rope[((size_t)p * half + i) * 2] = (float)std::cos(a);
+      rope[((size_t)p * half + i) * 2 + 1] = (float)std::sin(a);
+    }
+  HIPCHK(m, hipMemcpy(base + KL.rope, rope.data(), rope.size() * 4, hipMemcpyHostToDevice));
+  m->tot_qkv = m->tot_attn = m->tot_o = m->tot_gu = m->tot_d = m->tot_lm = 0;
+  ld_status st = compute_grids(m);
+  if (st != LD_OK) return st;
+  m->K.watchdog = m->watchdog_ticks;
+  m->kv_ready = true;
+  return LD_OK;
+}
+
+extern "C" ld_status ld_fill_kv(ld_model* m, uint64_t seed, float kv_std,
+                                const int32_t* prefill_len, void* stream) {
+  if (!m) return fail(nullptr, LD_EINVAL, "null model");
+  if (!m->kv_ready) return fail(m, LD_ESTATE, "ld_alloc_kv first");
+  if (!prefill_len) return fail(m, LD_EINVAL, "null prefill_len");
+  const int B = m->D.max_batch;
+  for (int b = 0; b < B; ++b)
+    if (prefill_len[b] < 0 || prefill_len[b] > m->D.max_seq)
+      return fail(m, LD_EINVAL, "prefill length outside [0, max_seq]");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int* len_dev = nullptr;
+  HIPCHK(m, hipMalloc(&len_dev, B * sizeof(int)));
+  hipError_t e = hipMemcpy(len_dev, prefill_len, B * sizeof(int), hipMemcpyHostToDevice);
+  const float kappa = ls_kappa(kv_std);
+  const int64_t per_layer = (int64_t)B * m->D.nkv * m->D.max_seq * m->D.d;
+  for (int l = 0; l < m->D.L && e == hipSuccess; ++l)
+    e = launch_gen_kv(m->K.kc + l * per_layer, m->K.vc + l * per_layer, len_dev, B, m->D.nkv,
+                      m->D.max_seq, m->D.d, ls_key(seed, LS_T_KCACHE(l)),
+                      ls_key(seed, LS_T_VCACHE(l)), kappa, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  (void)hipFree(len_dev);
+  if (e != hipSuccess) return fail(m, LD_EHIP, std::string("KV fill failed: ") + hipGetErrorString(e));
+  return LD_OK;
+}
+
+extern "C" ld_status ld_set_mode(ld_model* m, ld_mode mode) {
+  if (!m) return fail(nullptr, LD_EINVAL, "null model");
+  if (mode != LD_MODE_WAIT && mode != LD_MODE_FLAGS && mode != LD_MODE_MEGA)
+    return fail(m, LD_EINVAL, "unknown mode");
+  m->mode = mode;
+  return LD_OK;
+}
+
+static Params make_params(ld_model* m) {
+  Params P{};
+  P.D = m->D;
+  P.W = m->W;
+  P.K = m->K;
+  return P;
+}
+
+// Enqueue one step in the current mode.
+static ld_status enqueue_step(ld_model* m, const int32_t* tokens, int32_t B, const int32_t* pos,
+                              float* logits, int32_t* next, hipStream_t s0) {
+  Params P = make_params(m);
+  P.S.tokens = tokens;
+  P.S.pos = pos;
+  P.S.logits = logits;
+  P.S.next = next;
+  P.S.B = B;
+  P.S.gu_variant = m->gu_variant[B];
+  P.S.inject = m->inject_next;
+  m->inject_next = 0;
+  const int L = m->D.L;
+  const uint32_t attn_inc = (uint32_t)(B * m->D.nkv);
+  if (m->mode == LD_MODE_MEGA) {
+    const int nb = nb_for_batch(B);
+    const int g = m->grid_mega[nb];
+    m->tot_qkv += g;
+    m->tot_attn += attn_inc;
+    m->tot_o += g;
+    m->tot_gu += g;
+    m->tot_d += g;
+    m->tot_lm += g;
+    P.S.wait = 0;
+    P.S.t_qkv = m->tot_qkv; P.S.t_attn = m->tot_attn; P.S.t_o = m->tot_o;
+    P.S.t_gu = m->tot_gu; P.S.t_d = m->tot_d; P.S.t_lm = m->tot_lm;
+    HIPCHK(m, launch_mega(P, g, m->smem_mega, s0));
+    return LD_OK;
+  }
+  const bool flags = (m->mode == LD_MODE_FLAGS);
+  const int g = flags ? m->grid_flags : m->grid_wait;
+  const int ga = flags ? m->grid_attn_flags : m->grid_wait;
+  m->tot_qkv += g;
+  m->tot_attn += attn_inc;
+  m->tot_o += g;
+  m->tot_gu += g;
+  m->tot_d += g;
+  m->tot_lm += g;
+  P.S.wait = flags ? 0 : 1;
+  P.S.t_qkv = m->tot_qkv; P.S.t_attn = m->tot_attn; P.S.t_o = m->tot_o;
+  P.S.t_gu = m->tot_gu; P.S.t_d = m->tot_d; P.S.t_lm = m->tot_lm;
+  hipStream_t ss[2] = {s0, m->s1};
+  if (flags) {
+    HIPCHK(m, hipEventRecord(m->ev_fork, s0));
+    HIPCHK(m, hipStreamWaitEvent(m->s1, m->ev_fork, 0));
+  }
+  int k = 0;
+  auto launch = [&](int stage, int l, int grid, size_t smem) -> hipError_t {
+    hipStream_t s = flags ? ss[k & 1] : s0;
+    ++k;
+    return launch_stage(stage, P, l, grid, smem, s);
+  };
+  for (int l = 0; l < L; ++l) {
+    HIPCHK(m, launch(kSQkv, l, g, 0));
+    HIPCHK(m, launch(kSAttn, l, ga, m->smem_attn));
+    HIPCHK(m, launch(kSO, l, g, 0));
+    HIPCHK(m, launch(kSGu, l, g, 0));
+    HIPCHK(m, launch(kSD, l, g, 0));
+  }
+  HIPCHK(m, launch(kSLm, 0, g, 0));
+  if (flags) {
+    HIPCHK(m, hipEventRecord(m->ev_join, m->s1));
+    HIPCHK(m, hipStreamWaitEvent(s0, m->ev_join, 0));
+  }
+  return LD_OK;
+}
+
+extern "C" ld_status ld_decode_step(ld_model* m, const int32_t* tokens, int32_t batch,
+                                    const int32_t* positions, float* logits, int32_t* next_tokens,
+                                    void* stream) {
+  if (!m) return fail(nullptr, LD_EINVAL, "null model");
+  if (!m->kv_ready) return fail(m, LD_ESTATE, "ld_alloc_kv first");
+  if (batch < 1 || batch > m->D.max_batch) return fail(m, LD_EINVAL, "batch outside [1, max_batch]");
+  if (!tokens || !positions || !logits) return fail(m, LD_EINVAL, "null tokens, positions or logits");
+  if (((uintptr_t)tokens & 3) || ((uintptr_t)positions & 3) || ((uintptr_t)logits & 3) ||
+      ((uintptr_t)next_tokens & 3))
+    return fail(m, LD_EINVAL, "unaligned pointer");
+  return enqueue_step(m, tokens, batch, positions, logits, next_tokens,
+                      static_cast<hipStream_t>(stream));
+}
+
+extern "C" ld_status ld_device_error(ld_model* m) {
+  if (!m) return fail(nullptr, LD_EINVAL, "null model");
+  if (!m->kv_ready) return LD_OK;
+  HIPCHK(m, hipDeviceSynchronize());
+  int w = 0;
+  HIPCHK(m, hipMemcpy(&w, m->K.err, sizeof(int), hipMemcpyDeviceToHost));
+  if (w == 0) return LD_OK;
+  const int zero = 0;
+  HIPCHK(m, hipMemcpy(m->K.err, &zero, sizeof(int), hipMemcpyHostToDevice));
+  const int code = w & 0xFF, stage = w >> 8;
+  if (code == kErrTimeout) {
+    // the counters no longer match the host's totals: reset both
+    const size_t nctr = (size_t)m->D.L * kCtrPerLayer + 8 + (size_t)m->D.L * m->D.max_batch * m->D.nkv;
+    HIPCHK(m, hipMemset(m->K.ctr, 0, nctr * 4));
+    HIPCHK(m, hipDeviceSynchronize());
+    m->tot_qkv = m->tot_attn = m->tot_o = m->tot_gu = m->tot_d = m->tot_lm = 0;
+    char buf[96];
+    snprintf(buf, sizeof buf, "device wait timed out in stage %d", stage);
+    return fail(m, LD_ETIMEOUT, buf);
+  }
+  return fail(m, LD_EDEVICE, code == kErrToken ? "token outside [0, vocab)" : "position outside [0, max_seq)");
+}
+
+extern "C" const char* ld_last_error(const ld_model* m) {
+  return m ? m->err.c_str() : g_err.c_str();
+}
+
+extern "C" void ld_free(ld_model* m) {
+  if (!m) return;
+  (void)hipDeviceSynchronize();
+  if (m->own_w && m->warena) (void)hipFree(m->warena);
+  if (m->own_k && m->karena) (void)hipFree(m->karena);
+  if (m->s1) (void)hipStreamDestroy(m->s1);
+  if (m->ev_fork) (void)hipEventDestroy(m->ev_fork);
+  if (m->ev_join) (void)hipEventDestroy(m->ev_join);
+  delete m;
+}
+
+// ------------------------------------------------------------- tuning
+
+// Time one standalone SwiGLU launch of layer 0 with the given variant.
+static ld_status time_gu(ld_model* m, int B, int variant, int reps, float* ms_out) {
+  Params P = make_params(m);
+  P.K.ctr = m->tune_ctr;  // private counters: never disturbs the decode totals
+  P.S.B = B;
+  P.S.wait = 1;
+  P.S.gu_variant = variant;
+  hipStream_t s = nullptr;
+  hipEvent_t a, b;
+  HIPCHK(m, hipEventCreate(&a));
+  HIPCHK(m, hipEventCreate(&b));
+  for (int i = 0; i < 2; ++i) HIPCHK(m, launch_stage(kSGu, P, 0, m->grid_wait, 0, s));
+  HIPCHK(m, hipEventRecord(a, s));
+  for (int i = 0; i < reps; ++i) HIPCHK(m, launch_stage(kSGu, P, 0, m->grid_wait, 0, s));
+  HIPCHK(m, hipEventRecord(b, s));
+  HIPCHK(m, hipEventSynchronize(b));
+  float ms = 0.f;
+  HIPCHK(m, hipEventElapsedTime(&ms, a, b));
+  (void)hipEventDestroy(a);
+  (void)hipEventDestroy(b);
+  *ms_out = ms / reps;
+  return LD_OK;
+}
+
+static ld_status write_table(ld_model* m, const char* path) {
+  FILE* f = fopen(path, "w");
+  if (!f) return fail(m, LD_EINVAL, std::string("cannot write ") + path);
+  const ld_config& c = m->cfg;
+  fprintf(f, "{\"shape\": [%d, %d, %d, %d, %d, %d, %d], \"swiglu\": {", c.n_layers, c.hidden,
+          c.n_q_heads, c.n_kv_heads, c.head_dim, c.intermediate, c.vocab);
+  bool first = true;
+  for (int b = 1; b <= 64; ++b)
+    if (m->gu_tuned[b]) {
+      fprintf(f, "%s\"%d\": \"%s\"", first ? "" : ", ", b, m->gu_variant[b] == kGuRow ? "row" : "col");
+      first = false;
+    }
+  fprintf(f, "}}\n");
+  fclose(f);
+  return LD_OK;
+}
+
+extern "C" ld_status ld_tune(ld_model* m, const int32_t* batches, int32_t n, const char* table_path) {
+  if (!m) return fail(nullptr, LD_EINVAL, "null model");
+  if (!m->kv_ready) return fail(m, LD_ESTATE, "ld_alloc_kv first");
+  if (!batches || n < 1) return fail(m, LD_EINVAL, "no batch sizes");
+  for (int i = 0; i < n; ++i)
+    if (batches[i] < 1 || batches[i] > m->D.max_batch)
+      return fail(m, LD_EINVAL, "tuning batch outside [1, max_batch]");
+  HIPCHK(m, hipDeviceSynchronize());
+  for (int i = 0; i < n; ++i) {
+    const int B = batches[i];
+    float t_col = 0.f, t_row = 0.f;
+    ld_status st = time_gu(m, B, kGuCol, 10, &t_col);
+    if (st != LD_OK) return st;
+    st = time_gu(m, B, kGuRow, 10, &t_row);
+    if (st != LD_OK) return st;
+    m->gu_variant[B] = (t_row < t_col) ? kGuRow : kGuCol;
+    m->gu_tuned[B] = true;
+  }
+  HIPCHK(m, hipMemset(m->tune_ctr, 0, 4 * ((size_t)kCtrPerLayer * 2 + 8)));
+  HIPCHK(m, hipDeviceSynchronize());
+  if (table_path) return write_table(m, table_path);
+  return LD_OK;
+}
+
+extern "C" ld_status ld_load_tuning(ld_model* m, const char* table_path) {
+  if (!m) return fail(nullptr, LD_EINVAL, "null model");
+  if (!table_path) return fail(m, LD_EINVAL, "null path");
+  FILE* f = fopen(table_path, "r");
+  if (!f) return fail(m, LD_EINVAL, std::string("cannot read ") + table_path);
+  std::string txt;
+  char buf[4096];
+  size_t k;
+  while ((k = fread(buf, 1, sizeof buf, f)) > 0) txt.append(buf, k);
+  fclose(f);
+  const ld_config& c = m->cfg;
+  char shape[160];
+  snprintf(shape, sizeof shape, "\"shape\": [%d, %d, %d, %d, %d, %d, %d]", c.n_layers, c.hidden,
+           c.n_q_heads, c.n_kv_heads, c.head_dim, c.intermediate, c.vocab);
+  if (txt.find(shape) == std::string::npos) return fail(m, LD_EINVAL, "tuning table is for another shape");
+  const size_t sw = txt.find("\"swiglu\"");
+  if (sw == std::string::npos) return fail(m, LD_EINVAL, "tuning table has no swiglu entry");
+  size_t p = txt.find('{', sw);
+  const size_t end = txt.find('}', p);
+  if (p == std::string::npos || end == std::string::npos) return fail(m, LD_EINVAL, "malformed tuning table");
+  int parsed[65];
+  bool have[65] = {false};
+  while (true) {
+    const size_t q = txt.find('"', p + 1);
+    if (q == std::string::npos || q > end) break;
+    const int b = atoi(txt.c_str() + q + 1);
+    const size_t v = txt.find('"', txt.find(':', q) + 1);
+    if (b < 1 || b > 64 || v == std::string::npos || v > end) return fail(m, LD_EINVAL, "malformed tuning table");
+    if (txt.compare(v + 1, 3, "row") == 0) parsed[b] = kGuRow;
+    else if (txt.compare(v + 1, 3, "col") == 0) parsed[b] = kGuCol;
+    else return fail(m, LD_EINVAL, "unknown tiling in tuning table");
+    have[b] = true;
+    p = txt.find('"', v + 1);
+    if (p == std::string::npos || p > end) break;
+  }
+  for (int b = 1; b <= 64; ++b)
+    if (have[b]) {
+      m->gu_variant[b] = parsed[b];
+      m->gu_tuned[b] = true;
+    }
+  return LD_OK;
+}
+
+// --------------------------------------------------- inspection / tests
+
+static ld_status weight_ptr(ld_model* m, int kind, int layer, uint16_t** p, int64_t* rows,
+                            int64_t* cols) {
+  const Dims& D = m->D;
+  const bool per_layer = !(kind == LD_W_EMBED || kind == LD_W_FINAL_NORM || kind == LD_W_LM_HEAD);
+  if (per_layer && (layer < 0 || layer >= D.L)) return fail(m, LD_EINVAL, "layer out of range");
+  uint16_t* lb = const_cast<uint16_t*>(m->W.layer0) + (per_layer ? (int64_t)layer * m->W.layer_stride : 0);
+  const int64_t H = D.H, I = D.I, qd = D.qd, kvd = D.kvd;
+  switch (kind) {
+    case LD_W_EMBED: *p = const_cast<uint16_t*>(m->W.embed); *rows = D.V; *cols = H; break;
+    case LD_W_FINAL_NORM: *p = const_cast<uint16_t*>(m->W.final_norm); *rows = 1; *cols = H; break;
+    case LD_W_LM_HEAD: *p = const_cast<uint16_t*>(m->W.lm); *rows = D.V; *cols = H; break;
+    case LD_W_ATTN_NORM: *p = lb + m->W.o_attn_norm; *rows = 1; *cols = H; break;
+    case LD_W_Q: *p = lb + m->W.o_wqkv; *rows = qd; *cols = H; break;
+    case LD_W_K: *p = lb + m->W.o_wqkv + qd * H; *rows = kvd; *cols = H; break;
+    case LD_W_V: *p = lb + m->W.o_wqkv + (qd + kvd) * H; *rows = kvd; *cols = H; break;
+    case LD_W_O: *p = lb + m->W.o_wo; *rows = H; *cols = qd; break;
+    case LD_W_MLP_NORM: *p = lb + m->W.o_mlp_norm; *rows = 1; *cols = H; break;
+    case LD_W_GATE: *p = lb + m->W.o_wg; *rows = I; *cols = H; break;
+    case LD_W_UP: *p = lb + m->W.o_wu; *rows = I; *cols = H; break;
+    case LD_W_DOWN: *p = lb + m->W.o_wd; *rows = H; *cols = I; break;
+    default: return fail(m, LD_EINVAL, "unknown weight kind");
+  }
+  return LD_OK;
+}
+
+extern "C" ld_status ld_weight_shape(ld_model* m, int32_t kind, int32_t layer, int64_t* rows,
+                                     int64_t* cols) {
+  if (!m || !rows || !cols) return fail(m, LD_EINVAL, "null argument");
+  uint16_t* p;
+  return weight_ptr(m, kind, layer, &p, rows, cols);
+}
+
+extern "C" ld_status ld_read_weight(ld_model* m, int32_t kind, int32_t layer, uint16_t* host_dst) {
+  if (!m || !host_dst) return fail(m, LD_EINVAL, "null argument");
+  uint16_t* p;
+  int64_t r, c;
+  ld_status st = weight_ptr(m, kind, layer, &p, &r, &c);
+  if (st != LD_OK) return st;
+  HIPCHK(m, hipDeviceSynchronize());
+  HIPCHK(m, hipMemcpy(host_dst, p, (size_t)(r * c) * 2, hipMemcpyDeviceToHost));
+  return LD_OK;
+}
+
+extern "C" ld_status ld_write_weight(ld_model* m, int32_t kind, int32_t layer,
+                                     const uint16_t* host_src) {
+  if (!m || !host_src) return fail(m, LD_EINVAL, "null argument");
+  uint16_t* p;
+  int64_t r, c;
+  ld_status st = weight_ptr(m, kind, layer, &p, &r, &c);
+  if (st != LD_OK) return st;
+  if (kind == LD_W_LM_HEAD && m->cfg.tied) return fail(m, LD_EINVAL, "tied model: write the embedding");
+  HIPCHK(m, hipDeviceSynchronize());
+  HIPCHK(m, hipMemcpy(p, host_src, (size_t)(r * c) * 2, hipMemcpyHostToDevice));
+  return LD_OK;
+}
+
+extern "C" ld_status ld_read_kv(ld_model* m, int32_t layer, int32_t seq, int32_t kv_head,
+                                int32_t pos0, int32_t npos, uint16_t* k_dst, uint16_t* v_dst) {
+  if (!m) return fail(nullptr, LD_EINVAL, "null model");
+  if (!m->kv_ready) return fail(m, LD_ESTATE, "ld_alloc_kv first");
+  const Dims& D = m->D;
+  if (layer < 0 || layer >= D.L || seq < 0 || seq >= D.max_batch || kv_head < 0 ||
+      kv_head >= D.nkv || pos0 < 0 || npos < 0 || pos0 + npos > D.max_seq)
+    return fail(m, LD_EINVAL, "KV slice out of range");
+  const int64_t off = ((((int64_t)layer * D.max_batch + seq) * D.nkv + kv_head) * D.max_seq + pos0) * D.d;
+  HIPCHK(m, hipDeviceSynchronize());
+  if (k_dst) HIPCHK(m, hipMemcpy(k_dst, m->K.kc + off, (size_t)npos * D.d * 2, hipMemcpyDeviceToHost));
+  if (v_dst) HIPCHK(m, hipMemcpy(v_dst, m->K.vc + off, (size_t)npos * D.d * 2, hipMemcpyDeviceToHost));
+  return LD_OK;
+}
+
+extern "C" ld_status ld_set_swiglu_variant(ld_model* m, int32_t batch, int32_t variant) {
+  if (!m) return fail(nullptr, LD_EINVAL, "null model");
+  if (batch < 1 || batch > 64 || (variant != LD_SWIGLU_COL && variant != LD_SWIGLU_ROW))
+    return fail(m, LD_EINVAL, "bad batch or variant");
+  m->gu_variant[batch] = variant == LD_SWIGLU_ROW ? kGuRow : kGuCol;
+  return LD_OK;
+}
+
+extern "C" int32_t ld_get_swiglu_variant(const ld_model* m, int32_t batch) {
+  if (!m || batch < 1 || batch > 64) return -1;
+  return m->gu_variant[batch] == kGuRow ? LD_SWIGLU_ROW : LD_SWIGLU_COL;
+}
+
+extern "C" ld_status ld_set_watchdog(ld_model* m, double seconds) {
+  if (!m) return fail(nullptr, LD_EINVAL, "null model");
+  if (!(seconds > 0.0) || seconds > 3600.0) return fail(m, LD_EINVAL, "watchdog outside (0, 3600] s");
+  m->watchdog_ticks = (uint64_t)(m->wall_khz * 1000.0 * seconds);
+  m->K.watchdog = m->watchdog_ticks;
+  return LD_OK;
+}
+
+extern "C" ld_status ld_debug_inject_stall(ld_model* m) {
+  if (!m) return fail(nullptr, LD_EINVAL, "null model");
+  m->inject_next = 1;  // next step's attention waits for one signal too many
+  return LD_OK;
+}
+
+extern "C" ld_status ld_launch_info(const ld_model* m, int32_t* out, int32_t n) {
+  if (!m || !out || n < 6) return LD_EINVAL;
+  out[0] = m->n_cu;
+  out[1] = m->grid_wait;
+  out[2] = m->grid_flags;
+  out[3] = m->grid_mega[1];
+  out[4] = m->D.split_len;
+  out[5] = (int32_t)m->mode;
+  return LD_OK;
+}

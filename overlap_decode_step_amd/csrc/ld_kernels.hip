@@ -1,0 +1,191 @@
+// ld_kernels.hip - kernels of the decode step for gfx950 and their launch
+// wrappers (the host runtime calls only the wrappers in ld_launch.h).
+//
+//  k_qkv / k_attn / k_o / k_gu / k_d / k_lm : one kernel per stage, used by
+//      the whole-kernel-wait and tile-flag modes;
+//  k_mega : one persistent cooperative kernel per step whose workgroups run
+//      every stage of every layer in order, synchronising on the same
+//      readiness counters (the single-kernel decode of Hazy Research, "Look
+//      Ma, No Bubbles! Designing a Low-Latency Megakernel for Llama-1B");
+//  k_gen_normal / k_fill16 / k_gen_kv : seeded synthetic inputs.
+#include "ld_launch.h"
+#include "ld_stages.hpp"
+#include "../../synth/ld_synth.h"
+
+namespace ld {
+
+template <int NB>
+__global__ __launch_bounds__(kThreads) void k_qkv(Params P, int l) {
+  __shared__ GemvSmem sm;
+  stage_qkv<NB>(P, l, blockIdx.x, gridDim.x, sm);
+}
+
+__global__ __launch_bounds__(kThreads) void k_attn(Params P, int l) {
+  extern __shared__ __align__(16) char smem[];
+  stage_attn(P, l, blockIdx.x, gridDim.x, smem);
+}
+
+template <int NB>
+__global__ __launch_bounds__(kThreads) void k_o(Params P, int l) {
+  __shared__ GemvSmem sm;
+  stage_o<NB>(P, l, blockIdx.x, gridDim.x, sm);
+}
+
+template <int NB>
+__global__ __launch_bounds__(kThreads) void k_gu(Params P, int l) {
+  __shared__ GemvSmem sm;
+  stage_gu<NB>(P, l, blockIdx.x, gridDim.x, sm);
+}
+
+template <int NB>
+__global__ __launch_bounds__(kThreads) void k_d(Params P, int l) {
+  __shared__ GemvSmem sm;
+  stage_d<NB>(P, l, blockIdx.x, gridDim.x, sm);
+}
+
+template <int NB>
+__global__ __launch_bounds__(kThreads) void k_lm(Params P, int l) {
+  __shared__ GemvSmem sm;
+  stage_lm<NB>(P, blockIdx.x, gridDim.x, sm);
+}
+
+template <int NB>
+__global__ __launch_bounds__(kThreads) void k_mega(Params P) {
+  extern __shared__ __align__(16) char smem[];
+  GemvSmem& sm = *reinterpret_cast<GemvSmem*>(smem);
+  const int wg = blockIdx.x, nwg = gridDim.x;
+  for (int l = 0; l < P.D.L; ++l) {
+    stage_qkv<NB>(P, l, wg, nwg, sm);
+    stage_attn(P, l, wg, nwg, smem);
+    __syncthreads();
+    stage_o<NB>(P, l, wg, nwg, sm);
+    stage_gu<NB>(P, l, wg, nwg, sm);
+    stage_d<NB>(P, l, wg, nwg, sm);
+  }
+  stage_lm<NB>(P, wg, nwg, sm);
+}
+
+// ---------------------------------------------------------- generators
+
+__global__ void k_gen_normal(uint16_t* dst, int64_t n, uint64_t key, uint64_t index0,
+                             float kappa) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+    dst[i] = ls_normal_bf16(key, index0 + (uint64_t)i, kappa);
+}
+
+__global__ void k_fill16(uint16_t* dst, int64_t n, uint16_t v) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) dst[i] = v;
+}
+
+// KV prefill of one layer: blockIdx.y = seq * n_kv + head; positions < len[seq].
+__global__ void k_gen_kv(uint16_t* kc, uint16_t* vc, const int* len, int n_kv, int max_seq,
+                         int d, uint64_t kkey, uint64_t vkey, float kappa) {
+  const int bh = blockIdx.y, b = bh / n_kv, h = bh - b * n_kv;
+  const int64_t n = (int64_t)len[b] * d;
+  const int64_t base = (int64_t)bh * max_seq * d;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += stride) {
+    const uint64_t pos = (uint64_t)(e / d), i = (uint64_t)(e % d);
+    const uint64_t idx = ls_kv_index((uint64_t)b, (uint64_t)n_kv, (uint64_t)h, pos, (uint64_t)d, i);
+    kc[base + e] = ls_normal_bf16(kkey, idx, kappa);
+    vc[base + e] = ls_normal_bf16(vkey, idx, kappa);
+  }
+}
+
+// ------------------------------------------------------------ wrappers
+
+template <int NB>
+static const void* stage_fn(int stage) {
+  switch (stage) {
+    case kSQkv: return reinterpret_cast<const void*>(&k_qkv<NB>);
+    case kSAttn: return reinterpret_cast<const void*>(&k_attn);
+    case kSO: return reinterpret_cast<const void*>(&k_o<NB>);
+    case kSGu: return reinterpret_cast<const void*>(&k_gu<NB>);
+    case kSD: return reinterpret_cast<const void*>(&k_d<NB>);
+    case kSLm: return reinterpret_cast<const void*>(&k_lm<NB>);
+    default: return nullptr;
+  }
+}
+
+static const void* kernel_ptr(int stage, int nb) {
+  if (stage == 0) {
+    switch (nb) {
+      case 1: return reinterpret_cast<const void*>(&k_mega<1>);
+      case 2: return reinterpret_cast<const void*>(&k_mega<2>);
+      case 4: return reinterpret_cast<const void*>(&k_mega<4>);
+      default: return reinterpret_cast<const void*>(&k_mega<8>);
+    }
+  }
+  switch (nb) {
+    case 1: return stage_fn<1>(stage);
+    case 2: return stage_fn<2>(stage);
+    case 4: return stage_fn<4>(stage);
+    default: return stage_fn<8>(stage);
+  }
+}
+
+int nb_for_batch(int B) { return B <= 1 ? 1 : B <= 2 ? 2 : B <= 4 ? 4 : 8; }
+
+hipError_t launch_stage(int stage, const Params& P, int l, int grid, size_t smem,
+                        hipStream_t s) {
+  const void* fn = kernel_ptr(stage, nb_for_batch(P.S.B));
+  if (!fn) return hipErrorInvalidValue;
+  Params p = P;
+  void* args[] = {&p, &l};
+  return hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, smem, s);
+}
+
+hipError_t launch_mega(const Params& P, int grid, size_t smem, hipStream_t s) {
+  const void* fn = kernel_ptr(0, nb_for_batch(P.S.B));
+  Params p = P;
+  void* args[] = {&p};
+  return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(kThreads), args, (unsigned)smem, s);
+}
+
+hipError_t occupancy(int stage, int nb, size_t smem, int* blocks_per_cu) {
+  const void* fn = kernel_ptr(stage, nb);
+  if (!fn) return hipErrorInvalidValue;
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, fn, kThreads, smem);
+}
+
+hipError_t set_max_dynamic_smem(int stage, int nb, size_t smem) {
+  const void* fn = kernel_ptr(stage, nb);
+  if (!fn) return hipErrorInvalidValue;
+  return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+}
+
+size_t gemv_smem_bytes() { return sizeof(GemvSmem); }
+
+size_t attn_smem(int group, int d, int T) { return attn_smem_bytes(group, d, T); }
+
+hipError_t launch_gen_normal(uint16_t* dst, int64_t n, uint64_t key, uint64_t index0, float kappa,
+                             hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = (n + 255) / 256;
+  const int grid = (int)(blocks < 65536 ? blocks : 65536);
+  hipLaunchKernelGGL(k_gen_normal, dim3(grid), dim3(256), 0, s, dst, n, key, index0, kappa);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill16(uint16_t* dst, int64_t n, uint16_t v, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = (n + 255) / 256;
+  const int grid = (int)(blocks < 65536 ? blocks : 65536);
+  hipLaunchKernelGGL(k_fill16, dim3(grid), dim3(256), 0, s, dst, n, v);
+  return hipGetLastError();
+}
+
+hipError_t launch_gen_kv(uint16_t* kc, uint16_t* vc, const int* len_dev, int batch, int n_kv,
+                         int max_seq, int d, uint64_t kkey, uint64_t vkey, float kappa,
+                         hipStream_t s) {
+  const int64_t per = (int64_t)max_seq * d;
+  const int64_t bx = (per + 255) / 256;
+  const int gx = (int)(bx < 4096 ? bx : 4096);
+  hipLaunchKernelGGL(k_gen_kv, dim3(gx, batch * n_kv), dim3(256), 0, s, kc, vc, len_dev, n_kv,
+                     max_seq, d, kkey, vkey, kappa);
+  return hipGetLastError();
+}
+
+}  // namespace ld

@@ -1,0 +1,28 @@
+// ld_launch.h - launch wrappers exported by ld_kernels.hip to the host runtime.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ld_params.hpp"
+
+namespace ld {
+
+// stage: kSQkv..kSLm for the per-stage kernels, 0 for the persistent kernel.
+int nb_for_batch(int B);
+hipError_t launch_stage(int stage, const Params& P, int layer, int grid, size_t smem,
+                        hipStream_t s);
+hipError_t launch_mega(const Params& P, int grid, size_t smem, hipStream_t s);
+hipError_t occupancy(int stage, int nb, size_t smem, int* blocks_per_cu);
+hipError_t set_max_dynamic_smem(int stage, int nb, size_t smem);
+size_t gemv_smem_bytes();
+size_t attn_smem(int group, int d, int T);
+
+hipError_t launch_gen_normal(uint16_t* dst, int64_t n, uint64_t key, uint64_t index0, float kappa,
+                             hipStream_t s);
+hipError_t launch_fill16(uint16_t* dst, int64_t n, uint16_t v, hipStream_t s);
+hipError_t launch_gen_kv(uint16_t* kc, uint16_t* vc, const int* len_dev, int batch, int n_kv,
+                         int max_seq, int d, uint64_t kkey, uint64_t vkey, float kappa,
+                         hipStream_t s);
+
+}  // namespace ld

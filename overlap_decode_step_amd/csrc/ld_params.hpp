@@ -1,0 +1,82 @@
+// ld_params.hpp - argument blocks shared by the host runtime and the kernels.
+// Plain structs passed by value as kernel arguments.
+#pragma once
+
+#include <stdint.h>
+
+namespace ld {
+
+// Counter arena layout: per layer kCtrPerLayer slots, then the LM-head slot,
+// then the attention split counters [layer][seq][kv head].
+enum : int { kCQkv = 0, kCAttn = 1, kCO = 2, kCGu = 3, kCD = 4, kCtrPerLayer = 8 };
+
+// Stage ids (watchdog error codes and schedule bookkeeping).
+enum : int { kSQkv = 1, kSAttn = 2, kSO = 3, kSGu = 4, kSD = 5, kSLm = 6 };
+
+// Device error word codes (low byte; a timeout carries the stage id << 8).
+constexpr int kErrToken = 1;
+constexpr int kErrPos = 2;
+constexpr int kErrTimeout = 3;
+
+// SwiGLU tiling variants (chosen offline per batch size).
+enum : int { kGuCol = 0, kGuRow = 1 };
+
+struct Dims {
+  int L, H, nq, nkv, d, I, V, group;
+  int qd, kvd, qkv_rows;
+  int max_batch, max_seq;
+  int split_len, max_splits;
+  int tied;
+  float eps;
+  float attn_scale;  // 1 / sqrt(head_dim)
+};
+
+// Weight arena: every layer block has the same layout.
+struct Weights {
+  const uint16_t* embed;       // [V, H]
+  const uint16_t* lm;          // [V, H] (== embed when tied)
+  const uint16_t* final_norm;  // [H]
+  const uint16_t* layer0;      // first layer block
+  int64_t layer_stride;        // elements between layer blocks
+  int64_t o_attn_norm, o_wqkv, o_wo, o_mlp_norm, o_wg, o_wu, o_wd;  // offsets in a block
+};
+
+struct Work {
+  uint16_t* kc;   // K cache [L][maxB][nkv][max_seq][d]
+  uint16_t* vc;   // V cache, same layout
+  float* xa;      // residual stream after each layer [maxB][H]
+  float* xb;      // residual stream after attention [maxB][H]
+  float* qkv;     // raw q|k|v projections [maxB][qkv_rows]
+  float* ao;      // attention output [maxB][qd]
+  float* part;    // attention split partials [maxB][nq][max_splits][d + 2]
+  float* hbuf;    // SwiGLU output [maxB][I]
+  float* lm_val;  // argmax partials [max_wg][maxB]
+  int* lm_idx;
+  const float* rope;  // [max_seq][d/2][2] (cos, sin)
+  uint32_t* ctr;
+  int* err;
+  uint64_t watchdog;
+  int max_wg;
+};
+
+struct Step {
+  const int* tokens;
+  const int* pos;
+  float* logits;
+  int* next;
+  int B;
+  int wait;        // 1: whole-kernel-wait mode, stream order only (no counter waits)
+  int gu_variant;  // kGuCol / kGuRow
+  // cumulative counter targets once this step's signals are in
+  uint32_t t_qkv, t_attn, t_o, t_gu, t_d, t_lm;
+  uint32_t inject;  // debug: added to one wait target to force a watchdog timeout
+};
+
+struct Params {
+  Dims D;
+  Weights W;
+  Work K;
+  Step S;
+};
+
+}  // namespace ld

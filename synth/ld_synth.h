@@ -114,14 +114,15 @@ LS_FN int32_t ls_uniform_int(uint64_t key, uint64_t index, int32_t lo, int32_t h
   return lo + (int32_t)(((h >> 32) * span) >> 32);
 }
 
-#if !defined(__HIP_DEVICE_COMPILE__)
 #include <math.h>
 /* Scale that maps the Irwin-Hall(4) integer to standard deviation sigma.
  * Computed on the host only; the device receives the fp32 result. */
+#if defined(__HIPCC__)
+__host__
+#endif
 static inline float ls_kappa(float sigma) {
   return (float)((double)sigma / sqrt((65536.0 * 65536.0 - 1.0) / 3.0));
 }
-#endif
 
 /* bf16 bits of 1.0 (norm gains are 1.0 in every workload). */
 #define LS_BF16_ONE ((uint16_t)0x3F80u)

@@ -1,0 +1,349 @@
+"""GPU parity of the decode step against the CPU oracle, through the C ABI.
+
+Every test here calls libld.so (hand-written HIP for gfx950) through the
+ctypes binding and compares with the oracle on the same seeded inputs.
+"""
+import os
+
+import numpy as np
+import pytest
+
+from gpu_util import GpuRunner, check_row, oracle_trajectory
+from synth import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+MODES = ("wait", "flags", "mega")
+
+
+@pytest.fixture(scope="module")
+def ld():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    torch.cuda.set_device(0)
+    from overlap_decode_step_amd import ld as _ld
+    return _ld
+
+
+def gpu_model(ld, shape, max_batch, max_seq, prefill, w_std=0.02):
+    m = ld.Model(shape, seed=W.SEED_WEIGHTS, w_std=w_std)
+    m.alloc_kv(max_batch, max_seq)
+    m.fill_kv(W.SEED_KV, 1.0, prefill)
+    return m
+
+
+# ------------------------------------------------------------ generator
+
+def test_generator_weights_bit_exact(ld, orc):
+    shape = W.TINY
+    m = gpu_model(ld, shape, 2, 160, [130, 7])
+    om = orc.model(shape, seed=W.SEED_WEIGHTS, w_std=0.02)
+    from oracle import lo as L
+    pairs = [(ld.LD_W_EMBED, L.W_EMBED), (ld.LD_W_LM_HEAD, L.W_LM_HEAD),
+             (ld.LD_W_FINAL_NORM, L.W_FINAL_NORM)]
+    per_layer = [(ld.LD_W_ATTN_NORM, L.W_ATTN_NORM), (ld.LD_W_Q, L.W_Q), (ld.LD_W_K, L.W_K),
+                 (ld.LD_W_V, L.W_V), (ld.LD_W_O, L.W_O), (ld.LD_W_MLP_NORM, L.W_MLP_NORM),
+                 (ld.LD_W_GATE, L.W_GATE), (ld.LD_W_UP, L.W_UP), (ld.LD_W_DOWN, L.W_DOWN)]
+    for gk, ok in pairs:
+        assert np.array_equal(m.read_weight(gk), om.weight(ok).reshape(m.read_weight(gk).shape))
+    for layer in range(shape["n_layers"]):
+        for gk, ok in per_layer:
+            g = m.read_weight(gk, layer)
+            assert np.array_equal(g, om.weight(ok, layer).reshape(g.shape)), (gk, layer)
+    okv = orc.kv(shape, 2, 160, seed=W.SEED_KV, kv_std=1.0, prefill=[130, 7])
+    for layer in range(2):
+        for b, n in ((0, 130), (1, 7)):
+            for h in range(shape["n_kv_heads"]):
+                k, v = m.read_kv(layer, b, h, 0, n)
+                assert np.array_equal(k, okv.k(layer, b, h)[:n])
+                assert np.array_equal(v, okv.v(layer, b, h)[:n])
+    m.free()
+
+
+def test_generator_llama1b_sampled(ld, orc):
+    # The Llama-1B-shaped weights (2.5 GB) generated on the GPU equal the
+    # host generator's bytes on sampled rows of every matrix kind.
+    shape = W.LLAMA_1B
+    m = ld.Model(shape, seed=W.SEED_WEIGHTS, w_std=0.02)
+    kap = W.kappa(0.02)
+    rng = np.random.default_rng(11)
+    kinds = [(ld.LD_W_EMBED, W.T_EMBED, None), (ld.LD_W_Q, W.K_WQ, 3), (ld.LD_W_K, W.K_WK, 15),
+             (ld.LD_W_V, W.K_WV, 0), (ld.LD_W_O, W.K_WO, 7), (ld.LD_W_GATE, W.K_WG, 9),
+             (ld.LD_W_UP, W.K_WU, 1), (ld.LD_W_DOWN, W.K_WD, 12)]
+    for kind, tid, layer in kinds:
+        g = m.read_weight(kind, layer or 0)
+        tensor = tid if layer is None else W.t_layer(layer, tid)
+        key = W.key(W.SEED_WEIGHTS, tensor)
+        for idx in rng.integers(0, g.size, 16):
+            assert int(g.flat[idx]) == W.normal_bf16(key, int(idx), kap), (kind, idx)
+    m.free()
+
+
+# ---------------------------------------------------- tiny decoder parity
+
+@pytest.fixture(scope="module")
+def tiny_ref(orc):
+    shape = W.TINY
+    om = orc.model(shape, seed=W.SEED_WEIGHTS, w_std=0.02)
+    okv = orc.kv(shape, 1, 256, seed=W.SEED_KV, kv_std=1.0, prefill=[128])
+    tok0 = W.first_tokens(1, shape["vocab"])[0]
+    return oracle_trajectory(orc, om, okv, tok0, 128, 16)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_tiny_16_steps(ld, tiny_ref, mode):
+    shape = W.TINY
+    m = gpu_model(ld, shape, 1, 256, [128])
+    m.set_mode(mode)
+    run = GpuRunner(m, shape["vocab"], 1)
+    for s, (tok, pos, ref, ref_next) in enumerate(tiny_ref):
+        lg, nx = run.step([tok], [pos])
+        check_row(lg[0], ref, nx[0], ref_next, f"mode={mode} step={s}")
+    # the appended K/V rows equal bf16 of what the oracle appended (rows 128..143)
+    m.free()
+
+
+def test_modes_bitwise_equal_and_rerun(ld, tiny_ref):
+    shape = W.TINY
+    outs = {}
+    m = gpu_model(ld, shape, 1, 256, [128])
+    run = GpuRunner(m, shape["vocab"], 1)
+    for mode in MODES + ("mega",):
+        m.fill_kv(W.SEED_KV, 1.0, [128])
+        m.set_mode(mode)
+        seq = [run.step([tok], [pos])[0] for tok, pos, _, _ in tiny_ref[:6]]
+        if mode in outs:
+            assert all(np.array_equal(a, b) for a, b in zip(outs[mode], seq)), "rerun differs"
+        outs[mode] = seq
+    for mode in MODES[1:]:
+        for a, b in zip(outs["wait"], outs[mode]):
+            assert np.array_equal(a, b), f"{mode} differs from wait"
+    m.free()
+
+
+def test_tiny_appended_kv_matches_oracle(ld, orc, tiny_ref):
+    shape = W.TINY
+    om = orc.model(shape, seed=W.SEED_WEIGHTS, w_std=0.02)
+    okv = orc.kv(shape, 1, 256, seed=W.SEED_KV, kv_std=1.0, prefill=[128])
+    m = gpu_model(ld, shape, 1, 256, [128])
+    m.set_mode("mega")
+    run = GpuRunner(m, shape["vocab"], 1)
+    for tok, pos, _, _ in tiny_ref[:4]:
+        orc.decode_one(om, okv, 0, tok, pos)
+        run.step([tok], [pos])
+    for layer in range(2):
+        for h in range(2):
+            k, v = m.read_kv(layer, 0, h, 128, 4)
+            kr = okv.k(layer, 0, h)[128:132]
+            vr = okv.v(layer, 0, h)[128:132]
+            # bf16 rounding of nearly equal fp32 values: at most one ulp apart
+            dk = np.abs(k.astype(np.int32) - kr.astype(np.int32))
+            dv = np.abs(v.astype(np.int32) - vr.astype(np.int32))
+            assert dk.max() <= 1 and dv.max() <= 1
+            assert (dk == 0).mean() > 0.95 and (dv == 0).mean() > 0.95
+    m.free()
+
+
+# ------------------------------------------------ ragged shapes and batches
+
+RAGGED = W.shape(3, 136, 6, 2, 8, 200, 1000, 0, 1e-5, 10000.0)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_ragged_shape_multi_split(ld, orc, mode):
+    # hidden 136 and intermediate 200 leave ragged 512-element chunks, 1000
+    # vocab rows leave a ragged row tile, and positions 150..152 span three
+    # 64-position attention splits with a ragged last split.
+    shape = RAGGED
+    B, prefill = 3, [150, 64, 1]
+    om = orc.model(shape, seed=W.SEED_WEIGHTS, w_std=0.05)
+    m = gpu_model(ld, shape, B, 200, prefill, w_std=0.05)
+    m.set_mode(mode)
+    run = GpuRunner(m, shape["vocab"], B)
+    okvs = [orc.kv(shape, 1, 200, seed=W.SEED_KV, kv_std=1.0, prefill=[prefill[b]], seq0=b)
+            for b in range(B)]
+    toks = W.first_tokens(B, shape["vocab"])
+    for s in range(3):
+        pos = [prefill[b] + s for b in range(B)]
+        lg, nx = run.step(toks, pos)
+        new = []
+        for b in range(B):
+            ref, rn = orc.decode_one(om, okvs[b], 0, toks[b], pos[b])
+            check_row(lg[b], ref, nx[b], rn, f"mode={mode} step={s} seq={b}")
+            new.append(rn)
+        toks = new
+    m.free()
+
+
+@pytest.mark.parametrize("B", [2, 5, 16])
+def test_tiny_batches(ld, orc, B):
+    shape = W.TINY
+    prefill = W.kv_lengths(B, 1, 200)
+    om = orc.model(shape, seed=W.SEED_WEIGHTS, w_std=0.02)
+    m = gpu_model(ld, shape, B, 256, prefill)
+    run = GpuRunner(m, shape["vocab"], B)
+    okvs = [orc.kv(shape, 1, 256, seed=W.SEED_KV, kv_std=1.0, prefill=[prefill[b]], seq0=b)
+            for b in range(B)]
+    toks = W.first_tokens(B, shape["vocab"])
+    for mode in MODES:
+        m.fill_kv(W.SEED_KV, 1.0, prefill)
+        m.set_mode(mode)
+        for b in range(B):
+            okvs[b] = orc.kv(shape, 1, 256, seed=W.SEED_KV, kv_std=1.0, prefill=[prefill[b]],
+                             seq0=b)
+        t = list(toks)
+        for s in range(2):
+            pos = [prefill[b] + s for b in range(B)]
+            lg, nx = run.step(t, pos)
+            new = []
+            for b in range(B):
+                ref, rn = orc.decode_one(om, okvs[b], 0, t[b], pos[b])
+                check_row(lg[b], ref, nx[b], rn, f"B={B} mode={mode} step={s} seq={b}")
+                new.append(rn)
+            t = new
+    m.free()
+
+
+# ------------------------------------------------- Llama-1B-shaped decoder
+
+@pytest.fixture(scope="module")
+def llama1b(ld, orc):
+    shape = W.LLAMA_1B
+    om = orc.model(shape, seed=W.SEED_WEIGHTS, w_std=0.02)
+    return shape, om
+
+
+def test_llama1b_batch1_parity(ld, orc, llama1b):
+    shape, om = llama1b
+    okv = orc.kv(shape, 1, 640, seed=W.SEED_KV, kv_std=1.0, prefill=[512])
+    tok0 = W.first_tokens(1, shape["vocab"])[0]
+    ref = oracle_trajectory(orc, om, okv, tok0, 512, 2)
+    m = gpu_model(ld, shape, 1, 640, [512])
+    run = GpuRunner(m, shape["vocab"], 1)
+    for mode in MODES:
+        m.fill_kv(W.SEED_KV, 1.0, [512])
+        m.set_mode(mode)
+        for s, (tok, pos, lg_ref, nref) in enumerate(ref):
+            lg, nx = run.step([tok], [pos])
+            err, rel, _ = check_row(lg[0], lg_ref, nx[0], nref, f"mode={mode} step={s}")
+            print(f"llama1b B=1 mode={mode} step={s} max_abs={err:.2e} rel={rel:.2e}", flush=True)
+    m.free()
+
+
+@pytest.mark.parametrize("B", [4, 16, 64])
+def test_llama1b_batch_sweep_sampled(ld, orc, llama1b, B):
+    # Short-context sweep: KV length ~U[256, 1024] per sequence; the oracle
+    # checks sequences 0 and B-1 of one step in the tile-flag and persistent modes.
+    shape, om = llama1b
+    prefill = W.kv_lengths(B, 256, 1024)
+    toks = W.first_tokens(B, shape["vocab"])
+    m = gpu_model(ld, shape, B, 1040, prefill)
+    run = GpuRunner(m, shape["vocab"], B)
+    refs = {}
+    for b in sorted({0, B - 1}):
+        okv = orc.kv(shape, 1, 1040, seed=W.SEED_KV, kv_std=1.0, prefill=[prefill[b]], seq0=b)
+        refs[b] = orc.decode_one(om, okv, 0, toks[b], prefill[b])
+    for mode in ("flags", "mega"):
+        m.fill_kv(W.SEED_KV, 1.0, prefill)
+        m.set_mode(mode)
+        lg, nx = run.step(toks, prefill)
+        for b, (ref, rn) in refs.items():
+            err, rel, _ = check_row(lg[b], ref, nx[b], rn, f"B={B} mode={mode} seq={b}")
+            print(f"llama1b B={B} mode={mode} seq={b} max_abs={err:.2e} rel={rel:.2e}", flush=True)
+    m.free()
+
+
+# ------------------------------------------------------ errors and faults
+
+def test_host_argument_errors(ld):
+    import torch
+    shape = W.TINY
+    m = ld.Model(shape, seed=1, w_std=0.02)
+    dev = torch.device("cuda:0")
+    t = torch.zeros(2, dtype=torch.int32, device=dev)
+    lg = torch.empty((2, shape["vocab"]), dtype=torch.float32, device=dev)
+    with pytest.raises(ld.LdError) as e:  # decode before ld_alloc_kv
+        m.step(t, t, lg)
+    assert e.value.status == ld.LD_ESTATE
+    m.alloc_kv(2, 64)
+    with pytest.raises(ld.LdError) as e:
+        ld.ld_decode_step(m.h, t.data_ptr(), 3, t.data_ptr(), lg.data_ptr(), None, 0)
+    assert e.value.status == ld.LD_EINVAL
+    with pytest.raises(ld.LdError) as e:
+        ld.ld_decode_step(m.h, None, 1, t.data_ptr(), lg.data_ptr(), None, 0)
+    assert e.value.status == ld.LD_EINVAL
+    with pytest.raises(ld.LdError) as e:
+        ld.ld_set_mode(m.h, 7)
+    assert e.value.status == ld.LD_EINVAL
+    with pytest.raises(ld.LdError):
+        ld.ld_fill_kv(m.h, 2, 1.0, [65, 0], 0)  # prefill beyond max_seq
+    bad = dict(shape, head_dim=60)
+    assert ld.ld_weights_bytes(bad) == 0
+    m.free()
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_device_input_errors(ld, mode):
+    import torch
+    shape = W.TINY
+    m = gpu_model(ld, shape, 1, 64, [10])
+    m.set_mode(mode)
+    dev = torch.device("cuda:0")
+    lg = torch.empty((1, shape["vocab"]), dtype=torch.float32, device=dev)
+    m.step(torch.tensor([shape["vocab"]], dtype=torch.int32, device=dev),
+           torch.tensor([10], dtype=torch.int32, device=dev), lg)
+    assert m.device_error() == ld.LD_EDEVICE
+    m.step(torch.tensor([3], dtype=torch.int32, device=dev),
+           torch.tensor([64], dtype=torch.int32, device=dev), lg)
+    assert m.device_error() == ld.LD_EDEVICE
+    m.step(torch.tensor([3], dtype=torch.int32, device=dev),
+           torch.tensor([10], dtype=torch.int32, device=dev), lg)
+    assert m.device_error() == ld.LD_OK
+    m.free()
+
+
+@pytest.mark.parametrize("mode", ["flags", "mega"])
+def test_watchdog_turns_a_stall_into_an_error(ld, tiny_ref, mode):
+    # The host makes one wait target unreachable; the bounded wait must end
+    # the step with LD_ETIMEOUT instead of hanging, and the next step is exact.
+    shape = W.TINY
+    m = gpu_model(ld, shape, 1, 256, [128])
+    m.set_mode(mode)
+    ld.ld_set_watchdog(m.h, 0.05)
+    run = GpuRunner(m, shape["vocab"], 1)
+    ld.ld_debug_inject_stall(m.h)
+    import torch
+    dev = torch.device("cuda:0")
+    lg = torch.empty((1, shape["vocab"]), dtype=torch.float32, device=dev)
+    tok, pos, ref, rn = tiny_ref[0]
+    m.step(torch.tensor([tok], dtype=torch.int32, device=dev),
+           torch.tensor([pos], dtype=torch.int32, device=dev), lg)
+    assert m.device_error() == ld.LD_ETIMEOUT
+    m.fill_kv(W.SEED_KV, 1.0, [128])
+    lg2, nx = run.step([tok], [pos])
+    check_row(lg2[0], ref, nx[0], rn, f"after timeout mode={mode}")
+    m.free()
+
+
+def test_tuning_table_roundtrip(ld, tmp_path, tiny_ref):
+    shape = W.TINY
+    m = gpu_model(ld, shape, 16, 256, [128] * 16)
+    path = str(tmp_path / "tune.json")
+    ld.ld_tune(m.h, [1, 4, 16], path)
+    txt = open(path).read()
+    assert '"swiglu"' in txt and '"16"' in txt
+    chosen = {b: ld.ld_get_swiglu_variant(m.h, b) for b in (1, 4, 16)}
+    for b in (1, 4, 16):
+        ld.ld_set_swiglu_variant(m.h, b, 1 - chosen[b])
+    ld.ld_load_tuning(m.h, path)
+    assert {b: ld.ld_get_swiglu_variant(m.h, b) for b in (1, 4, 16)} == chosen
+    # both tilings compute the same sums in the same order: bitwise equal logits
+    run = GpuRunner(m, shape["vocab"], 16)
+    toks = W.first_tokens(16, shape["vocab"])
+    outs = []
+    for variant in (ld.LD_SWIGLU_COL, ld.LD_SWIGLU_ROW):
+        ld.ld_set_swiglu_variant(m.h, 16, variant)
+        m.fill_kv(W.SEED_KV, 1.0, [128] * 16)
+        outs.append(run.step(toks, [128] * 16)[0])
+    assert np.array_equal(outs[0], outs[1])
+    m.free()
