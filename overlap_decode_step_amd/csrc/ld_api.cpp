@@ -38,16 +38,20 @@ struct ld_model {
   hipEvent_t ev_fork = nullptr, ev_join = nullptr;
   // cumulative counter totals (what every layer's counter will read once all
   // enqueued steps have finished)
-  uint32_t tot_qkv = 0, tot_attn = 0, tot_o = 0, tot_gu = 0, tot_d = 0, tot_lm = 0;
+  uint32_t tot_qkv = 0, tot_attn = 0, tot_o = 0, tot_gu = 0, tot_d = 0;
   int gu_variant[65];
   bool gu_tuned[65];
+  // launch geometry per mode: grid, threads per workgroup, LDS bytes, LDS for staged inputs
   int grid_wait = 0, grid_flags = 0, grid_mega[9] = {0};  // grid_mega indexed by nb
-  int grid_attn_flags = 0;
-  size_t smem_attn = 0, smem_mega = 0;
+  int thr_wait = 1024, thr_flags = 512, thr_mega = 1024;
+  size_t smem_wait = 0, smem_flags = 0, smem_mega = 0;
+  uint32_t xcap_wait = 0, xcap_flags = 0, xcap_mega = 0;
+  bool flags_ok = true;
   uint64_t watchdog_ticks = 0;
   double wall_khz = 100000.0;
   uint32_t inject_next = 0;
   uint32_t* tune_ctr = nullptr;  // counter slots for standalone tuning launches
+  size_t ctr_bytes = 0;          // bytes of all counters (stage, LM, split)
   std::string err;
 };
 
@@ -147,7 +151,8 @@ extern "C" size_t ld_weights_bytes(const ld_config* cfg) {
 
 // KV + workspace arena layout (byte offsets).
 struct KLayout {
-  size_t kc, vc, xa, xb, qkv, ao, part, hbuf, lm_val, lm_idx, rope, ctr, err, tune_ctr, total;
+  size_t kc, vc, xa, xb, qkv, ao, part, hbuf, lm_val, lm_idx, rope, ctr, lm_ctr, split_ctr, err,
+      tune_ctr, total;
   int split_len, max_splits, max_wg;
 };
 
@@ -178,10 +183,13 @@ static KLayout klayout(const ld_config* c, int maxB, int max_seq) {
   K.lm_val = take((size_t)K.max_wg * maxB * 4);
   K.lm_idx = take((size_t)K.max_wg * maxB * 4);
   K.rope = take((size_t)max_seq * (d / 2) * 2 * 4);
-  K.ctr = take(((size_t)c->n_layers * kCtrPerLayer + 8 + (size_t)c->n_layers * maxB * c->n_kv_heads) *
-               4);
+  // counters: contiguous so they can be cleared together
+  K.ctr = take((size_t)c->n_layers * kStageCtrs * kCtrWords * 4);
+  K.lm_ctr = take((size_t)kCtrWords * 4);
+  K.split_ctr = take((size_t)c->n_layers * maxB * c->n_kv_heads * 16 * 4);
   K.err = take(256);
-  K.tune_ctr = take(((size_t)kCtrPerLayer * 2 + 8 + (size_t)maxB * c->n_kv_heads) * 4);
+  // private counters of standalone tuning launches (one layer's worth)
+  K.tune_ctr = take(((size_t)kStageCtrs * kCtrWords + kCtrWords + (size_t)maxB * c->n_kv_heads * 16) * 4);
   K.total = off;
   return K;
 }
@@ -307,33 +315,46 @@ extern "C" ld_status ld_init_weights(ld_model** out, const ld_config* cfg, void*
   return LD_OK;
 }
 
+// LDS bytes available per CU, and the scratch area every decode kernel uses.
+static const size_t kLdsPerCu = 160 * 1024;
+
 static ld_status compute_grids(ld_model* m) {
-  const int maxnb = nb_for_batch(m->D.max_batch);
-  m->smem_attn = attn_smem(m->D.group, m->D.d, m->D.split_len);
-  const size_t gs = gemv_smem_bytes();
-  m->smem_mega = std::max(m->smem_attn, gs);
-  if (m->smem_attn > 160 * 1024 || m->smem_mega > 160 * 1024)
-    return fail(m, LD_EINVAL, "attention tile does not fit in LDS");
-  HIPCHK(m, set_max_dynamic_smem(kSAttn, 1, m->smem_attn));
-  // per-stage kernels: the smallest occupancy over stages and batch tiles
-  int occ_min = 1 << 30;
+  const Dims& D = m->D;
+  const int maxnb = nb_for_batch(D.max_batch);
+  const size_t scratch = scratch_bytes();
+  const size_t attn = attn_smem(D.group, D.d, D.split_len);
+  const size_t kmax = (size_t)std::max(std::max(D.H, D.I), D.qd) * 4;  // longest staged input row
+  // whole-kernel wait and persistent modes: one 1024-thread workgroup per CU
+  const uint32_t xcap_full = 128 * 1024;
+  if (kmax > xcap_full) return fail(m, LD_EINVAL, "input rows longer than the LDS staging area");
+  m->xcap_wait = m->xcap_mega = xcap_full;
+  m->smem_wait = m->smem_mega = scratch + std::max<size_t>(xcap_full, attn);
+  // tile-flag mode: two consecutive stage kernels share each CU, so each
+  // 512-thread workgroup gets at most half the LDS
+  const size_t half = kLdsPerCu / 2;
+  m->xcap_flags = (uint32_t)(half - scratch);
+  m->smem_flags = scratch + std::max<size_t>(m->xcap_flags, attn);
+  m->flags_ok = (kmax <= m->xcap_flags) && (m->smem_flags <= half);
+  if (m->smem_mega > kLdsPerCu) return fail(m, LD_EINVAL, "attention tile does not fit in LDS");
   for (int nb = 1; nb <= maxnb; nb *= 2) {
-    for (int st = kSQkv; st <= kSLm; ++st) {
-      int occ = 0;
-      const size_t sm = (st == kSAttn) ? m->smem_attn : 0;
-      HIPCHK(m, occupancy(st, nb, sm, &occ));
-      occ_min = std::min(occ_min, std::max(occ, 1));
+    for (int st = 0; st <= kSLm; ++st) {
+      const size_t sm = (st == 0) ? m->smem_mega : std::max(m->smem_wait, m->smem_flags);
+      HIPCHK(m, set_max_dynamic_smem(st, nb, sm));
     }
-    int occm = 0;
-    HIPCHK(m, set_max_dynamic_smem(0, nb, m->smem_mega));
-    HIPCHK(m, occupancy(0, nb, m->smem_mega, &occm));
-    if (occm < 1) return fail(m, LD_EINVAL, "persistent kernel does not fit on a CU");
-    m->grid_mega[nb] = std::min(occm * m->n_cu, m->K.max_wg);
+    int occ = 0;
+    HIPCHK(m, occupancy(0, nb, m->thr_mega, m->smem_mega, &occ));
+    if (occ < 1) return fail(m, LD_EINVAL, "persistent kernel does not fit on a CU");
+    m->grid_mega[nb] = std::min(occ * m->n_cu, m->K.max_wg);
+    for (int st = kSQkv; st <= kSLm; ++st) {
+      int o1 = 0, o2 = 0;
+      HIPCHK(m, occupancy(st, nb, m->thr_wait, m->smem_wait, &o1));
+      HIPCHK(m, occupancy(st, nb, m->thr_flags, m->smem_flags, &o2));
+      if (o1 < 1) return fail(m, LD_EINVAL, "stage kernel does not fit on a CU");
+      if (o2 < 2) m->flags_ok = false;  // two tile-flag kernels must fit side by side
+    }
   }
-  m->grid_wait = std::min(occ_min * m->n_cu, m->K.max_wg);
-  // tile-flag mode: two kernels in flight, each may hold at most half the machine
-  m->grid_flags = std::max(1, occ_min / 2) * m->n_cu;
-  m->grid_attn_flags = m->grid_flags;
+  m->grid_wait = m->n_cu;
+  m->grid_flags = m->n_cu;
   return LD_OK;
 }
 
@@ -369,7 +390,10 @@ extern "C" ld_status ld_alloc_kv(ld_model* m, void* dev_buf, size_t bytes, int32
   K.lm_idx = reinterpret_cast<int*>(base + KL.lm_idx);
   K.rope = reinterpret_cast<const float*>(base + KL.rope);
   K.ctr = reinterpret_cast<uint32_t*>(base + KL.ctr);
+  K.lm_ctr = reinterpret_cast<uint32_t*>(base + KL.lm_ctr);
+  K.split_ctr = reinterpret_cast<uint32_t*>(base + KL.split_ctr);
   K.err = reinterpret_cast<int*>(base + KL.err);
+  m->ctr_bytes = KL.err - KL.ctr;
   K.max_wg = KL.max_wg;
   m->tune_ctr = reinterpret_cast<uint32_t*>(base + KL.tune_ctr);
   m->D.max_batch = max_batch;
@@ -390,7 +414,7 @@ extern "C" ld_status ld_alloc_kv(ld_model* m, void* dev_buf, size_t bytes, int32
       rope[((size_t)p * half + i) * 2 + 1] = (float)std::sin(a);
     }
   HIPCHK(m, hipMemcpy(base + KL.rope, rope.data(), rope.size() * 4, hipMemcpyHostToDevice));
-  m->tot_qkv = m->tot_attn = m->tot_o = m->tot_gu = m->tot_d = m->tot_lm = 0;
+  m->tot_qkv = m->tot_attn = m->tot_o = m->tot_gu = m->tot_d = 0;
   ld_status st = compute_grids(m);
   if (st != LD_OK) return st;
   m->K.watchdog = m->watchdog_ticks;
@@ -427,6 +451,8 @@ extern "C" ld_status ld_set_mode(ld_model* m, ld_mode mode) {
   if (!m) return fail(nullptr, LD_EINVAL, "null model");
   if (mode != LD_MODE_WAIT && mode != LD_MODE_FLAGS && mode != LD_MODE_MEGA)
     return fail(m, LD_EINVAL, "unknown mode");
+  if (mode == LD_MODE_FLAGS && m->kv_ready && !m->flags_ok)
+    return fail(m, LD_EINVAL, "tile-flag mode cannot keep two stage kernels of this shape on a CU");
   m->mode = mode;
   return LD_OK;
 }
@@ -453,52 +479,54 @@ static ld_status enqueue_step(ld_model* m, const int32_t* tokens, int32_t B, con
   m->inject_next = 0;
   const int L = m->D.L;
   const uint32_t attn_inc = (uint32_t)(B * m->D.nkv);
-  if (m->mode == LD_MODE_MEGA) {
-    const int nb = nb_for_batch(B);
-    const int g = m->grid_mega[nb];
+  auto add_targets = [&](int g) {
     m->tot_qkv += g;
     m->tot_attn += attn_inc;
     m->tot_o += g;
     m->tot_gu += g;
     m->tot_d += g;
-    m->tot_lm += g;
+    P.S.t_qkv = m->tot_qkv;
+    P.S.t_attn = m->tot_attn;
+    P.S.t_o = m->tot_o;
+    P.S.t_gu = m->tot_gu;
+    P.S.t_d = m->tot_d;
+  };
+  if (m->mode == LD_MODE_MEGA) {
+    const int g = m->grid_mega[nb_for_batch(B)];
+    add_targets(g);
     P.S.wait = 0;
-    P.S.t_qkv = m->tot_qkv; P.S.t_attn = m->tot_attn; P.S.t_o = m->tot_o;
-    P.S.t_gu = m->tot_gu; P.S.t_d = m->tot_d; P.S.t_lm = m->tot_lm;
-    HIPCHK(m, launch_mega(P, g, m->smem_mega, s0));
+    P.S.x_cap = m->xcap_mega;
+    HIPCHK(m, launch_mega(P, g, m->thr_mega, m->smem_mega, s0));
     return LD_OK;
   }
   const bool flags = (m->mode == LD_MODE_FLAGS);
+  if (flags && !m->flags_ok)
+    return fail(m, LD_EINVAL, "tile-flag mode cannot keep two stage kernels of this shape on a CU");
   const int g = flags ? m->grid_flags : m->grid_wait;
-  const int ga = flags ? m->grid_attn_flags : m->grid_wait;
-  m->tot_qkv += g;
-  m->tot_attn += attn_inc;
-  m->tot_o += g;
-  m->tot_gu += g;
-  m->tot_d += g;
-  m->tot_lm += g;
+  const int thr = flags ? m->thr_flags : m->thr_wait;
+  const size_t smem = flags ? m->smem_flags : m->smem_wait;
+  if (flags) add_targets(g);  // whole-kernel-wait kernels do not signal
   P.S.wait = flags ? 0 : 1;
-  P.S.t_qkv = m->tot_qkv; P.S.t_attn = m->tot_attn; P.S.t_o = m->tot_o;
-  P.S.t_gu = m->tot_gu; P.S.t_d = m->tot_d; P.S.t_lm = m->tot_lm;
+  P.S.x_cap = flags ? m->xcap_flags : m->xcap_wait;
   hipStream_t ss[2] = {s0, m->s1};
   if (flags) {
     HIPCHK(m, hipEventRecord(m->ev_fork, s0));
     HIPCHK(m, hipStreamWaitEvent(m->s1, m->ev_fork, 0));
   }
   int k = 0;
-  auto launch = [&](int stage, int l, int grid, size_t smem) -> hipError_t {
+  auto launch = [&](int stage, int l) -> hipError_t {
     hipStream_t s = flags ? ss[k & 1] : s0;
     ++k;
-    return launch_stage(stage, P, l, grid, smem, s);
+    return launch_stage(stage, P, l, g, thr, smem, s);
   };
   for (int l = 0; l < L; ++l) {
-    HIPCHK(m, launch(kSQkv, l, g, 0));
-    HIPCHK(m, launch(kSAttn, l, ga, m->smem_attn));
-    HIPCHK(m, launch(kSO, l, g, 0));
-    HIPCHK(m, launch(kSGu, l, g, 0));
-    HIPCHK(m, launch(kSD, l, g, 0));
+    HIPCHK(m, launch(kSQkv, l));
+    HIPCHK(m, launch(kSAttn, l));
+    HIPCHK(m, launch(kSO, l));
+    HIPCHK(m, launch(kSGu, l));
+    HIPCHK(m, launch(kSD, l));
   }
-  HIPCHK(m, launch(kSLm, 0, g, 0));
+  HIPCHK(m, launch(kSLm, 0));
   if (flags) {
     HIPCHK(m, hipEventRecord(m->ev_join, m->s1));
     HIPCHK(m, hipStreamWaitEvent(s0, m->ev_join, 0));
@@ -532,10 +560,9 @@ extern "C" ld_status ld_device_error(ld_model* m) {
   const int code = w & 0xFF, stage = w >> 8;
   if (code == kErrTimeout) {
     // the counters no longer match the host's totals: reset both
-    const size_t nctr = (size_t)m->D.L * kCtrPerLayer + 8 + (size_t)m->D.L * m->D.max_batch * m->D.nkv;
-    HIPCHK(m, hipMemset(m->K.ctr, 0, nctr * 4));
+    HIPCHK(m, hipMemset(m->K.ctr, 0, m->ctr_bytes));
     HIPCHK(m, hipDeviceSynchronize());
-    m->tot_qkv = m->tot_attn = m->tot_o = m->tot_gu = m->tot_d = m->tot_lm = 0;
+    m->tot_qkv = m->tot_attn = m->tot_o = m->tot_gu = m->tot_d = 0;
     char buf[96];
     snprintf(buf, sizeof buf, "device wait timed out in stage %d", stage);
     return fail(m, LD_ETIMEOUT, buf);
@@ -563,17 +590,24 @@ extern "C" void ld_free(ld_model* m) {
 // Time one standalone SwiGLU launch of layer 0 with the given variant.
 static ld_status time_gu(ld_model* m, int B, int variant, int reps, float* ms_out) {
   Params P = make_params(m);
-  P.K.ctr = m->tune_ctr;  // private counters: never disturbs the decode totals
+  // private counters: never disturbs the decode totals (whole-kernel-wait
+  // launches of one stage do not signal anyway)
+  P.K.ctr = m->tune_ctr;
+  P.K.lm_ctr = m->tune_ctr + kStageCtrs * kCtrWords;
+  P.K.split_ctr = P.K.lm_ctr + kCtrWords;
   P.S.B = B;
   P.S.wait = 1;
   P.S.gu_variant = variant;
+  P.S.x_cap = m->xcap_wait;
   hipStream_t s = nullptr;
   hipEvent_t a, b;
   HIPCHK(m, hipEventCreate(&a));
   HIPCHK(m, hipEventCreate(&b));
-  for (int i = 0; i < 2; ++i) HIPCHK(m, launch_stage(kSGu, P, 0, m->grid_wait, 0, s));
+  for (int i = 0; i < 2; ++i)
+    HIPCHK(m, launch_stage(kSGu, P, 0, m->grid_wait, m->thr_wait, m->smem_wait, s));
   HIPCHK(m, hipEventRecord(a, s));
-  for (int i = 0; i < reps; ++i) HIPCHK(m, launch_stage(kSGu, P, 0, m->grid_wait, 0, s));
+  for (int i = 0; i < reps; ++i)
+    HIPCHK(m, launch_stage(kSGu, P, 0, m->grid_wait, m->thr_wait, m->smem_wait, s));
   HIPCHK(m, hipEventRecord(b, s));
   HIPCHK(m, hipEventSynchronize(b));
   float ms = 0.f;
@@ -619,7 +653,6 @@ extern "C" ld_status ld_tune(ld_model* m, const int32_t* batches, int32_t n, con
     m->gu_variant[B] = (t_row < t_col) ? kGuRow : kGuCol;
     m->gu_tuned[B] = true;
   }
-  HIPCHK(m, hipMemset(m->tune_ctr, 0, 4 * ((size_t)kCtrPerLayer * 2 + 8)));
   HIPCHK(m, hipDeviceSynchronize());
   if (table_path) return write_table(m, table_path);
   return LD_OK;
@@ -772,7 +805,7 @@ extern "C" ld_status ld_launch_info(const ld_model* m, int32_t* out, int32_t n) 
   if (!m || !out || n < 6) return LD_EINVAL;
   out[0] = m->n_cu;
   out[1] = m->grid_wait;
-  out[2] = m->grid_flags;
+  out[2] = m->flags_ok ? m->grid_flags : 0;
   out[3] = m->grid_mega[1];
   out[4] = m->D.split_len;
   out[5] = (int32_t)m->mode;

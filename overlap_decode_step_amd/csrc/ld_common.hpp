@@ -1,6 +1,6 @@
 // ld_common.hpp - shared device definitions for the decode-step kernels
-// (gfx950, wave64): bf16 helpers, wave reductions, readiness counters and
-// the argument blocks every stage reads.
+// (gfx950, wave64): bf16 helpers, wave reductions, coherent loads/stores and
+// the readiness counters every stage uses.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -11,9 +11,14 @@
 namespace ld {
 
 constexpr int kWave = 64;
-constexpr int kWaves = 4;                 // waves per workgroup
-constexpr int kThreads = kWave * kWaves;  // 256 threads per workgroup
-constexpr int kChunk = kWave * 8;         // bf16 elements covered by one 16-byte load per lane
+constexpr int kMaxWaves = 16;              // waves per workgroup at most (1024 threads)
+constexpr int kChunk = kWave * 8;          // bf16 elements covered by one 16-byte load per lane
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int nwaves() { return blockDim.x >> 6; }
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
 // ----------------------------------------------------------------- bf16
 
@@ -21,25 +26,12 @@ __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w <
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 __device__ __forceinline__ float bf16f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
-// fp32 -> bf16 bits, round to nearest even (finite inputs; NaN kept quiet).
+// fp32 -> bf16 bits, round to nearest even (NaN kept quiet).
 __device__ __forceinline__ uint16_t f2bf(float f) {
   uint32_t u = __float_as_uint(f);
   if ((u & 0x7F800000u) == 0x7F800000u) return (uint16_t)((u >> 16) | ((u & 0x7FFFFFu) ? 0x40u : 0u));
   u += 0x7FFFu + ((u >> 16) & 1u);
   return (uint16_t)(u >> 16);
-}
-
-// Eight bf16 (one 16-byte word) dotted with eight floats, accumulated in order.
-__device__ __forceinline__ float dot8(const uint4& w, const float* x, float acc) {
-  acc = fmaf(bf16lo(w.x), x[0], acc);
-  acc = fmaf(bf16hi(w.x), x[1], acc);
-  acc = fmaf(bf16lo(w.y), x[2], acc);
-  acc = fmaf(bf16hi(w.y), x[3], acc);
-  acc = fmaf(bf16lo(w.z), x[4], acc);
-  acc = fmaf(bf16hi(w.z), x[5], acc);
-  acc = fmaf(bf16lo(w.w), x[6], acc);
-  acc = fmaf(bf16hi(w.w), x[7], acc);
-  return acc;
 }
 
 // ------------------------------------------------------------ reductions
@@ -56,36 +48,65 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-// Sum over the workgroup; every thread gets the result.  `red` holds kWaves floats.
-__device__ __forceinline__ float block_sum(float v, float* red) {
-  v = wave_sum(v);
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  __syncthreads();
-  if (lane == 0) red[wave] = v;
-  __syncthreads();
-  float s = 0.f;
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) s += red[w];
-  return s;
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+// ------------------------------------------- coherent (agent-scope) access
+//
+// Activations, partial results and counters pass between workgroups that may
+// sit on different XCDs, each with its own L2.  They are written with
+// agent-scope stores (write-through past the non-coherent L2) and read with
+// agent-scope loads (which miss any stale L2 copy), so no L2 write-back or
+// invalidate is needed at each hand-off; weights are read-only and use
+// ordinary non-temporal loads.
+
+__device__ __forceinline__ void st_coh(float* p, float v) {
+  __hip_atomic_store(reinterpret_cast<uint32_t*>(p), __float_as_uint(v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_coh_i(int* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_coh(const float* p) {
+  return __uint_as_float(__hip_atomic_load(reinterpret_cast<const uint32_t*>(p), __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT));
+}
+__device__ __forceinline__ int ld_coh_i(const int* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// eight consecutive floats (32-byte aligned) through four 64-bit coherent loads
+__device__ __forceinline__ void ld_coh8(const float* p, float* o) {
+  const uint64_t* q = reinterpret_cast<const uint64_t*>(p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint64_t v = __hip_atomic_load(q + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    o[2 * i] = __uint_as_float((uint32_t)v);
+    o[2 * i + 1] = __uint_as_float((uint32_t)(v >> 32));
+  }
 }
 
 // ------------------------------------------------- readiness counters
 //
-// A producer workgroup writes its tiles, passes a workgroup barrier (which
-// waits for every wave's stores), and one thread adds 1 to the counter with
-// release semantics at agent scope.  A consumer's first thread spins on an
-// acquire load until the counter reaches the cumulative target of this step
-// (counters only grow; targets are compared modulo 2^32), then releases the
-// workgroup through a barrier.  This is the tile-level hand-off between
-// dependent kernels of the MegaOps summary ("In plain words": a later kernel
-// starts once the pieces of shared data it needs are ready).  The spin is
-// bounded by a watchdog: on timeout (or once another workgroup has timed
-// out) it records an error and returns, so every kernel always exits.
+// A stage signals completion through 16 "leaf" counters, each on its own
+// 128-byte line; workgroup w adds 1 to leaf w % 16 once its outputs are
+// stored, and a consumer sums the leaves (one wave-wide load) and compares
+// with the cumulative number of signals expected by the end of this step
+// (counters only grow; comparisons are modulo 2^32).  This is the tile-level
+// hand-off between dependent stages of the MegaOps summary ("In plain
+// words": a later kernel starts once the pieces of shared data it needs are
+// ready).  Ordering: every wave waits for its own stores to complete
+// (s_waitcnt 0), the workgroup barrier makes that true for all waves, then
+// one relaxed atomic add publishes it; the consumer issues its data loads
+// only after it has seen the count.  The spin is bounded by a watchdog: on
+// timeout, or once another workgroup has timed out, it records an error and
+// returns, so every kernel always exits.
 
 struct SyncArgs {
-  uint32_t* ctr;        // counter arena
-  int* err;             // device error word
-  uint64_t watchdog;    // spin limit in s_memrealtime ticks (100 MHz)
+  int* err;           // device error word
+  uint64_t watchdog;  // spin limit in s_memrealtime ticks (100 MHz)
 };
 
 __device__ __forceinline__ bool reached(uint32_t v, uint32_t target) {
@@ -98,35 +119,62 @@ __device__ __forceinline__ void raise_error(int* err, int code) {
                                        __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Workgroup-wide wait for *ctr >= target.  Must be called by every thread.
+// All of this wave's memory operations have completed.
+__device__ __forceinline__ void wave_drain() { __builtin_amdgcn_s_waitcnt(0); }
+
+// Workgroup-wide wait until the leaves of `ctr` sum to >= target.  Every
+// thread calls it.
 __device__ __forceinline__ void wg_wait(const SyncArgs& s, const uint32_t* ctr, uint32_t target,
                                         int stage) {
-  if (threadIdx.x == 0) {
-    uint32_t v = __hip_atomic_load(ctr, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-    if (!reached(v, target)) {
-      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-      for (;;) {
-        __builtin_amdgcn_s_sleep(1);
-        v = __hip_atomic_load(ctr, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-        if (reached(v, target)) break;
-        // another workgroup already timed out: stop waiting so the grid drains
-        if ((__hip_atomic_load(s.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & 0xFF) ==
-            kErrTimeout)
-          break;
-        if (__builtin_amdgcn_s_memrealtime() - t0 > s.watchdog) {
-          raise_error(s.err, kErrTimeout | (stage << 8));
-          break;
-        }
+  if (threadIdx.x < kWave) {
+    const int lane = threadIdx.x;
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    for (;;) {
+      uint32_t v = lane < kLeaves
+                       ? __hip_atomic_load(ctr + lane * kLeafStride, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT)
+                       : 0u;
+      v = wave_sum_u32(v);
+      if (reached(v, target)) break;
+      if ((__hip_atomic_load(s.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & 0xFF) ==
+          kErrTimeout)
+        break;  // another workgroup already timed out: let the grid drain
+      if (__builtin_amdgcn_s_memrealtime() - t0 > s.watchdog) {
+        if (lane == 0) raise_error(s.err, kErrTimeout | (stage << 8));
+        break;
       }
+      __builtin_amdgcn_s_sleep(1);
     }
   }
   __syncthreads();
 }
 
-// Workgroup-wide signal: every thread calls it after writing its outputs.
-__device__ __forceinline__ void wg_signal(uint32_t* ctr) {
+// Workgroup-wide signal after this workgroup's outputs are stored.
+__device__ __forceinline__ void wg_signal(uint32_t* ctr, int who) {
+  wave_drain();
   __syncthreads();
-  if (threadIdx.x == 0) __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0)
+    __hip_atomic_fetch_add(ctr + (who & (kLeaves - 1)) * kLeafStride, 1u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Last-arriver detection within one step: each of the n participants calls
+// it once (one thread, after its results are stored and drained).  Returns
+// true for exactly one caller, the last, and leaves the counter at zero for
+// the next step.  Two levels: leaf who % 16, then a root slot.
+__device__ __forceinline__ bool last_arriver(uint32_t* ctr, int who, int n) {
+  const int leaf = who & (kLeaves - 1);
+  const uint32_t per = (uint32_t)((n - leaf + kLeaves - 1) / kLeaves);
+  const int nleaf = n < kLeaves ? n : kLeaves;
+  uint32_t* lp = ctr + leaf * kLeafStride;
+  const uint32_t old = __hip_atomic_fetch_add(lp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (old + 1u != per) return false;
+  __hip_atomic_store(lp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  uint32_t* root = ctr + kLeaves * kLeafStride;
+  const uint32_t r = __hip_atomic_fetch_add(root, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (r + 1u != (uint32_t)nleaf) return false;
+  __hip_atomic_store(root, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return true;
 }
 
 }  // namespace ld

@@ -1,24 +1,23 @@
 // ld_gemv.hpp - weight-streaming GEMV engine for small batches (VALU path).
 //
-// Each wave owns NR weight rows at a time and streams them in blocks of UC
-// 512-element chunks: every lane issues one 16-byte non-temporal load per
-// (row, chunk), so a block keeps NR*UC KB in flight per wave.  The bf16
-// weights are widened in registers and multiplied with fp32 activations
-// (fp32 FMA); each lane's partial sums are reduced across the wave with
-// butterfly shuffles.  There is no cross-wave reduction: waves are
-// independent, which keeps the engine latency-tolerant and free of barriers.
-//
 // Decode at batch 1 is bound by streaming the weights from HBM (Hazy
-// Research, "Look Ma, No Bubbles!", introduction), so the engine's job is to
-// keep enough 16-byte loads in flight on every CU; arithmetic per weight byte
-// is B/2 FMAs.
+// Research, "Look Ma, No Bubbles!", introduction).  The engine keeps many
+// 16-byte non-temporal loads in flight on every CU:
+//  - each wave owns NR weight rows at a time (a task) and streams them in
+//    blocks of UC 512-element chunks, one 16-byte load per lane per (row,
+//    chunk); the first block of a stage is issued before the stage waits for
+//    its input (prefetch across the readiness wait);
+//  - the input vectors (fp32, RMSNorm gain applied) are staged once per stage
+//    into LDS with coherent loads, together with the sum of squares of the
+//    deferred RMSNorm; the FMA loop then reads them with ds_read_b128;
+//  - bf16 weights are widened in registers and multiplied in fp32; each
+//    lane's partial sums are reduced across the wave with shuffles, so waves
+//    never wait for each other inside a stage.
 #pragma once
 
 #include "ld_common.hpp"
 
 namespace ld {
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float dot8v(const u32x4& w, const float* x, float acc) {
   acc = fmaf(bf16lo(w.x), x[0], acc);
@@ -32,25 +31,19 @@ __device__ __forceinline__ float dot8v(const u32x4& w, const float* x, float acc
   return acc;
 }
 
-// Input-vector accessor: eight consecutive fp32 inputs of batch row b at
-// column k (k % 8 == 0).  Either an fp32 activation matrix or, for the first
-// layer, the widened bf16 embedding rows of the input tokens.  An optional
-// bf16 gain multiplies the inputs (RMSNorm gain; the 1/rms factor itself is
-// deferred to the epilogue).
-struct XIn {
-  const float* x;         // [B][ldx] fp32, or nullptr for embedding rows
+// Where a stage's input vectors come from: an fp32 activation matrix written
+// by another workgroup (read coherently), or, for the first layer, the bf16
+// embedding rows of the input tokens (read-only weights).
+struct XSrc {
+  const float* x;       // [B][ldx] fp32, or nullptr for embedding rows
   int ldx;
-  const uint16_t* emb;    // [V][ldx] bf16 when x == nullptr
-  const int* tokens;      // [B]
+  const uint16_t* emb;  // [V][ldx] bf16 when x == nullptr
+  const int* tokens;    // [B]
   int V;
-  const uint16_t* gain;   // [K] bf16 or nullptr
 
   __device__ __forceinline__ void raw8(int b, int k, float* o) const {
     if (x) {
-      const float4* p = reinterpret_cast<const float4*>(x + (int64_t)b * ldx + k);
-      const float4 a = p[0], c = p[1];
-      o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
-      o[4] = c.x; o[5] = c.y; o[6] = c.z; o[7] = c.w;
+      ld_coh8(x + (int64_t)b * ldx + k, o);
     } else {
       int t = tokens[b];
       t = ((unsigned)t < (unsigned)V) ? t : 0;
@@ -59,31 +52,65 @@ struct XIn {
       o[4] = bf16lo(w.z); o[5] = bf16hi(w.z); o[6] = bf16lo(w.w); o[7] = bf16hi(w.w);
     }
   }
-
-  __device__ __forceinline__ void load8(int b, int k, float* o) const {
-    raw8(b, k, o);
-    if (gain) {
-      const u32x4 g = *reinterpret_cast<const u32x4*>(gain + k);
-      o[0] *= bf16lo(g.x); o[1] *= bf16hi(g.x); o[2] *= bf16lo(g.y); o[3] *= bf16hi(g.y);
-      o[4] *= bf16lo(g.z); o[5] *= bf16hi(g.z); o[6] *= bf16lo(g.w); o[7] *= bf16hi(g.w);
-    }
-  }
 };
 
-// Deferred RMSNorm factors r_b = 1/sqrt(sum_k x_bk^2 / K + eps) for b < B,
-// computed by the whole workgroup into rs[0..B).  red: kWaves floats of LDS.
-__device__ __forceinline__ void norm_scales(const XIn& xin, int B, int K, float eps, float* rs,
-                                            float* red) {
-  for (int b = 0; b < B; ++b) {
-    float ss = 0.f;
-    for (int k = threadIdx.x * 8; k < K; k += kThreads * 8) {
-      float v[8];
-      xin.raw8(b, k, v);
+// Shared-memory scratch at the start of a workgroup's dynamic LDS.
+struct Scratch {
+  float red[kMaxWaves][8];
+  float rs[64];  // deferred-norm factors of the staged batch rows
+  float bestv[kMaxWaves][64];
+  int besti[kMaxWaves][64];
+  int flag[4];
+};
+constexpr int kScratchBytes = (int)((sizeof(Scratch) + 255) / 256 * 256);
+
+// Stage batch rows [b0, b0+nb) of the input into LDS: xs[b*K + k] =
+// x[b0+b][k] * gain[k] (gain may be null).  With `norm`, also
+// rs[b] = 1/sqrt(sum_k x^2 / K + eps) over the raw inputs.  nb <= NB.
+template <int NB>
+__device__ __forceinline__ void stage_x(const XSrc& src, int b0, int nb, int K,
+                                        const uint16_t* gain, bool norm, float eps, float* xs,
+                                        Scratch& sc) {
+  float ss[NB];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) ss = fmaf(v[i], v[i], ss);
+  for (int b = 0; b < NB; ++b) ss[b] = 0.f;
+  const int n8 = K >> 3;
+  for (int j = threadIdx.x; j < n8; j += blockDim.x) {
+    float g[8];
+    if (gain) {
+      const u32x4 gw = *reinterpret_cast<const u32x4*>(gain + j * 8);
+      g[0] = bf16lo(gw.x); g[1] = bf16hi(gw.x); g[2] = bf16lo(gw.y); g[3] = bf16hi(gw.y);
+      g[4] = bf16lo(gw.z); g[5] = bf16hi(gw.z); g[6] = bf16lo(gw.w); g[7] = bf16hi(gw.w);
     }
-    ss = block_sum(ss, red);
-    if (threadIdx.x == 0) rs[b] = 1.0f / sqrtf(ss / (float)K + eps);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      if (b < nb) {
+        float v[8];
+        src.raw8(b0 + b, j * 8, v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ss[b] = fmaf(v[i], v[i], ss[b]);
+        if (gain) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) v[i] *= g[i];
+        }
+        float4* d = reinterpret_cast<float4*>(xs + (int64_t)b * K + j * 8);
+        d[0] = make_float4(v[0], v[1], v[2], v[3]);
+        d[1] = make_float4(v[4], v[5], v[6], v[7]);
+      }
+    }
+  }
+  if (norm) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const float s = wave_sum(ss[b]);
+      if (lane_id() == 0) sc.red[wave_id()][b] = s;
+    }
+    __syncthreads();
+    if (threadIdx.x < nb) {
+      float s = 0.f;
+      for (int w = 0; w < nwaves(); ++w) s += sc.red[w][threadIdx.x];
+      sc.rs[threadIdx.x] = 1.0f / sqrtf(s / (float)K + eps);
+    }
   }
   __syncthreads();
 }
@@ -94,7 +121,7 @@ template <int NR, int UC>
 struct WBlock {
   u32x4 w[NR][UC];
 
-  // rows[r] points at row r of the task (nullptr = masked row).
+  // rows[r]: row r of the task (nullptr = masked row).
   __device__ __forceinline__ void load(const uint16_t* const (&rows)[NR], int K, int c0, int lane) {
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
@@ -109,9 +136,9 @@ struct WBlock {
     }
   }
 
-  // acc[r][b] += W[r, chunk] . x[b0 + b, chunk] for b < nb (nb <= NB).
+  // acc[r][b] += W[r, block] . xs[b, block] for b < nb, inputs in LDS [nb][K].
   template <int NB>
-  __device__ __forceinline__ void fma(const XIn& xin, int b0, int nb, int K, int c0, int lane,
+  __device__ __forceinline__ void fma(const float* xs, int nb, int K, int c0, int lane,
                                       float (&acc)[NR][NB]) const {
 #pragma unroll
     for (int u = 0; u < UC; ++u) {
@@ -120,8 +147,9 @@ struct WBlock {
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
           if (b < nb) {
-            float xv[8];
-            xin.load8(b0 + b, k, xv);
+            const float4* p = reinterpret_cast<const float4*>(xs + (int64_t)b * K + k);
+            const float4 a = p[0], c = p[1];
+            const float xv[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
 #pragma unroll
             for (int r = 0; r < NR; ++r) acc[r][b] = dot8v(w[r][u], xv, acc[r][b]);
           }
@@ -131,48 +159,66 @@ struct WBlock {
   }
 };
 
-// Drive one wave over its tasks.  A task is (batch tile bt, row tile t) with
-// task index = bt * ntile + t; RowFn(t, rows) fills the NR row pointers of
-// tile t; Epi(t, b0, nb, acc) consumes the wave-reduced sums (every lane
-// holds every sum).  `blk` may already hold block 0 of the first task
-// (prefetched before a readiness wait).
-template <int NR, int UC, int NB, class RowFn, class Epi>
-__device__ __forceinline__ void gemv_waves(const RowFn& rowfn, int ntile, int nbt, int K,
-                                           const XIn& xin, int B, Epi& epi, WBlock<NR, UC>& blk,
-                                           bool prefetched, int first, int stride, int lane) {
+// One GEMV stage for one workgroup: rows are split into tiles of NR rows
+// (RowFn(tile, rows) fills the row pointers), tiles are dealt to the waves of
+// the whole grid, the batch is processed in tiles of at most `bw` rows that
+// fit the LDS staging area.  Epi(tile, b0, nb, acc) consumes wave-reduced
+// sums (every lane holds every sum).  Wait(): the readiness wait, called once
+// after the first block has been issued.
+template <int NR, int UC, int NB, class RowFn, class WaitFn, class Epi>
+__device__ __forceinline__ void gemv_stage(const RowFn& rowfn, int ntile, int K, const XSrc& src,
+                                           const uint16_t* gain, bool norm, float eps, int B,
+                                           int bw, const WaitFn& wait, Epi& epi, int wg, int nwg,
+                                           char* smem) {
+  Scratch& sc = *reinterpret_cast<Scratch*>(smem);
+  float* xs = reinterpret_cast<float*>(smem + kScratchBytes);
+  const int lane = lane_id();
+  const int first = wg * nwaves() + wave_id(), stride = nwg * nwaves();
   const int nch = (K + kChunk - 1) / kChunk;
-  const int ntask = ntile * nbt;
+  const int nbt = (B + bw - 1) / bw;
   const uint16_t* rows[NR];
-  int t = first;
-  if (t < ntask) {
-    rowfn(t % ntile, rows);
-    if (!prefetched) blk.load(rows, K, 0, lane);
+  WBlock<NR, UC> blk;
+  bool have = false;  // blk holds block 0 of task `first`
+  if (first < ntile) {
+    rowfn(first, rows);
+    blk.load(rows, K, 0, lane);
+    have = true;
   }
-  for (; t < ntask; t += stride) {
-    const int tile = t % ntile, bt = t / ntile;
-    const int b0 = bt * NB, nb = min(NB, B - b0);
-    float acc[NR][NB];
+  wait();
+  for (int bt = 0; bt < nbt; ++bt) {
+    const int b0 = bt * bw, nb = min(bw, B - b0);
+    stage_x<NB>(src, b0, nb, K, gain, norm, eps, xs, sc);
+    for (int t = first; t < ntile; t += stride) {
+      if (!have) {
+        rowfn(t, rows);
+        blk.load(rows, K, 0, lane);
+      }
+      have = false;
+      float acc[NR][NB];
 #pragma unroll
-    for (int r = 0; r < NR; ++r)
+      for (int r = 0; r < NR; ++r)
 #pragma unroll
-      for (int b = 0; b < NB; ++b) acc[r][b] = 0.f;
-    for (int c0 = 0;;) {
-      blk.template fma<NB>(xin, b0, nb, K, c0, lane, acc);
-      c0 += UC;
-      if (c0 >= nch) break;
-      blk.load(rows, K, c0, lane);
+        for (int b = 0; b < NB; ++b) acc[r][b] = 0.f;
+      for (int c0 = 0;;) {
+        blk.template fma<NB>(xs, nb, K, c0, lane, acc);
+        c0 += UC;
+        if (c0 >= nch) break;
+        blk.load(rows, K, c0, lane);
+      }
+      // issue the next task's first block before reducing this one
+      const int tn = t + stride;
+      if (tn < ntile || (bt + 1 < nbt && first < ntile)) {
+        rowfn(tn < ntile ? tn : first, rows);
+        blk.load(rows, K, 0, lane);
+        have = true;
+      }
+#pragma unroll
+      for (int r = 0; r < NR; ++r)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) acc[r][b] = wave_sum(acc[r][b]);
+      epi(t, b0, nb, acc, sc);
     }
-    // start streaming the next task's first block before reducing this one
-    const int tn = t + stride;
-    if (tn < ntask) {
-      rowfn(tn % ntile, rows);
-      blk.load(rows, K, 0, lane);
-    }
-#pragma unroll
-    for (int r = 0; r < NR; ++r)
-#pragma unroll
-      for (int b = 0; b < NB; ++b) acc[r][b] = wave_sum(acc[r][b]);
-    epi(tile, b0, nb, acc);
+    if (bt + 1 < nbt) __syncthreads();  // every wave is done with xs before restaging
   }
 }
 

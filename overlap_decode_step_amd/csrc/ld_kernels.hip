@@ -8,61 +8,65 @@
 //      readiness counters (the single-kernel decode of Hazy Research, "Look
 //      Ma, No Bubbles! Designing a Low-Latency Megakernel for Llama-1B");
 //  k_gen_normal / k_fill16 / k_gen_kv : seeded synthetic inputs.
+// All decode kernels use dynamic LDS: a scratch area, then the staged input
+// vectors or the attention tiles.
 #include "ld_launch.h"
 #include "ld_stages.hpp"
 #include "../../synth/ld_synth.h"
 
 namespace ld {
 
+constexpr int kMaxThreads = kMaxWaves * kWave;
+
 template <int NB>
-__global__ __launch_bounds__(kThreads) void k_qkv(Params P, int l) {
-  __shared__ GemvSmem sm;
-  stage_qkv<NB>(P, l, blockIdx.x, gridDim.x, sm);
+__global__ __launch_bounds__(kMaxThreads) void k_qkv(Params P, int l) {
+  extern __shared__ __align__(16) char smem[];
+  stage_qkv<NB>(P, l, blockIdx.x, gridDim.x, smem);
 }
 
-__global__ __launch_bounds__(kThreads) void k_attn(Params P, int l) {
+__global__ __launch_bounds__(kMaxThreads) void k_attn(Params P, int l) {
   extern __shared__ __align__(16) char smem[];
   stage_attn(P, l, blockIdx.x, gridDim.x, smem);
 }
 
 template <int NB>
-__global__ __launch_bounds__(kThreads) void k_o(Params P, int l) {
-  __shared__ GemvSmem sm;
-  stage_o<NB>(P, l, blockIdx.x, gridDim.x, sm);
-}
-
-template <int NB>
-__global__ __launch_bounds__(kThreads) void k_gu(Params P, int l) {
-  __shared__ GemvSmem sm;
-  stage_gu<NB>(P, l, blockIdx.x, gridDim.x, sm);
-}
-
-template <int NB>
-__global__ __launch_bounds__(kThreads) void k_d(Params P, int l) {
-  __shared__ GemvSmem sm;
-  stage_d<NB>(P, l, blockIdx.x, gridDim.x, sm);
-}
-
-template <int NB>
-__global__ __launch_bounds__(kThreads) void k_lm(Params P, int l) {
-  __shared__ GemvSmem sm;
-  stage_lm<NB>(P, blockIdx.x, gridDim.x, sm);
-}
-
-template <int NB>
-__global__ __launch_bounds__(kThreads) void k_mega(Params P) {
+__global__ __launch_bounds__(kMaxThreads) void k_o(Params P, int l) {
   extern __shared__ __align__(16) char smem[];
-  GemvSmem& sm = *reinterpret_cast<GemvSmem*>(smem);
+  stage_o<NB>(P, l, blockIdx.x, gridDim.x, smem);
+}
+
+template <int NB>
+__global__ __launch_bounds__(kMaxThreads) void k_gu(Params P, int l) {
+  extern __shared__ __align__(16) char smem[];
+  stage_gu<NB>(P, l, blockIdx.x, gridDim.x, smem);
+}
+
+template <int NB>
+__global__ __launch_bounds__(kMaxThreads) void k_d(Params P, int l) {
+  extern __shared__ __align__(16) char smem[];
+  stage_d<NB>(P, l, blockIdx.x, gridDim.x, smem);
+}
+
+template <int NB>
+__global__ __launch_bounds__(kMaxThreads) void k_lm(Params P, int l) {
+  extern __shared__ __align__(16) char smem[];
+  stage_lm<NB>(P, blockIdx.x, gridDim.x, smem);
+}
+
+template <int NB>
+__global__ __launch_bounds__(kMaxThreads) void k_mega(Params P) {
+  extern __shared__ __align__(16) char smem[];
   const int wg = blockIdx.x, nwg = gridDim.x;
+#pragma clang loop unroll(disable)
   for (int l = 0; l < P.D.L; ++l) {
-    stage_qkv<NB>(P, l, wg, nwg, sm);
+    stage_qkv<NB>(P, l, wg, nwg, smem);
     stage_attn(P, l, wg, nwg, smem);
     __syncthreads();
-    stage_o<NB>(P, l, wg, nwg, sm);
-    stage_gu<NB>(P, l, wg, nwg, sm);
-    stage_d<NB>(P, l, wg, nwg, sm);
+    stage_o<NB>(P, l, wg, nwg, smem);
+    stage_gu<NB>(P, l, wg, nwg, smem);
+    stage_d<NB>(P, l, wg, nwg, smem);
   }
-  stage_lm<NB>(P, wg, nwg, sm);
+  stage_lm<NB>(P, wg, nwg, smem);
 }
 
 // ---------------------------------------------------------- generators
@@ -99,6 +103,7 @@ __global__ void k_gen_kv(uint16_t* kc, uint16_t* vc, const int* len, int n_kv, i
 template <int NB>
 static const void* stage_fn(int stage) {
   switch (stage) {
+    case 0: return reinterpret_cast<const void*>(&k_mega<NB>);
     case kSQkv: return reinterpret_cast<const void*>(&k_qkv<NB>);
     case kSAttn: return reinterpret_cast<const void*>(&k_attn);
     case kSO: return reinterpret_cast<const void*>(&k_o<NB>);
@@ -110,14 +115,6 @@ static const void* stage_fn(int stage) {
 }
 
 static const void* kernel_ptr(int stage, int nb) {
-  if (stage == 0) {
-    switch (nb) {
-      case 1: return reinterpret_cast<const void*>(&k_mega<1>);
-      case 2: return reinterpret_cast<const void*>(&k_mega<2>);
-      case 4: return reinterpret_cast<const void*>(&k_mega<4>);
-      default: return reinterpret_cast<const void*>(&k_mega<8>);
-    }
-  }
   switch (nb) {
     case 1: return stage_fn<1>(stage);
     case 2: return stage_fn<2>(stage);
@@ -128,26 +125,26 @@ static const void* kernel_ptr(int stage, int nb) {
 
 int nb_for_batch(int B) { return B <= 1 ? 1 : B <= 2 ? 2 : B <= 4 ? 4 : 8; }
 
-hipError_t launch_stage(int stage, const Params& P, int l, int grid, size_t smem,
+hipError_t launch_stage(int stage, const Params& P, int l, int grid, int threads, size_t smem,
                         hipStream_t s) {
   const void* fn = kernel_ptr(stage, nb_for_batch(P.S.B));
-  if (!fn) return hipErrorInvalidValue;
+  if (!fn || stage == 0) return hipErrorInvalidValue;
   Params p = P;
   void* args[] = {&p, &l};
-  return hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, smem, s);
+  return hipLaunchKernel(fn, dim3(grid), dim3(threads), args, smem, s);
 }
 
-hipError_t launch_mega(const Params& P, int grid, size_t smem, hipStream_t s) {
+hipError_t launch_mega(const Params& P, int grid, int threads, size_t smem, hipStream_t s) {
   const void* fn = kernel_ptr(0, nb_for_batch(P.S.B));
   Params p = P;
   void* args[] = {&p};
-  return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(kThreads), args, (unsigned)smem, s);
+  return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(threads), args, (unsigned)smem, s);
 }
 
-hipError_t occupancy(int stage, int nb, size_t smem, int* blocks_per_cu) {
+hipError_t occupancy(int stage, int nb, int threads, size_t smem, int* blocks_per_cu) {
   const void* fn = kernel_ptr(stage, nb);
   if (!fn) return hipErrorInvalidValue;
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, fn, kThreads, smem);
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, fn, threads, smem);
 }
 
 hipError_t set_max_dynamic_smem(int stage, int nb, size_t smem) {
@@ -156,7 +153,7 @@ hipError_t set_max_dynamic_smem(int stage, int nb, size_t smem) {
   return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
 }
 
-size_t gemv_smem_bytes() { return sizeof(GemvSmem); }
+size_t scratch_bytes() { return kScratchBytes; }
 
 size_t attn_smem(int group, int d, int T) { return attn_smem_bytes(group, d, T); }
 

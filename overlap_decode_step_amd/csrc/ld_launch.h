@@ -10,12 +10,12 @@ namespace ld {
 
 // stage: kSQkv..kSLm for the per-stage kernels, 0 for the persistent kernel.
 int nb_for_batch(int B);
-hipError_t launch_stage(int stage, const Params& P, int layer, int grid, size_t smem,
+hipError_t launch_stage(int stage, const Params& P, int layer, int grid, int threads, size_t smem,
                         hipStream_t s);
-hipError_t launch_mega(const Params& P, int grid, size_t smem, hipStream_t s);
-hipError_t occupancy(int stage, int nb, size_t smem, int* blocks_per_cu);
+hipError_t launch_mega(const Params& P, int grid, int threads, size_t smem, hipStream_t s);
+hipError_t occupancy(int stage, int nb, int threads, size_t smem, int* blocks_per_cu);
 hipError_t set_max_dynamic_smem(int stage, int nb, size_t smem);
-size_t gemv_smem_bytes();
+size_t scratch_bytes();
 size_t attn_smem(int group, int d, int T);
 
 hipError_t launch_gen_normal(uint16_t* dst, int64_t n, uint64_t key, uint64_t index0, float kappa,

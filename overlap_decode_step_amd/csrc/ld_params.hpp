@@ -6,9 +6,14 @@
 
 namespace ld {
 
-// Counter arena layout: per layer kCtrPerLayer slots, then the LM-head slot,
-// then the attention split counters [layer][seq][kv head].
-enum : int { kCQkv = 0, kCAttn = 1, kCO = 2, kCGu = 3, kCD = 4, kCtrPerLayer = 8 };
+// Stage-completion counters: per layer one counter per stage (each counter
+// is a set of leaves, see ld_common.hpp).
+enum : int { kCQkv = 0, kCAttn = 1, kCO = 2, kCGu = 3, kCD = 4, kStageCtrs = 5 };
+
+// One counter: kLeaves leaf words 128 bytes apart, plus a root slot.
+constexpr int kLeaves = 16;
+constexpr int kLeafStride = 32;  // uint32 slots between leaves (128 bytes)
+constexpr int kCtrWords = (kLeaves + 1) * kLeafStride;
 
 // Stage ids (watchdog error codes and schedule bookkeeping).
 enum : int { kSQkv = 1, kSAttn = 2, kSO = 3, kSGu = 4, kSD = 5, kSLm = 6 };
@@ -53,7 +58,9 @@ struct Work {
   float* lm_val;  // argmax partials [max_wg][maxB]
   int* lm_idx;
   const float* rope;  // [max_seq][d/2][2] (cos, sin)
-  uint32_t* ctr;
+  uint32_t* ctr;        // stage counters [L][kStageCtrs][counter words]
+  uint32_t* lm_ctr;     // LM-head last-arriver counter
+  uint32_t* split_ctr;  // attention last-arriver counters [L][maxB][nkv][16]
   int* err;
   uint64_t watchdog;
   int max_wg;
@@ -70,6 +77,7 @@ struct Step {
   // cumulative counter targets once this step's signals are in
   uint32_t t_qkv, t_attn, t_o, t_gu, t_d, t_lm;
   uint32_t inject;  // debug: added to one wait target to force a watchdog timeout
+  uint32_t x_cap;   // bytes of LDS for staged input vectors
 };
 
 struct Params {
