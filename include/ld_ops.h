@@ -61,6 +61,16 @@ ld_status ld_set_watchdog(ld_model* m, double seconds);
  * exits; ld_device_error() then reports LD_ETIMEOUT and resets the counters. */
 ld_status ld_debug_inject_stall(ld_model* m);
 
+/* Stage timeline (profiling).  When dev_buf is not NULL every decode kernel
+ * stores, for each workgroup w < 1024, the GPU's constant 100 MHz clock
+ * (s_memrealtime) at stage entry (ev 0), after the readiness wait (ev 1),
+ * after the compute (ev 2) and at stage exit (ev 3), as uint64 at
+ * dev_buf[((layer * 8 + stage) * 4 + ev) * 1024 + w]; stage ids 1..5 are
+ * QKV, attention, O, SwiGLU, Down and the LM head is stage 6 of layer
+ * n_layers.  NULL turns it off.  bytes >= ld_trace_bytes(cfg). */
+size_t ld_trace_bytes(const ld_config* cfg);
+ld_status ld_set_trace(ld_model* m, void* dev_buf, size_t bytes);
+
 /* Launch geometry: out[0] CUs, out[1] grid of the whole-kernel-wait kernels,
  * out[2] grid of the tile-flag kernels, out[3] persistent grid at batch 1,
  * out[4] attention split length, out[5] current mode.  n >= 6. */

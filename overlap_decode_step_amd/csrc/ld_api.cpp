@@ -88,8 +88,8 @@ static bool cfg_ok(const ld_config* c, std::string* why) {
     *why = "hidden, intermediate and n_q_heads*head_dim must be multiples of 8";
     return false;
   }
-  if (c->head_dim % 8 || c->head_dim > 256) {
-    *why = "head_dim must be a multiple of 8 and at most 256";
+  if (c->head_dim < 8 || c->head_dim > 256 || (c->head_dim & (c->head_dim - 1))) {
+    *why = "head_dim must be a power of two in [8, 256]";
     return false;
   }
   if (c->n_q_heads % c->n_kv_heads || c->n_q_heads / c->n_kv_heads > 8) {
@@ -156,13 +156,29 @@ struct KLayout {
   int split_len, max_splits, max_wg;
 };
 
-static int split_len_for(const ld_config* c) { return c->head_dim > 64 ? 32 : 64; }
+// LDS bytes available per CU.
+static const size_t kLdsPerCu = 160 * 1024;
+
+// Attention positions per work item: the largest multiple of 32 up to 512
+// (one position per thread of the 512-thread tile-flag workgroups) whose
+// tiles fit half a CU's LDS, so two tile-flag kernels still share a CU.
+static int split_len_for(const ld_config* c, int max_seq) {
+  const int group = c->n_q_heads / c->n_kv_heads;
+  const int tpp = (c->head_dim / 8 + 7) / 8;  // threads per position (64 channels each)
+  int T = 512 / tpp;
+  while (T > 32) {
+    const int ms = (max_seq + T - 1) / T;
+    if (scratch_bytes() + attn_smem(group, c->head_dim, T, ms, 1024) <= kLdsPerCu / 2) break;
+    T -= 32;
+  }
+  return T;
+}
 
 static KLayout klayout(const ld_config* c, int maxB, int max_seq) {
   KLayout K{};
   const size_t H = c->hidden, I = c->intermediate, d = c->head_dim;
   const size_t qd = (size_t)c->n_q_heads * d, kvd = (size_t)c->n_kv_heads * d;
-  K.split_len = split_len_for(c);
+  K.split_len = split_len_for(c, max_seq);
   K.max_splits = (max_seq + K.split_len - 1) / K.split_len;
   K.max_wg = 8192;
   size_t off = 0;
@@ -315,27 +331,27 @@ extern "C" ld_status ld_init_weights(ld_model** out, const ld_config* cfg, void*
   return LD_OK;
 }
 
-// LDS bytes available per CU, and the scratch area every decode kernel uses.
-static const size_t kLdsPerCu = 160 * 1024;
-
 static ld_status compute_grids(ld_model* m) {
   const Dims& D = m->D;
   const int maxnb = nb_for_batch(D.max_batch);
-  const size_t scratch = scratch_bytes();
-  const size_t attn = attn_smem(D.group, D.d, D.split_len);
+  const size_t scratch = scratch_bytes(), best = best_bytes();
   const size_t kmax = (size_t)std::max(std::max(D.H, D.I), D.qd) * 4;  // longest staged input row
   // whole-kernel wait and persistent modes: one 1024-thread workgroup per CU
   const uint32_t xcap_full = 128 * 1024;
   if (kmax > xcap_full) return fail(m, LD_EINVAL, "input rows longer than the LDS staging area");
   m->xcap_wait = m->xcap_mega = xcap_full;
-  m->smem_wait = m->smem_mega = scratch + std::max<size_t>(xcap_full, attn);
+  const size_t attn_full = attn_smem(D.group, D.d, D.split_len, D.max_splits, m->thr_mega);
+  m->smem_wait = m->smem_mega = scratch + std::max<size_t>(xcap_full + best, attn_full);
+  if (m->smem_mega > kLdsPerCu) return fail(m, LD_EINVAL, "stage tiles do not fit in LDS");
   // tile-flag mode: two consecutive stage kernels share each CU, so each
   // 512-thread workgroup gets at most half the LDS
   const size_t half = kLdsPerCu / 2;
-  m->xcap_flags = (uint32_t)(half - scratch);
-  m->smem_flags = scratch + std::max<size_t>(m->xcap_flags, attn);
-  m->flags_ok = (kmax <= m->xcap_flags) && (m->smem_flags <= half);
-  if (m->smem_mega > kLdsPerCu) return fail(m, LD_EINVAL, "attention tile does not fit in LDS");
+  m->xcap_flags = (uint32_t)(half - scratch - best);
+  const size_t attn_half = attn_smem(D.group, D.d, D.split_len, D.max_splits, m->thr_flags);
+  m->smem_flags = scratch + std::max<size_t>(m->xcap_flags + best, attn_half);
+  const int tpp = (D.d / 8 + 7) / 8;
+  m->flags_ok = (kmax <= m->xcap_flags) && (m->smem_flags <= half) &&
+                (D.split_len * tpp <= m->thr_flags);
   for (int nb = 1; nb <= maxnb; nb *= 2) {
     for (int st = 0; st <= kSLm; ++st) {
       const size_t sm = (st == 0) ? m->smem_mega : std::max(m->smem_wait, m->smem_flags);
@@ -799,6 +815,20 @@ extern "C" ld_status ld_debug_inject_stall(ld_model* m) {
   if (!m) return fail(nullptr, LD_EINVAL, "null model");
   m->inject_next = 1;  // next step's attention waits for one signal too many
   return LD_OK;
+}
+
+extern "C" ld_status ld_set_trace(ld_model* m, void* dev_buf, size_t bytes) {
+  if (!m) return fail(nullptr, LD_EINVAL, "null model");
+  if (!m->kv_ready) return fail(m, LD_ESTATE, "ld_alloc_kv first");
+  const size_t need = ld_trace_bytes(&m->cfg);
+  if (dev_buf && bytes < need) return fail(m, LD_ENOMEM, "trace buffer too small");
+  m->K.trace = static_cast<uint64_t*>(dev_buf);
+  return LD_OK;
+}
+
+extern "C" size_t ld_trace_bytes(const ld_config* cfg) {
+  if (!cfg) return 0;
+  return ((size_t)cfg->n_layers + 1) * 8 * 4 * 1024 * sizeof(uint64_t);
 }
 
 extern "C" ld_status ld_launch_info(const ld_model* m, int32_t* out, int32_t n) {

@@ -35,23 +35,51 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
 }
 
 // ------------------------------------------------------------ reductions
+//
+// Wave-wide reductions with DPP lane moves (VALU, a few cycles each) instead
+// of LDS permutes: pairs and quads inside each 4-lane group, rotations inside
+// each 16-lane row, then row broadcasts 15 -> next row and 31 -> upper half;
+// lane 63 ends with the total, which is read back as a uniform value.
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_f(float old, float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(x), CTRL,
+                                                    ROW_MASK, 0xF, false));
+}
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t old, uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)x, CTRL, ROW_MASK, 0xF, false);
+}
 
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
-  return v;
+  v += dpp_f<0xB1, 0xF>(0.f, v);   // quad_perm [1,0,3,2]
+  v += dpp_f<0x4E, 0xF>(0.f, v);   // quad_perm [2,3,0,1]
+  v += dpp_f<0x124, 0xF>(0.f, v);  // row_ror:4
+  v += dpp_f<0x128, 0xF>(0.f, v);  // row_ror:8
+  v += dpp_f<0x142, 0xA>(0.f, v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_f<0x143, 0xC>(0.f, v);  // row_bcast:31 into rows 2 and 3
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
-  return v;
+  const float lo = -INFINITY;
+  v = fmaxf(v, dpp_f<0xB1, 0xF>(lo, v));
+  v = fmaxf(v, dpp_f<0x4E, 0xF>(lo, v));
+  v = fmaxf(v, dpp_f<0x124, 0xF>(lo, v));
+  v = fmaxf(v, dpp_f<0x128, 0xF>(lo, v));
+  v = fmaxf(v, dpp_f<0x142, 0xA>(lo, v));
+  v = fmaxf(v, dpp_f<0x143, 0xC>(lo, v));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
-  return v;
+  v += dpp_u<0xB1, 0xF>(0u, v);
+  v += dpp_u<0x4E, 0xF>(0u, v);
+  v += dpp_u<0x124, 0xF>(0u, v);
+  v += dpp_u<0x128, 0xF>(0u, v);
+  v += dpp_u<0x142, 0xA>(0u, v);
+  v += dpp_u<0x143, 0xC>(0u, v);
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
 // ------------------------------------------- coherent (agent-scope) access

@@ -57,12 +57,24 @@ struct XSrc {
 // Shared-memory scratch at the start of a workgroup's dynamic LDS.
 struct Scratch {
   float red[kMaxWaves][8];
-  float rs[64];  // deferred-norm factors of the staged batch rows
-  float bestv[kMaxWaves][64];
-  int besti[kMaxWaves][64];
+  float rs[64];   // deferred-norm factors of the staged batch rows
+  int pos[64];    // positions of the step (valid once pos_ok is set)
+  int pos_ok;
   int flag[4];
 };
+
+// Every decode kernel starts with this (the scratch area persists across
+// the stages of the persistent kernel).
+__device__ __forceinline__ void scratch_init(char* smem) {
+  if (threadIdx.x == 0) reinterpret_cast<Scratch*>(smem)->pos_ok = 0;
+  __syncthreads();
+}
 constexpr int kScratchBytes = (int)((sizeof(Scratch) + 255) / 256 * 256);
+
+// Reductions across a workgroup use a fixed partition of kRedThreads
+// threads, so every execution mode (1024- or 512-thread workgroups) adds the
+// same numbers in the same order and produces bitwise-equal results.
+constexpr int kRedThreads = 512;
 
 // Stage batch rows [b0, b0+nb) of the input into LDS: xs[b*K + k] =
 // x[b0+b][k] * gain[k] (gain may be null).  With `norm`, also
@@ -75,40 +87,44 @@ __device__ __forceinline__ void stage_x(const XSrc& src, int b0, int nb, int K,
 #pragma unroll
   for (int b = 0; b < NB; ++b) ss[b] = 0.f;
   const int n8 = K >> 3;
-  for (int j = threadIdx.x; j < n8; j += blockDim.x) {
-    float g[8];
-    if (gain) {
-      const u32x4 gw = *reinterpret_cast<const u32x4*>(gain + j * 8);
-      g[0] = bf16lo(gw.x); g[1] = bf16hi(gw.x); g[2] = bf16lo(gw.y); g[3] = bf16hi(gw.y);
-      g[4] = bf16lo(gw.z); g[5] = bf16hi(gw.z); g[6] = bf16lo(gw.w); g[7] = bf16hi(gw.w);
-    }
+  if (threadIdx.x < kRedThreads) {
+    for (int j = threadIdx.x; j < n8; j += kRedThreads) {
+      float g[8];
+      if (gain) {
+        const u32x4 gw = *reinterpret_cast<const u32x4*>(gain + j * 8);
+        g[0] = bf16lo(gw.x); g[1] = bf16hi(gw.x); g[2] = bf16lo(gw.y); g[3] = bf16hi(gw.y);
+        g[4] = bf16lo(gw.z); g[5] = bf16hi(gw.z); g[6] = bf16lo(gw.w); g[7] = bf16hi(gw.w);
+      }
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      if (b < nb) {
-        float v[8];
-        src.raw8(b0 + b, j * 8, v);
+      for (int b = 0; b < NB; ++b) {
+        if (b < nb) {
+          float v[8];
+          src.raw8(b0 + b, j * 8, v);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) ss[b] = fmaf(v[i], v[i], ss[b]);
-        if (gain) {
+          for (int i = 0; i < 8; ++i) ss[b] = fmaf(v[i], v[i], ss[b]);
+          if (gain) {
 #pragma unroll
-          for (int i = 0; i < 8; ++i) v[i] *= g[i];
+            for (int i = 0; i < 8; ++i) v[i] *= g[i];
+          }
+          float4* d = reinterpret_cast<float4*>(xs + (int64_t)b * K + j * 8);
+          d[0] = make_float4(v[0], v[1], v[2], v[3]);
+          d[1] = make_float4(v[4], v[5], v[6], v[7]);
         }
-        float4* d = reinterpret_cast<float4*>(xs + (int64_t)b * K + j * 8);
-        d[0] = make_float4(v[0], v[1], v[2], v[3]);
-        d[1] = make_float4(v[4], v[5], v[6], v[7]);
       }
     }
   }
   if (norm) {
+    if (threadIdx.x < kRedThreads) {
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const float s = wave_sum(ss[b]);
-      if (lane_id() == 0) sc.red[wave_id()][b] = s;
+      for (int b = 0; b < NB; ++b) {
+        const float s = wave_sum(ss[b]);
+        if (lane_id() == 0) sc.red[wave_id()][b] = s;
+      }
     }
     __syncthreads();
     if (threadIdx.x < nb) {
       float s = 0.f;
-      for (int w = 0; w < nwaves(); ++w) s += sc.red[w][threadIdx.x];
+      for (int w = 0; w < kRedThreads / kWave; ++w) s += sc.red[w][threadIdx.x];
       sc.rs[threadIdx.x] = 1.0f / sqrtf(s / (float)K + eps);
     }
   }
@@ -121,14 +137,15 @@ template <int NR, int UC>
 struct WBlock {
   u32x4 w[NR][UC];
 
-  // rows[r]: row r of the task (nullptr = masked row).
-  __device__ __forceinline__ void load(const uint16_t* const (&rows)[NR], int K, int c0, int lane) {
+  // rows[r]: row r of the task (nullptr = masked row); columns >= kend masked.
+  __device__ __forceinline__ void load(const uint16_t* const (&rows)[NR], int kend, int c0,
+                                       int lane) {
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
 #pragma unroll
       for (int u = 0; u < UC; ++u) {
         const int k = (c0 + u) * kChunk + lane * 8;
-        if (rows[r] != nullptr && k < K)
+        if (rows[r] != nullptr && k < kend)
           w[r][u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rows[r] + k));
         else
           w[r][u] = u32x4{0u, 0u, 0u, 0u};
@@ -136,18 +153,19 @@ struct WBlock {
     }
   }
 
-  // acc[r][b] += W[r, block] . xs[b, block] for b < nb, inputs in LDS [nb][K].
+  // acc[r][b] += W[r, block] . xs[b, block] for b < nb; inputs in LDS with
+  // row stride ldx; columns >= kend skipped.
   template <int NB>
-  __device__ __forceinline__ void fma(const float* xs, int nb, int K, int c0, int lane,
+  __device__ __forceinline__ void fma(const float* xs, int ldx, int nb, int kend, int c0, int lane,
                                       float (&acc)[NR][NB]) const {
 #pragma unroll
     for (int u = 0; u < UC; ++u) {
       const int k = (c0 + u) * kChunk + lane * 8;
-      if (k < K) {
+      if (k < kend) {
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
           if (b < nb) {
-            const float4* p = reinterpret_cast<const float4*>(xs + (int64_t)b * K + k);
+            const float4* p = reinterpret_cast<const float4*>(xs + (int64_t)b * ldx + k);
             const float4 a = p[0], c = p[1];
             const float xv[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
 #pragma unroll
@@ -159,64 +177,113 @@ struct WBlock {
   }
 };
 
-// One GEMV stage for one workgroup: rows are split into tiles of NR rows
-// (RowFn(tile, rows) fills the row pointers), tiles are dealt to the waves of
-// the whole grid, the batch is processed in tiles of at most `bw` rows that
-// fit the LDS staging area.  Epi(tile, b0, nb, acc) consumes wave-reduced
-// sums (every lane holds every sum).  Wait(): the readiness wait, called once
+// One GEMV stage for one workgroup.  Rows are split into tiles of NR rows
+// (RowFn(tile, rows) fills the row pointers) and the K dimension into KS
+// slices; a task is (tile, slice) and tasks are dealt to the waves of the
+// whole grid in rounds.  The KS slices of a tile land on KS neighbouring
+// waves of one workgroup and are added through LDS in fixed order.  The batch
+// is processed in tiles of at most `bw` rows that fit the LDS staging area.
+// Epi(tile, b0, nb, acc, scratch) consumes the reduced sums (every lane of the
+// calling wave holds every sum).  Wait(): the readiness wait, called once
 // after the first block has been issued.
-template <int NR, int UC, int NB, class RowFn, class WaitFn, class Epi>
+template <int NR, int UC, int NB, int KS, class RowFn, class WaitFn, class Epi>
 __device__ __forceinline__ void gemv_stage(const RowFn& rowfn, int ntile, int K, const XSrc& src,
                                            const uint16_t* gain, bool norm, float eps, int B,
                                            int bw, const WaitFn& wait, Epi& epi, int wg, int nwg,
                                            char* smem) {
+  static_assert(NR * NB <= 8 || KS == 1, "K-split partials must fit the scratch row");
   Scratch& sc = *reinterpret_cast<Scratch*>(smem);
   float* xs = reinterpret_cast<float*>(smem + kScratchBytes);
-  const int lane = lane_id();
-  const int first = wg * nwaves() + wave_id(), stride = nwg * nwaves();
+  const int lane = lane_id(), wave = wave_id();
+  const int first = wg * nwaves() + wave, stride = nwg * nwaves();
   const int nch = (K + kChunk - 1) / kChunk;
+  const int nchp = (nch + KS - 1) / KS;  // chunks per K slice
+  const int ntask = ntile * KS;
+  const int rounds = (ntask + stride - 1) / stride;
   const int nbt = (B + bw - 1) / bw;
+  auto slice = [&](int t, int& c0, int& kend) {
+    const int kp = t % KS;
+    c0 = kp * nchp;
+    kend = min(K, (kp + 1) * nchp * kChunk);
+  };
   const uint16_t* rows[NR];
   WBlock<NR, UC> blk;
   bool have = false;  // blk holds block 0 of task `first`
-  if (first < ntile) {
-    rowfn(first, rows);
-    blk.load(rows, K, 0, lane);
+  // Prefetch across the wait, except in wave 0: it polls the readiness
+  // counter, and loads return in order, so weight loads in flight would delay
+  // every poll it makes.
+  if (first < ntask && wave != 0) {
+    int c0, kend;
+    slice(first, c0, kend);
+    rowfn(first / KS, rows);
+    blk.load(rows, kend, c0, lane);
     have = true;
   }
   wait();
   for (int bt = 0; bt < nbt; ++bt) {
     const int b0 = bt * bw, nb = min(bw, B - b0);
     stage_x<NB>(src, b0, nb, K, gain, norm, eps, xs, sc);
-    for (int t = first; t < ntile; t += stride) {
-      if (!have) {
-        rowfn(t, rows);
-        blk.load(rows, K, 0, lane);
-      }
-      have = false;
+    for (int r = 0; r < rounds; ++r) {
+      const int t = first + r * stride;
       float acc[NR][NB];
 #pragma unroll
-      for (int r = 0; r < NR; ++r)
+      for (int i = 0; i < NR; ++i)
 #pragma unroll
-        for (int b = 0; b < NB; ++b) acc[r][b] = 0.f;
-      for (int c0 = 0;;) {
-        blk.template fma<NB>(xs, nb, K, c0, lane, acc);
-        c0 += UC;
-        if (c0 >= nch) break;
-        blk.load(rows, K, c0, lane);
+        for (int b = 0; b < NB; ++b) acc[i][b] = 0.f;
+      if (t < ntask) {
+        int c0, kend;
+        slice(t, c0, kend);
+        if (!have) {
+          rowfn(t / KS, rows);
+          blk.load(rows, kend, c0, lane);
+        }
+        have = false;
+        const int cend = min(nch, c0 + nchp);
+        for (int c = c0;;) {
+          blk.template fma<NB>(xs, K, nb, kend, c, lane, acc);
+          c += UC;
+          if (c >= cend) break;
+          blk.load(rows, kend, c, lane);
+        }
+        // issue the next task's first block before reducing this one
+        const int tn = t + stride;
+        const int tnext = tn < ntask ? tn : ((bt + 1 < nbt) ? first : -1);
+        if (tnext >= 0) {
+          int c1, k1;
+          slice(tnext, c1, k1);
+          rowfn(tnext / KS, rows);
+          blk.load(rows, k1, c1, lane);
+          have = true;
+        }
+#pragma unroll
+        for (int i = 0; i < NR; ++i)
+#pragma unroll
+          for (int b = 0; b < NB; ++b) acc[i][b] = wave_sum(acc[i][b]);
       }
-      // issue the next task's first block before reducing this one
-      const int tn = t + stride;
-      if (tn < ntile || (bt + 1 < nbt && first < ntile)) {
-        rowfn(tn < ntile ? tn : first, rows);
-        blk.load(rows, K, 0, lane);
-        have = true;
+      if constexpr (KS == 1) {
+        if (t < ntask) epi(t, b0, nb, acc, sc);
+      } else {
+        // slices of one tile sit on waves wave - wave % KS .. + KS - 1
+        if (lane == 0) {
+#pragma unroll
+          for (int i = 0; i < NR; ++i)
+#pragma unroll
+            for (int b = 0; b < NB; ++b) sc.red[wave][i * NB + b] = acc[i][b];
+        }
+        __syncthreads();
+        if (t < ntask && wave % KS == 0) {
+#pragma unroll
+          for (int i = 0; i < NR; ++i)
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+              float v = 0.f;
+              for (int q = 0; q < KS; ++q) v += sc.red[wave + q][i * NB + b];
+              acc[i][b] = v;
+            }
+          epi(t / KS, b0, nb, acc, sc);
+        }
+        __syncthreads();
       }
-#pragma unroll
-      for (int r = 0; r < NR; ++r)
-#pragma unroll
-        for (int b = 0; b < NB; ++b) acc[r][b] = wave_sum(acc[r][b]);
-      epi(t, b0, nb, acc, sc);
     }
     if (bt + 1 < nbt) __syncthreads();  // every wave is done with xs before restaging
   }

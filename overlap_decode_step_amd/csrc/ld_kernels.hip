@@ -26,6 +26,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_qkv(Params P, int l) {
 
 __global__ __launch_bounds__(kMaxThreads) void k_attn(Params P, int l) {
   extern __shared__ __align__(16) char smem[];
+  scratch_init(smem);
   stage_attn(P, l, blockIdx.x, gridDim.x, smem);
 }
 
@@ -56,6 +57,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_lm(Params P, int l) {
 template <int NB>
 __global__ __launch_bounds__(kMaxThreads) void k_mega(Params P) {
   extern __shared__ __align__(16) char smem[];
+  scratch_init(smem);
   const int wg = blockIdx.x, nwg = gridDim.x;
 #pragma clang loop unroll(disable)
   for (int l = 0; l < P.D.L; ++l) {
@@ -155,7 +157,11 @@ hipError_t set_max_dynamic_smem(int stage, int nb, size_t smem) {
 
 size_t scratch_bytes() { return kScratchBytes; }
 
-size_t attn_smem(int group, int d, int T) { return attn_smem_bytes(group, d, T); }
+size_t attn_smem(int group, int d, int T, int max_splits, int threads) {
+  return attn_smem_bytes(group, d, T, max_splits, threads);
+}
+
+size_t best_bytes() { return kBestBytes; }
 
 hipError_t launch_gen_normal(uint16_t* dst, int64_t n, uint64_t key, uint64_t index0, float kappa,
                              hipStream_t s) {

@@ -62,6 +62,7 @@ struct Work {
   uint32_t* lm_ctr;     // LM-head last-arriver counter
   uint32_t* split_ctr;  // attention last-arriver counters [L][maxB][nkv][16]
   int* err;
+  uint64_t* trace;  // optional stage timestamps (see trace_ev), nullptr = off
   uint64_t watchdog;
   int max_wg;
 };

@@ -29,14 +29,20 @@ namespace ld {
 constexpr int kNrQkv = 1, kUcQkv = 4;
 constexpr int kNrO = 1, kUcO = 4;
 constexpr int kPairsGu = 1, kUcGu = 4;  // one (gate, up) row pair per task
-constexpr int kNrD = 1, kUcD = 8;
+constexpr int kNrD = 1, kUcD = 8, kKsD = 2;  // Down: K split over two waves
 constexpr int kNrLm = 2, kUcLm = 4;
 
-__host__ __device__ constexpr size_t attn_smem_bytes(int group, int d, int T) {
-  return (size_t)group * d * 4             /* rotated q */
-         + 2 * (size_t)T * (d / 2 + 1) * 4 /* K, V tiles, rows padded by one dword */
-         + (size_t)group * T * 4           /* scores */
-         + (size_t)group * 2 * 4;          /* (max, sum) per head */
+// Attention LDS: rotated q [group][d], then a tile region holding the K and
+// V tiles (rows padded by one dword against bank conflicts) or, in the
+// combining workgroup, the split statistics, then scores [group][T] and the
+// split-local (max, sum) per head.
+__host__ __device__ constexpr int attn_tile_words(int group, int d, int T, int max_splits) {
+  return 2 * T * (d / 2 + 1) > 2 * group * max_splits + group ? 2 * T * (d / 2 + 1)
+                                                              : 2 * group * max_splits + group;
+}
+__host__ __device__ constexpr size_t attn_smem_bytes(int group, int d, int T, int max_splits) {
+  return (size_t)group * d * 4 + (size_t)attn_tile_words(group, d, T, max_splits) * 4 +
+         (size_t)group * T * 4 + (size_t)group * 2 * 4;
 }
 
 __device__ __forceinline__ const uint16_t* layer_w(const Params& P, int l, int64_t off) {
@@ -70,6 +76,16 @@ __device__ __forceinline__ void signal_if(const Params& P, uint32_t* ctr, int wh
   if (!P.S.wait) wg_signal(ctr, who);
 }
 
+// Optional timeline: thread 0 of each workgroup stores the constant-rate
+// clock (s_memrealtime) at stage entry (ev 0), after the readiness wait
+// (ev 1), after the compute (ev 2) and at stage exit (ev 3), at
+// trace[((layer * 8 + stage) * 4 + ev) * kTraceWgs + wg].
+constexpr int kTraceWgs = 1024;
+__device__ __forceinline__ void trace_ev(const Params& P, int l, int stage, int ev, int wg) {
+  if (P.K.trace != nullptr && threadIdx.x == 0 && wg < kTraceWgs)
+    P.K.trace[(((int64_t)l * 8 + stage) * 4 + ev) * kTraceWgs + wg] = __builtin_amdgcn_s_memrealtime();
+}
+
 // ----------------------------------------------------------------- QKV
 
 template <int NB>
@@ -91,8 +107,10 @@ __device__ void stage_qkv(const Params& P, int l, int wg, int nwg, char* smem) {
     if ((unsigned)t >= (unsigned)D.V) raise_error(P.K.err, kErrToken);
     if ((unsigned)p >= (unsigned)D.max_seq) raise_error(P.K.err, kErrPos);
   }
+  trace_ev(P, l, kSQkv, 0, wg);
   auto wait = [&]() {
     if (!P.S.wait && l > 0) wg_wait(sync_of(P), stage_ctr(P, l - 1, kCD), P.S.t_d, kSQkv);
+    trace_ev(P, l, kSQkv, 1, wg);
   };
   const XSrc src{l == 0 ? nullptr : P.K.xa, K, P.W.embed, P.S.tokens, D.V};
   float* out = P.K.qkv;
@@ -106,29 +124,77 @@ __device__ void stage_qkv(const Params& P, int l, int wg, int nwg, char* smem) {
           st_coh(out + (int64_t)(b0 + b) * rows_total + row, acc[r][b] * sc.rs[b]);
       }
   };
-  gemv_stage<NR, UC, NB>(rowfn, (rows_total + NR - 1) / NR, K, src,
+  gemv_stage<NR, UC, NB, 1>(rowfn, (rows_total + NR - 1) / NR, K, src,
                          layer_w(P, l, P.W.o_attn_norm), true, D.eps, B, batch_tile(P, K, NB),
                          wait, epi, wg, nwg, smem);
+  trace_ev(P, l, kSQkv, 2, wg);
   signal_if(P, stage_ctr(P, l, kCQkv), wg);
+  trace_ev(P, l, kSQkv, 3, wg);
 }
 
 // ------------------------------------------------------------ attention
+//
+// Split-KV grouped-query decode attention.  A work item is (sequence b, kv
+// head, split s): positions [n0, n1) of 0..p, the splits of a sequence
+// balanced to at most T positions each.  One workgroup per item:
+//  - one round of loads: the group's q heads (rotated to p into LDS), each
+//    thread's K row into registers (one position per thread), each V row
+//    into LDS; the split holding p also rotates the new key, rounds k and v
+//    to bf16 and appends them to the cache;
+//  - scores (q . K_t) / sqrt(d) per position, the split's softmax statistics
+//    per head, and the unnormalised output sum_t e_t V_t;
+//  - a single split writes o / l directly; otherwise each split stores
+//    (m, l, o) and the last-arriving split combines all splits in fixed order.
 
-// One (sequence b, kv head, split s) item: positions [s*T, min(s*T+T, p+1)).
+__host__ __device__ constexpr size_t attn_tile_bytes(int group, int d, int T, int max_splits) {
+  // V tile [T][d] bf16, or the combining workgroup's split statistics
+  return (size_t)T * d * 2 > (size_t)(2 * group * max_splits + group) * 4
+             ? (size_t)T * d * 2
+             : (size_t)(2 * group * max_splits + group) * 4;
+}
+__host__ __device__ constexpr size_t attn_smem_bytes(int group, int d, int T, int max_splits,
+                                                     int threads) {
+  return (size_t)group * d * 4                           /* rotated q */
+         + (attn_tile_bytes(group, d, T, max_splits) + 15) / 16 * 16
+         + (size_t)group * T * 4                         /* scores / weights */
+         + (size_t)8 * group * d * 4                     /* output partials per position slice */
+         + (size_t)group * 2 * 4                         /* (max, sum) per head */
+         + (size_t)d * 2 + 16;                           /* new key row */
+}
+
+// Each thread holds up to 64 channels of one K row (kKw 16-byte words);
+// wider heads use tpp = ceil(d / 64) neighbouring threads per position.
+constexpr int kKw = 8;
+constexpr int kAttnParts = 8;  // position slices of the output sum (fixed: mode independent)
+constexpr int kMaxGroup = 8;   // query heads per kv head at most
+
 __device__ void attn_item(const Params& P, int l, int b, int kvh, int s, int nsplit, int p,
                           char* smem) {
+  // head_dim is a power of two (checked on the host): index math uses shifts,
+  // which keeps this once-per-item code small
   const Dims& D = P.D;
-  const int T = D.split_len, d = D.d, half = d / 2, group = D.group, rowd = half + 1;
+  const int d = D.d, half = d / 2, group = D.group, w8 = d / 8;
+  const int ld = 31 - __builtin_clz(d);
+  const int tpp = (w8 + kKw - 1) / kKw;  // threads per position (1, 2 or 4)
+  const int ltpp = 31 - __builtin_clz(tpp);
   const int tid = threadIdx.x, nth = blockDim.x, lane = lane_id(), wave = wave_id();
   Scratch& sc = *reinterpret_cast<Scratch*>(smem);
-  float* qs = reinterpret_cast<float*>(smem + kScratchBytes);  // [group][d]
-  uint32_t* Ks = reinterpret_cast<uint32_t*>(qs + group * d);  // [T][rowd]
-  uint32_t* Vs = Ks + T * rowd;                                // [T][rowd]
-  float* Sc = reinterpret_cast<float*>(Vs + T * rowd);         // [group][T]
-  float* ml = Sc + group * T;                                  // [group][2]
+  char* base = smem + kScratchBytes;
+  float* qs = reinterpret_cast<float*>(base);                                   // [group][d]
+  uint16_t* Vs = reinterpret_cast<uint16_t*>(base + (size_t)group * d * 4);    // [T][d]
+  char* after_tile = reinterpret_cast<char*>(Vs) +
+                     (attn_tile_bytes(group, d, D.split_len, D.max_splits) + 15) / 16 * 16;
+  float* Sc = reinterpret_cast<float*>(after_tile);                             // [group][T]
+  float* op = Sc + group * D.split_len;                  // [kAttnParts][group][d]
+  float* ml = op + kAttnParts * group * d;                                      // [group][2]
+  uint16_t* Knew = reinterpret_cast<uint16_t*>(ml + group * 2);                 // [d]
+  const int T = D.split_len;
 
-  const int n0 = s * T, n1 = min(n0 + T, p + 1), n = n1 - n0;
-  const bool has_new = (n1 == p + 1);
+  const int len = p + 1;
+  const int n0 = (s * len) / nsplit, n1 = ((s + 1) * len) / nsplit;
+  const int n = n1 - n0;
+  const bool has_new = (n1 == len);
+  const int ncached = has_new ? n - 1 : n;  // rows read from the cache
   const float* qkv = P.K.qkv + (int64_t)b * D.qkv_rows;
   const float* rope = P.K.rope + (int64_t)p * half * 2;
   const int64_t cache_off =
@@ -136,73 +202,122 @@ __device__ void attn_item(const Params& P, int l, int b, int kvh, int s, int nsp
   uint16_t* kc = P.K.kc + cache_off;
   uint16_t* vc = P.K.vc + cache_off;
 
-  // q heads of this group, rotated to position p (rotate-half pairs)
-  for (int idx = tid; idx < group * half; idx += nth) {
-    const int g = idx / half, i = idx - g * half;
-    const float* qh = qkv + (int64_t)(kvh * group + g) * d;
-    const float q0 = ld_coh(qh + i), q1 = ld_coh(qh + i + half);
-    const float c = rope[2 * i], sn = rope[2 * i + 1];
-    qs[g * d + i] = q0 * c - q1 * sn;
-    qs[g * d + i + half] = q0 * sn + q1 * c;
+  // ---- one round of loads, all issued before any is consumed
+  trace_ev(P, l, 6, 0, blockIdx.x);
+  // cached V rows [n0, n0 + ncached) are contiguous: copy them into LDS with
+  // direct-to-LDS loads, 1 KB per wave instruction
+  {
+    const int bytes = ncached * d * 2;
+    const char* src = reinterpret_cast<const char*>(vc + (int64_t)n0 * d);
+    char* dst = reinterpret_cast<char*>(Vs);
+    for (int c = wave * 1024; c < bytes; c += nwaves() * 1024) {
+      const int off = c + lane * 16;
+      if (off < bytes)
+        __builtin_amdgcn_global_load_lds(src + off,
+                                         (__attribute__((address_space(3))) void*)(dst + c), 16, 0,
+                                         0);
+    }
   }
-  // cached K/V rows of this split (the new row, if any, is filled below)
-  const int ncached = has_new ? n - 1 : n;
-  const int w8 = d / 8;  // 16-byte words per row
-  for (int idx = tid; idx < ncached * w8; idx += nth) {
-    const int t = idx / w8, j = idx - t * w8;
-    const u32x4 kk = *reinterpret_cast<const u32x4*>(kc + (int64_t)(n0 + t) * d + j * 8);
-    const u32x4 vv = *reinterpret_cast<const u32x4*>(vc + (int64_t)(n0 + t) * d + j * 8);
-    uint32_t* kd = Ks + t * rowd + j * 4;
-    uint32_t* vd = Vs + t * rowd + j * 4;
-    kd[0] = kk.x; kd[1] = kk.y; kd[2] = kk.z; kd[3] = kk.w;
-    vd[0] = vv.x; vd[1] = vv.y; vd[2] = vv.z; vd[3] = vv.w;
+  // this thread's slice of one position's K row into registers
+  const int t = tid >> ltpp, part = tid & (tpp - 1), j0 = part * kKw;
+  const bool mine = t < ncached;
+  u32x4 kr[kKw];
+  if (mine) {
+    const uint16_t* krow = kc + (int64_t)(n0 + t) * d + j0 * 8;
+#pragma unroll
+    for (int j = 0; j < kKw; ++j)
+      if (j0 + j < w8) kr[j] = *reinterpret_cast<const u32x4*>(krow + j * 8);
   }
-  if (has_new) {
-    // rotate the new key, round k and v to bf16, append them to the cache at p
+  // q heads of this group (one (head, pair) per thread: group * half <= nth)
+  // and, in the split holding p, the new k and v
+  const bool qthread = tid < group * half;
+  const int qg = tid >> (ld - 1), qi = tid & (half - 1);
+  float q0 = 0.f, q1 = 0.f, cq = 0.f, sq = 0.f;
+  if (qthread) {
+    const float* qh = qkv + (int64_t)(kvh * group + qg) * d;
+    q0 = ld_coh(qh + qi);
+    q1 = ld_coh(qh + qi + half);
+    cq = rope[2 * qi];
+    sq = rope[2 * qi + 1];
+  }
+  float k0 = 0.f, k1 = 0.f, v0 = 0.f, v1 = 0.f;
+  const bool newrow = has_new && tid < half;
+  if (newrow) {
     const float* kh = qkv + D.qd + (int64_t)kvh * d;
-    const float* vh = qkv + D.qd + D.kvd + (int64_t)kvh * d;
-    uint16_t* kl = reinterpret_cast<uint16_t*>(Ks + (n - 1) * rowd);
-    uint16_t* vl = reinterpret_cast<uint16_t*>(Vs + (n - 1) * rowd);
-    for (int i = tid; i < half; i += nth) {
-      const float k0 = ld_coh(kh + i), k1 = ld_coh(kh + i + half);
-      const float c = rope[2 * i], sn = rope[2 * i + 1];
-      const uint16_t a = f2bf(k0 * c - k1 * sn), bb = f2bf(k0 * sn + k1 * c);
-      const uint16_t v0 = f2bf(ld_coh(vh + i)), v1 = f2bf(ld_coh(vh + i + half));
-      kc[(int64_t)p * d + i] = a;
-      kc[(int64_t)p * d + i + half] = bb;
-      vc[(int64_t)p * d + i] = v0;
-      vc[(int64_t)p * d + i + half] = v1;
-      kl[i] = a;
-      kl[i + half] = bb;
-      vl[i] = v0;
-      vl[i + half] = v1;
-    }
+    const float* vh = kh + D.kvd;
+    k0 = ld_coh(kh + tid);
+    k1 = ld_coh(kh + tid + half);
+    v0 = ld_coh(vh + tid);
+    v1 = ld_coh(vh + tid + half);
   }
+  if (qthread) {  // rotate q (rotate-half pairs) into LDS
+    qs[qg * d + qi] = q0 * cq - q1 * sq;
+    qs[qg * d + qi + half] = q0 * sq + q1 * cq;
+  }
+  if (newrow) {
+    // rotate the new key, round k and v to bf16, append them to the cache at p
+    // (thread tid < half holds pair tid, whose cos/sin it loaded as a q thread)
+    const uint16_t a = f2bf(k0 * cq - k1 * sq), bb = f2bf(k0 * sq + k1 * cq);
+    const uint16_t e0 = f2bf(v0), e1 = f2bf(v1);
+    kc[(int64_t)p * d + tid] = a;
+    kc[(int64_t)p * d + tid + half] = bb;
+    vc[(int64_t)p * d + tid] = e0;
+    vc[(int64_t)p * d + tid + half] = e1;
+    Knew[tid] = a;
+    Knew[tid + half] = bb;
+    Vs[(int64_t)(n - 1) * d + tid] = e0;
+    Vs[(int64_t)(n - 1) * d + tid + half] = e1;
+  }
+  wave_drain();  // direct-to-LDS copies have landed
   __syncthreads();
+  trace_ev(P, l, 7, 0, blockIdx.x);
 
-  // scores s_t = (q . K_t) * scale, channels summed in ascending order
-  for (int idx = tid; idx < group * n; idx += nth) {
-    const int g = idx / n, t = idx - g * n;
-    const float* q = qs + g * d;
-    const uint32_t* kr = Ks + t * rowd;
+  // ---- scores s_t = (q . K_t) * scale; a position's channel slices are
+  // added in ascending order across its tpp neighbouring lanes
+  if (t < n && !mine) {
+#pragma unroll
+    for (int j = 0; j < kKw; ++j)
+      if (j0 + j < w8) kr[j] = *reinterpret_cast<const u32x4*>(Knew + (j0 + j) * 8);
+  }
+  // one head at a time (a runtime loop keeps this code small: it runs once
+  // per item, so its instruction fetches are not amortised)
+#pragma clang loop unroll(disable)
+  for (int g = 0; g < group; ++g) {
     float acc = 0.f;
-    for (int j = 0; j < half; ++j) {
-      const uint32_t w = kr[j];
-      acc = fmaf(q[2 * j], bf16lo(w), acc);
-      acc = fmaf(q[2 * j + 1], bf16hi(w), acc);
+    if (t < n) {
+      const float* qgp = qs + g * d + j0 * 8;
+#pragma unroll
+      for (int j = 0; j < kKw; ++j) {
+        if (j0 + j < w8) {
+          const float4 qa = *reinterpret_cast<const float4*>(qgp + j * 8);
+          const float4 qb = *reinterpret_cast<const float4*>(qgp + j * 8 + 4);
+          acc = fmaf(qa.x, bf16lo(kr[j].x), acc);
+          acc = fmaf(qa.y, bf16hi(kr[j].x), acc);
+          acc = fmaf(qa.z, bf16lo(kr[j].y), acc);
+          acc = fmaf(qa.w, bf16hi(kr[j].y), acc);
+          acc = fmaf(qb.x, bf16lo(kr[j].z), acc);
+          acc = fmaf(qb.y, bf16hi(kr[j].z), acc);
+          acc = fmaf(qb.z, bf16lo(kr[j].w), acc);
+          acc = fmaf(qb.w, bf16hi(kr[j].w), acc);
+        }
+      }
     }
-    Sc[g * T + t] = acc * D.attn_scale;
+    for (int q2 = 1; q2 < tpp; ++q2) {
+      const float o = __shfl(acc, (lane & ~(tpp - 1)) + q2, kWave);
+      if (part == 0) acc += o;
+    }
+    if (t < n && part == 0) Sc[g * T + t] = acc * D.attn_scale;
   }
   __syncthreads();
-  // split-local softmax statistics
+  // ---- split-local softmax statistics per head
   for (int g = wave; g < group; g += nwaves()) {
     float m = -INFINITY;
-    for (int t = lane; t < n; t += kWave) m = fmaxf(m, Sc[g * T + t]);
+    for (int u = lane; u < n; u += kWave) m = fmaxf(m, Sc[g * T + u]);
     m = wave_max(m);
     float sum = 0.f;
-    for (int t = lane; t < n; t += kWave) {
-      const float e = expf(Sc[g * T + t] - m);
-      Sc[g * T + t] = e;
+    for (int u = lane; u < n; u += kWave) {
+      const float e = expf(Sc[g * T + u] - m);
+      Sc[g * T + u] = e;
       sum += e;
     }
     sum = wave_sum(sum);
@@ -212,30 +327,67 @@ __device__ void attn_item(const Params& P, int l, int b, int kvh, int s, int nsp
     }
   }
   __syncthreads();
-  // unnormalised output of this split
-  float* out = P.K.ao + (int64_t)b * D.qd;
-  for (int idx = tid; idx < group * d; idx += nth) {
-    const int g = idx / d, i = idx - g * d;
+  trace_ev(P, l, 7, 1, blockIdx.x);
+  // ---- unnormalised output sum_t e_t V_t: each item is (position slice,
+  // head, 8 channels); per position one 16-byte V read and one broadcast
+  // weight, two independent accumulator sets; the kAttnParts slices are then
+  // added in fixed order
+  const int gd = group * d;
+  for (int it = tid; it < kAttnParts * group * w8; it += nth) {
+    const int c8 = it & (w8 - 1);
+    const int slg = it >> (ld - 3);  // slice * group + head
+    const int sl = slg / group, g = slg - sl * group;
+    const int u0 = (sl * n) / kAttnParts, u1 = ((sl + 1) * n) / kAttnParts;
     const float* e = Sc + g * T;
-    const int hi = i & 1;
-    const uint32_t* vcol = Vs + (i >> 1);
-    float acc = 0.f;
-    for (int t = 0; t < n; ++t) {
-      const uint32_t w = vcol[t * rowd];
-      acc = fmaf(e[t], hi ? bf16hi(w) : bf16lo(w), acc);
+    const uint16_t* vcol = Vs + c8 * 8;
+    float a[8], c[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) a[k] = c[k] = 0.f;
+    int u = u0;
+    for (; u + 2 <= u1; u += 2) {
+      const u32x4 va = *reinterpret_cast<const u32x4*>(vcol + u * d);
+      const u32x4 vb = *reinterpret_cast<const u32x4*>(vcol + (u + 1) * d);
+      const float ea = e[u], eb = e[u + 1];
+      a[0] = fmaf(ea, bf16lo(va.x), a[0]); a[1] = fmaf(ea, bf16hi(va.x), a[1]);
+      a[2] = fmaf(ea, bf16lo(va.y), a[2]); a[3] = fmaf(ea, bf16hi(va.y), a[3]);
+      a[4] = fmaf(ea, bf16lo(va.z), a[4]); a[5] = fmaf(ea, bf16hi(va.z), a[5]);
+      a[6] = fmaf(ea, bf16lo(va.w), a[6]); a[7] = fmaf(ea, bf16hi(va.w), a[7]);
+      c[0] = fmaf(eb, bf16lo(vb.x), c[0]); c[1] = fmaf(eb, bf16hi(vb.x), c[1]);
+      c[2] = fmaf(eb, bf16lo(vb.y), c[2]); c[3] = fmaf(eb, bf16hi(vb.y), c[3]);
+      c[4] = fmaf(eb, bf16lo(vb.z), c[4]); c[5] = fmaf(eb, bf16hi(vb.z), c[5]);
+      c[6] = fmaf(eb, bf16lo(vb.w), c[6]); c[7] = fmaf(eb, bf16hi(vb.w), c[7]);
     }
-    const int hq = kvh * group + g;
+    if (u < u1) {
+      const u32x4 va = *reinterpret_cast<const u32x4*>(vcol + u * d);
+      const float ea = e[u];
+      a[0] = fmaf(ea, bf16lo(va.x), a[0]); a[1] = fmaf(ea, bf16hi(va.x), a[1]);
+      a[2] = fmaf(ea, bf16lo(va.y), a[2]); a[3] = fmaf(ea, bf16hi(va.y), a[3]);
+      a[4] = fmaf(ea, bf16lo(va.z), a[4]); a[5] = fmaf(ea, bf16hi(va.z), a[5]);
+      a[6] = fmaf(ea, bf16lo(va.w), a[6]); a[7] = fmaf(ea, bf16hi(va.w), a[7]);
+    }
+    float4* o4 = reinterpret_cast<float4*>(op + sl * gd + g * d + c8 * 8);
+    o4[0] = make_float4(a[0] + c[0], a[1] + c[1], a[2] + c[2], a[3] + c[3]);
+    o4[1] = make_float4(a[4] + c[4], a[5] + c[5], a[6] + c[6], a[7] + c[7]);
+  }
+  __syncthreads();
+  float* out = P.K.ao + (int64_t)b * D.qd + kvh * gd;
+  for (int r = tid; r < gd; r += nth) {
+    const int g = r >> ld, i = r & (d - 1);
+    float o = 0.f;
+#pragma clang loop unroll(disable)
+    for (int sl = 0; sl < kAttnParts; ++sl) o += op[sl * gd + r];
     if (nsplit == 1) {
-      st_coh(out + hq * d + i, acc / ml[2 * g + 1]);
+      st_coh(out + r, o / ml[2 * g + 1]);
     } else {
-      float* pp = P.K.part + (((int64_t)b * D.nq + hq) * D.max_splits + s) * (d + 2);
-      st_coh(pp + 2 + i, acc);
+      float* pp = P.K.part + (((int64_t)b * D.nq + kvh * group + g) * D.max_splits + s) * (d + 2);
+      st_coh(pp + 2 + i, o);
       if (i == 0) {
         st_coh(pp, ml[2 * g]);
         st_coh(pp + 1, ml[2 * g + 1]);
       }
     }
   }
+  trace_ev(P, l, 7, 2, blockIdx.x);
   if (nsplit > 1) {
     // last-arriving split combines all splits in fixed order
     wave_drain();
@@ -248,37 +400,71 @@ __device__ void attn_item(const Params& P, int l, int b, int kvh, int s, int nsp
       sc.flag[0] = last;
     }
     __syncthreads();
+    trace_ev(P, l, 7, 3, blockIdx.x);
     if (!sc.flag[0]) return;
-    for (int idx = tid; idx < group * d; idx += nth) {
-      const int g = idx / d, i = idx - g * d;
-      const int hq = kvh * group + g;
-      const float* pp = P.K.part + ((int64_t)b * D.nq + hq) * D.max_splits * (d + 2);
-      float M = -INFINITY;
-      for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, ld_coh(pp + sp * (d + 2)));
-      float Ls = 0.f, O = 0.f;
-      for (int sp = 0; sp < nsplit; ++sp) {
-        const float* q = pp + sp * (d + 2);
-        const float f = expf(ld_coh(q) - M);
-        Ls = fmaf(ld_coh(q + 1), f, Ls);
-        O = fmaf(ld_coh(q + 2 + i), f, O);
+    // split statistics of the group's heads -> LDS (over the V tile); then per
+    // head M = max m_s, f_s = e^(m_s - M), L = sum l_s f_s
+    float* ms = reinterpret_cast<float*>(Vs);  // [group][nsplit] max, then weight f_s
+    float* ls = ms + group * nsplit;           // [group][nsplit] sums
+    float* Lg = ls + group * nsplit;           // [group] combined sums
+    const float* pbase = P.K.part + ((int64_t)b * D.nq + kvh * group) * D.max_splits * (d + 2);
+    for (int g = 0; g < group; ++g)
+      for (int sp = tid; sp < nsplit; sp += nth) {
+        const float* q = pbase + ((int64_t)g * D.max_splits + sp) * (d + 2);
+        ms[g * nsplit + sp] = ld_coh(q);
+        ls[g * nsplit + sp] = ld_coh(q + 1);
       }
-      st_coh(out + hq * d + i, O / Ls);
+    __syncthreads();
+    for (int g = wave; g < group; g += nwaves()) {
+      float M = -INFINITY;
+      for (int sp = lane; sp < nsplit; sp += kWave) M = fmaxf(M, ms[g * nsplit + sp]);
+      M = wave_max(M);
+      float L = 0.f;
+      for (int sp = lane; sp < nsplit; sp += kWave) {
+        const float f = expf(ms[g * nsplit + sp] - M);
+        ms[g * nsplit + sp] = f;
+        L = fmaf(ls[g * nsplit + sp], f, L);
+      }
+      L = wave_sum(L);
+      if (lane == 0) Lg[g] = L;
+    }
+    __syncthreads();
+    // weighted sum of the split outputs, four coherent loads in flight per thread
+    for (int r = tid; r < gd; r += nth) {
+      const int g = r >> ld, i = r & (d - 1);
+      const float* q = pbase + (int64_t)g * D.max_splits * (d + 2) + 2 + i;
+      const float* f = ms + g * nsplit;
+      float O = 0.f;
+      for (int s0 = 0; s0 < nsplit; s0 += 4) {
+        float v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = (s0 + u < nsplit) ? ld_coh(q + (s0 + u) * (d + 2)) : 0.f;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (s0 + u < nsplit) O = fmaf(v[u], f[s0 + u], O);
+      }
+      st_coh(out + r, O / Lg[g]);
     }
   }
   signal_if(P, stage_ctr(P, l, kCAttn), b * D.nkv + kvh);
 }
 
-__device__ void stage_attn(const Params& P, int l, int wg, int nwg, char* smem) {
+__device__ void attn_items(const Params& P, int l, int wg, int nwg, char* smem) {
   const Dims& D = P.D;
-  if (!P.S.wait) wg_wait(sync_of(P), stage_ctr(P, l, kCQkv), P.S.t_qkv + P.S.inject, kSAttn);
   const int T = D.split_len, B = P.S.B;
+  Scratch& sc = *reinterpret_cast<Scratch*>(smem);
+  if (!sc.pos_ok) {  // positions of the step, read once per kernel
+    if (threadIdx.x < B) sc.pos[threadIdx.x] = clamp_pos(P, threadIdx.x);
+    __syncthreads();
+    if (threadIdx.x == 0) sc.pos_ok = 1;
+  }
   int total = 0;
-  for (int b = 0; b < B; ++b) total += D.nkv * ((clamp_pos(P, b) + T) / T);
+  for (int b = 0; b < B; ++b) total += D.nkv * ((sc.pos[b] + T) / T);
   for (int it = wg; it < total; it += nwg) {
     int b = 0, base = 0, ns = 0, p = 0;
     for (;; ++b) {
-      p = clamp_pos(P, b);
-      ns = (p + T) / T;
+      p = sc.pos[b];
+      ns = (p + T) / T;  // splits of at most T positions over 0..p
       if (it < base + D.nkv * ns) break;
       base += D.nkv * ns;
     }
@@ -286,6 +472,14 @@ __device__ void stage_attn(const Params& P, int l, int wg, int nwg, char* smem) 
     attn_item(P, l, b, kvh, s, ns, p, smem);
     __syncthreads();  // shared memory is reused by the next item
   }
+}
+
+__device__ void stage_attn(const Params& P, int l, int wg, int nwg, char* smem) {
+  trace_ev(P, l, kSAttn, 0, wg);
+  if (!P.S.wait) wg_wait(sync_of(P), stage_ctr(P, l, kCQkv), P.S.t_qkv + P.S.inject, kSAttn);
+  trace_ev(P, l, kSAttn, 1, wg);
+  attn_items(P, l, wg, nwg, smem);
+  trace_ev(P, l, kSAttn, 3, wg);
 }
 
 // ----------------------------------------------------------- O-proj
@@ -304,8 +498,10 @@ __device__ void stage_o(const Params& P, int l, int wg, int nwg, char* smem) {
       rows[r] = row < rows_total ? Wm + (int64_t)row * K : nullptr;
     }
   };
+  trace_ev(P, l, kSO, 0, wg);
   auto wait = [&]() {
     if (!P.S.wait) wg_wait(sync_of(P), stage_ctr(P, l, kCAttn), P.S.t_attn, kSO);
+    trace_ev(P, l, kSO, 1, wg);
   };
   const XSrc src{P.K.ao, K, nullptr, nullptr, 0};
   // residual input: the layer input (the embedding row for layer 0)
@@ -333,9 +529,11 @@ __device__ void stage_o(const Params& P, int l, int wg, int nwg, char* smem) {
         }
       }
   };
-  gemv_stage<NR, UC, NB>(rowfn, (rows_total + NR - 1) / NR, K, src, nullptr, false, D.eps, B,
+  gemv_stage<NR, UC, NB, 1>(rowfn, (rows_total + NR - 1) / NR, K, src, nullptr, false, D.eps, B,
                          batch_tile(P, K, NB), wait, epi, wg, nwg, smem);
+  trace_ev(P, l, kSO, 2, wg);
   signal_if(P, stage_ctr(P, l, kCO), wg);
+  trace_ev(P, l, kSO, 3, wg);
 }
 
 // -------------------------------------------------------- fused SwiGLU
@@ -362,8 +560,10 @@ __device__ void stage_gu(const Params& P, int l, int wg, int nwg, char* smem) {
       rows[NP + r] = row < I ? Wu + (int64_t)row * K : nullptr;
     }
   };
+  trace_ev(P, l, kSGu, 0, wg);
   auto wait = [&]() {
     if (!P.S.wait) wg_wait(sync_of(P), stage_ctr(P, l, kCO), P.S.t_o, kSGu);
+    trace_ev(P, l, kSGu, 1, wg);
   };
   const XSrc src{P.K.xb, K, nullptr, nullptr, 0};
   float* h = P.K.hbuf;
@@ -380,9 +580,11 @@ __device__ void stage_gu(const Params& P, int l, int wg, int nwg, char* smem) {
       }
   };
   const int bw = (P.S.gu_variant == kGuRow) ? min(2, batch_tile(P, K, NB)) : batch_tile(P, K, NB);
-  gemv_stage<NR, UC, NB>(rowfn, (I + NP - 1) / NP, K, src, layer_w(P, l, P.W.o_mlp_norm), true,
+  gemv_stage<NR, UC, NB, 1>(rowfn, (I + NP - 1) / NP, K, src, layer_w(P, l, P.W.o_mlp_norm), true,
                          D.eps, B, bw, wait, epi, wg, nwg, smem);
+  trace_ev(P, l, kSGu, 2, wg);
   signal_if(P, stage_ctr(P, l, kCGu), wg);
+  trace_ev(P, l, kSGu, 3, wg);
 }
 
 // ---------------------------------------------------------- Down-proj
@@ -401,8 +603,10 @@ __device__ void stage_d(const Params& P, int l, int wg, int nwg, char* smem) {
       rows[r] = row < rows_total ? Wm + (int64_t)row * K : nullptr;
     }
   };
+  trace_ev(P, l, kSD, 0, wg);
   auto wait = [&]() {
     if (!P.S.wait) wg_wait(sync_of(P), stage_ctr(P, l, kCGu), P.S.t_gu, kSD);
+    trace_ev(P, l, kSD, 1, wg);
   };
   const XSrc src{P.K.hbuf, K, nullptr, nullptr, 0};
   const float* xb = P.K.xb;
@@ -419,9 +623,11 @@ __device__ void stage_d(const Params& P, int l, int wg, int nwg, char* smem) {
         }
       }
   };
-  gemv_stage<NR, UC, NB>(rowfn, (rows_total + NR - 1) / NR, K, src, nullptr, false, D.eps, B,
+  gemv_stage<NR, UC, NB, kKsD>(rowfn, (rows_total + NR - 1) / NR, K, src, nullptr, false, D.eps, B,
                          batch_tile(P, K, NB), wait, epi, wg, nwg, smem);
+  trace_ev(P, l, kSD, 2, wg);
   signal_if(P, stage_ctr(P, l, kCD), wg);
+  trace_ev(P, l, kSD, 3, wg);
 }
 
 // ------------------------------------------------- LM head + argmax
@@ -430,11 +636,19 @@ __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
   return v > bv || (v == bv && i < bi);
 }
 
+// Per-wave running argmax of the LM head, placed after the staged inputs.
+struct Best {
+  float v[kMaxWaves][64];
+  int i[kMaxWaves][64];
+};
+constexpr int kBestBytes = (int)sizeof(Best);
+
 template <int NB>
 __device__ void stage_lm(const Params& P, int wg, int nwg, char* smem) {
   constexpr int NR = kNrLm, UC = kUcLm;
   const Dims& D = P.D;
   Scratch& sc = *reinterpret_cast<Scratch*>(smem);
+  Best& bs = *reinterpret_cast<Best*>(smem + kScratchBytes + P.S.x_cap);
   const int lane = lane_id(), wave = wave_id();
   const int rows_total = D.V, K = D.H, B = P.S.B;
   const uint16_t* Wm = P.W.lm;
@@ -445,12 +659,14 @@ __device__ void stage_lm(const Params& P, int wg, int nwg, char* smem) {
       rows[r] = row < rows_total ? Wm + (int64_t)row * K : nullptr;
     }
   };
+  trace_ev(P, D.L, kSLm, 0, wg);
   auto wait = [&]() {
     if (!P.S.wait) wg_wait(sync_of(P), stage_ctr(P, D.L - 1, kCD), P.S.t_d, kSLm);
+    trace_ev(P, D.L, kSLm, 1, wg);
   };
   for (int b = lane; b < 64; b += kWave) {
-    sc.bestv[wave][b] = -INFINITY;
-    sc.besti[wave][b] = 0x7FFFFFFF;
+    bs.v[wave][b] = -INFINITY;
+    bs.i[wave][b] = 0x7FFFFFFF;
   }
   const XSrc src{P.K.xa, K, nullptr, nullptr, 0};
   float* logits = P.S.logits;
@@ -458,8 +674,8 @@ __device__ void stage_lm(const Params& P, int wg, int nwg, char* smem) {
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       if (b < nb) {
-        float bv = s.bestv[wave][b0 + b];
-        int bi = s.besti[wave][b0 + b];
+        float bv = bs.v[wave][b0 + b];
+        int bi = bs.i[wave][b0 + b];
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
           const int row = t * NR + r;
@@ -473,23 +689,24 @@ __device__ void stage_lm(const Params& P, int wg, int nwg, char* smem) {
           }
         }
         if (lane == 0) {
-          s.bestv[wave][b0 + b] = bv;
-          s.besti[wave][b0 + b] = bi;
+          bs.v[wave][b0 + b] = bv;
+          bs.i[wave][b0 + b] = bi;
         }
       }
     }
   };
-  gemv_stage<NR, UC, NB>(rowfn, (rows_total + NR - 1) / NR, K, src, P.W.final_norm, true, D.eps,
+  gemv_stage<NR, UC, NB, 1>(rowfn, (rows_total + NR - 1) / NR, K, src, P.W.final_norm, true, D.eps,
                          B, batch_tile(P, K, NB), wait, epi, wg, nwg, smem);
+  trace_ev(P, D.L, kSLm, 2, wg);
   __syncthreads();
   // this workgroup's best per sequence -> partials
   for (int b = threadIdx.x; b < B; b += blockDim.x) {
-    float bv = sc.bestv[0][b];
-    int bi = sc.besti[0][b];
+    float bv = bs.v[0][b];
+    int bi = bs.i[0][b];
     for (int w = 1; w < nwaves(); ++w)
-      if (better(sc.bestv[w][b], sc.besti[w][b], bv, bi)) {
-        bv = sc.bestv[w][b];
-        bi = sc.besti[w][b];
+      if (better(bs.v[w][b], bs.i[w][b], bv, bi)) {
+        bv = bs.v[w][b];
+        bi = bs.i[w][b];
       }
     st_coh(P.K.lm_val + (int64_t)wg * D.max_batch + b, bv);
     st_coh_i(P.K.lm_idx + (int64_t)wg * D.max_batch + b, bi);
@@ -498,6 +715,7 @@ __device__ void stage_lm(const Params& P, int wg, int nwg, char* smem) {
   __syncthreads();
   if (threadIdx.x == 0) sc.flag[1] = last_arriver(P.K.lm_ctr, wg, nwg);
   __syncthreads();
+  trace_ev(P, D.L, kSLm, 3, wg);
   if (!sc.flag[1] || P.S.next == nullptr) return;
   // last arriver: reduce the partials of every workgroup, per sequence
   for (int b = 0; b < B; ++b) {
@@ -521,15 +739,15 @@ __device__ void stage_lm(const Params& P, int wg, int nwg, char* smem) {
       }
     }
     if (lane == 0) {
-      sc.bestv[wave][0] = bv;
-      sc.besti[wave][0] = bi;
+      bs.v[wave][0] = bv;
+      bs.i[wave][0] = bi;
     }
     __syncthreads();
     if (threadIdx.x == 0) {
       for (int w = 1; w < nwaves(); ++w)
-        if (better(sc.bestv[w][0], sc.besti[w][0], bv, bi)) {
-          bv = sc.bestv[w][0];
-          bi = sc.besti[w][0];
+        if (better(bs.v[w][0], bs.i[w][0], bv, bi)) {
+          bv = bs.v[w][0];
+          bi = bs.i[w][0];
         }
       P.S.next[b] = (bi == 0x7FFFFFFF) ? 0 : bi;
     }

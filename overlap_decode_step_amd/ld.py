@@ -62,6 +62,8 @@ def _load():
         "ld_set_watchdog": (S, [P, D]),
         "ld_debug_inject_stall": (S, [P]),
         "ld_launch_info": (S, [P, P, I32]),
+        "ld_trace_bytes": (ctypes.c_size_t, [CP]),
+        "ld_set_trace": (S, [P, P, ctypes.c_size_t]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -172,6 +174,14 @@ def ld_set_watchdog(m, seconds):
 
 def ld_debug_inject_stall(m):
     return _check(LIB.ld_debug_inject_stall(m), m)
+
+
+def ld_trace_bytes(shape):
+    return int(LIB.ld_trace_bytes(ctypes.byref(_cfg(shape))))
+
+
+def ld_set_trace(m, dev_buf, nbytes):
+    return _check(LIB.ld_set_trace(m, dev_buf, nbytes), m)
 
 
 def ld_launch_info(m):

@@ -152,15 +152,16 @@ RAGGED = W.shape(3, 136, 6, 2, 8, 200, 1000, 0, 1e-5, 10000.0)
 @pytest.mark.parametrize("mode", MODES)
 def test_ragged_shape_multi_split(ld, orc, mode):
     # hidden 136 and intermediate 200 leave ragged 512-element chunks, 1000
-    # vocab rows leave a ragged row tile, and positions 150..152 span three
-    # 64-position attention splits with a ragged last split.
+    # vocab rows leave a ragged row tile, and contexts of 1101..1103, 513..515
+    # and 2..4 positions need three, two and one attention splits.
     shape = RAGGED
-    B, prefill = 3, [150, 64, 1]
+    B, prefill = 3, [1100, 512, 1]
     om = orc.model(shape, seed=W.SEED_WEIGHTS, w_std=0.05)
-    m = gpu_model(ld, shape, B, 200, prefill, w_std=0.05)
+    m = gpu_model(ld, shape, B, 1200, prefill, w_std=0.05)
     m.set_mode(mode)
+    assert ld.ld_launch_info(m.h)["split_len"] <= 512
     run = GpuRunner(m, shape["vocab"], B)
-    okvs = [orc.kv(shape, 1, 200, seed=W.SEED_KV, kv_std=1.0, prefill=[prefill[b]], seq0=b)
+    okvs = [orc.kv(shape, 1, 1200, seed=W.SEED_KV, kv_std=1.0, prefill=[prefill[b]], seq0=b)
             for b in range(B)]
     toks = W.first_tokens(B, shape["vocab"])
     for s in range(3):
