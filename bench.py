@@ -7,10 +7,16 @@ random weights (synthetic data).  A step is one full decode step: every
 layer and the LM head with greedy argmax, inputs resident in HBM.
 
 Prints one JSON line: decode tokens/s (value), the roofline of the dominant
-kernel (HBM bytes the step must move / its measured duration, against
-8 TB/s), and the CPU oracle's rate on a bounded sample.
+kernel (algorithmic HBM bytes per launch / its measured duration, against
+8 TB/s), the HBM traffic the hardware counters saw for that kernel (from the
+committed counter summary, when it was taken on the current kernel sources)
+and the CPU oracle's rate on a bounded sample.
+
+--copy-calibration instead copies a 1 GiB device buffer three times: the
+plain copy whose FETCH_SIZE / WRITE_SIZE counters scale the kernel's.
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -20,6 +26,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+CSRC = os.path.join(ROOT, "overlap_decode_step_amd", "csrc")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "k_mega_llama1b_b1_hbm_traffic.md")
 
 
 def algorithmic_bytes(shape, batch, positions):
@@ -35,6 +43,68 @@ def algorithmic_bytes(shape, batch, positions):
     return weights + sum(per_seq)
 
 
+def kernel_source_digest():
+    """Digest of the HIP/C++ sources the decode kernels are built from."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".hpp", ".h", ".cpp")):
+            h.update(name.encode())
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(mode, batch):
+    """HBM bytes per launch of the persistent kernel from the committed counter
+    summary, or None when there is none for this launch or the kernel sources
+    have changed since the counters were taken."""
+    if mode != "mega" or batch != 1 or not os.path.exists(TRAFFIC_SUMMARY):
+        return None
+    kv = {}
+    with open(TRAFFIC_SUMMARY) as f:
+        for line in f:
+            if line.startswith("- ") and ": " in line:
+                k, v = line[2:].split(": ", 1)
+                kv[k.strip()] = v.strip().strip("`")
+    if kv.get("kernel_source_digest") != kernel_source_digest():
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(shape, prefill, steps):
+    """The oracle (single-threaded C, fp32 over bf16 weights) decoding `steps`
+    greedy steps of sequence 0 from position `prefill`; weights and KV are
+    generated first and not timed."""
+    from oracle.lo import Oracle
+    from synth import workloads as W
+    orc = Oracle("f32")
+    om = orc.model(shape, seed=W.SEED_WEIGHTS, w_std=0.02)
+    okv = orc.kv(shape, 1, prefill + steps + 1, seed=W.SEED_KV, kv_std=1.0, prefill=[prefill])
+    tok = W.first_tokens(1, shape["vocab"])[0]
+    w0, c0 = time.perf_counter(), time.process_time()
+    for s in range(steps):
+        _, tok = orc.decode_one(om, okv, 0, tok, prefill + s)
+    wall, cpu = time.perf_counter() - w0, time.process_time() - c0
+    return {"value": steps / wall, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{steps} greedy steps of one sequence, positions {prefill}..{prefill + steps - 1}, "
+                      f"same shape and seeds; {wall:.1f} s wall, {cpu:.1f} s CPU (one thread)"}
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "copies": 3}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -44,12 +114,17 @@ def main():
     ap.add_argument("--batch", type=int, default=1)
     ap.add_argument("--all-modes", action="store_true", help="also time the other modes")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-steps", type=int, default=4, help="oracle steps in the CPU baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only copy a 1 GiB buffer (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU only; --gpus must be 1", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
-    import numpy as np
     import torch
 
     from overlap_decode_step_amd import ld
@@ -70,27 +145,29 @@ def main():
     toks = torch.tensor(W.first_tokens(B, shape["vocab"]), dtype=torch.int32, device=dev)
     pos_all = [torch.full((B,), prefill + i, dtype=torch.int32, device=dev)
                for i in range(max(steps, warmup))]
+    # every kernel of a step is enqueued on this stream (the persistent kernel
+    # and the whole-kernel-wait kernels; the tile-flag mode forks a second
+    # stream and joins it back before the step returns)
     stream = torch.cuda.current_stream()
 
     def run(mode, n, timed):
         # greedy decode: the next tokens of step i are the inputs of step i + 1
         m.set_mode(mode)
+        m.fill_kv(W.SEED_KV, 1.0, [prefill] * B)
         tbuf = [toks.clone(), torch.empty_like(toks)]
+        torch.cuda.synchronize()
         if timed:
             ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            torch.cuda.synchronize()
             ev0.record(stream)
         for i in range(n):
             m.step(tbuf[i & 1], pos_all[i], logits, tbuf[(i + 1) & 1])
         if timed:
             ev1.record(stream)
-            torch.cuda.synchronize()
-            st = m.device_error()
-            if st != 0:
-                raise RuntimeError(f"device error {st} in mode {mode}")
-            return ev0.elapsed_time(ev1) / n
         torch.cuda.synchronize()
-        return None
+        st = m.device_error()
+        if st != 0:
+            raise RuntimeError(f"device error {st} in mode {mode}")
+        return ev0.elapsed_time(ev1) / n if timed else None
 
     results = {}
     modes = ["wait", "flags", "mega"] if args.all_modes else [args.mode]
@@ -101,9 +178,23 @@ def main():
         print(f"# mode={mode} batch={B} ms/step={ms:.4f} tok/s={B * 1000.0 / ms:.1f}",
               file=sys.stderr, flush=True)
     ms = results[args.mode]
+    m.free()
+    del m
+    torch.cuda.synchronize()
     positions = [prefill + i for i in range(steps)]
     bytes_avg = sum(algorithmic_bytes(shape, B, [p] * B) for p in positions) / steps
+    # In the persistent mode one launch is one whole step, so the per-launch
+    # duration is the timed region over the number of steps.
     achieved = bytes_avg / (ms * 1e-3) / 1e9
+    digest = kernel_source_digest()
+    print(f"# kernel_source_digest={digest} algorithmic_bytes_per_step={bytes_avg:.0f}",
+          file=sys.stderr, flush=True)
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(shape, prefill, args.cpu_steps)
+        print(f"# cpu_baseline {cpu}", file=sys.stderr, flush=True)
+    kernel = {"mega": "k_mega (persistent, one launch per step)",
+              "wait": "all stage kernels of one step", "flags": "all stage kernels of one step"}
     out = {
         "metric": "decode tokens/s + achieved HBM GB/s vs peak, Llama-1B shape, batch 1",
         "value": B * 1000.0 / ms,
@@ -121,7 +212,9 @@ def main():
                                f"positions {prefill}..{prefill + steps - 1}",
                    "mode": args.mode, "batch": B},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": read_traffic(args.mode, B),
+                     "kernel": kernel[args.mode], "algorithmic_bytes": bytes_avg},
+        "cpu_baseline": cpu,
         "modes_ms_per_step": results,
     }
     print(json.dumps(out), flush=True)

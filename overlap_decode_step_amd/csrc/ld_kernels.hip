@@ -54,8 +54,13 @@ __global__ __launch_bounds__(kMaxThreads) void k_lm(Params P, int l) {
   stage_lm<NB>(P, blockIdx.x, gridDim.x, smem);
 }
 
+// 512 threads: two waves per SIMD, so each wave may hold 256 VGPRs; the
+// union of every stage's live state does not fit in the 128 of a 1024-thread
+// workgroup without spilling to scratch memory.
+constexpr int kMegaThreads = 512;
+
 template <int NB>
-__global__ __launch_bounds__(kMaxThreads) void k_mega(Params P) {
+__global__ __launch_bounds__(kMegaThreads) void k_mega(Params P) {
   extern __shared__ __align__(16) char smem[];
   scratch_init(smem);
   const int wg = blockIdx.x, nwg = gridDim.x;
