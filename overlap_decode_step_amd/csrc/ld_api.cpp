@@ -162,13 +162,32 @@ static const size_t kLdsPerCu = 160 * 1024;
 // Attention positions per work item: the largest multiple of 32 up to 512
 // (one position per thread of the 512-thread tile-flag workgroups) whose
 // tiles fit half a CU's LDS, so two tile-flag kernels still share a CU.
+// Attention split lengths.  The longest split (Tmax) sizes the LDS tiles: a
+// multiple of 32 up to 512 whose K and V tiles fit next to the other
+// attention buffers in half a CU's LDS (two tile-flag kernels share a CU).
+// A step uses T = step_split_len(Tmax, batch): short splits at small batch
+// spread one sequence's attention over many workgroups, long ones at large
+// batch keep the number of items (and of partial results) down.
+constexpr int kMinSplit = 64;
+
+static int step_split_len(int Tmax, int batch) {
+  int T = kMinSplit;
+  while (T < 32 * batch && T < Tmax) T *= 2;
+  return std::min(T, Tmax);
+}
+
+static int max_splits_for(int Tmax, int max_seq) {
+  const int Tmin = std::min(kMinSplit, Tmax);
+  return (max_seq + Tmin - 1) / Tmin;
+}
+
 static int split_len_for(const ld_config* c, int max_seq) {
   const int group = c->n_q_heads / c->n_kv_heads;
-  const int tpp = (c->head_dim / 8 + 7) / 8;  // threads per position (64 channels each)
-  int T = 512 / tpp;
+  int T = 512;
   while (T > 32) {
-    const int ms = (max_seq + T - 1) / T;
-    if (scratch_bytes() + attn_smem(group, c->head_dim, T, ms, 1024) <= kLdsPerCu / 2) break;
+    if (scratch_bytes() + attn_smem(group, c->head_dim, T, max_splits_for(T, max_seq)) <=
+        kLdsPerCu / 2)
+      break;
     T -= 32;
   }
   return T;
@@ -179,7 +198,7 @@ static KLayout klayout(const ld_config* c, int maxB, int max_seq) {
   const size_t H = c->hidden, I = c->intermediate, d = c->head_dim;
   const size_t qd = (size_t)c->n_q_heads * d, kvd = (size_t)c->n_kv_heads * d;
   K.split_len = split_len_for(c, max_seq);
-  K.max_splits = (max_seq + K.split_len - 1) / K.split_len;
+  K.max_splits = max_splits_for(K.split_len, max_seq);
   K.max_wg = 8192;
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -341,18 +360,16 @@ static ld_status compute_grids(ld_model* m) {
   const uint32_t xcap_full = 128 * 1024;
   if (kmax > xcap_full) return fail(m, LD_EINVAL, "input rows longer than the LDS staging area");
   m->xcap_wait = m->xcap_mega = xcap_full;
-  const size_t attn_full = attn_smem(D.group, D.d, D.split_len, D.max_splits, m->thr_mega);
+  const size_t attn_full = attn_smem(D.group, D.d, D.split_len, D.max_splits);
   m->smem_wait = m->smem_mega = scratch + std::max<size_t>(xcap_full + best, attn_full);
   if (m->smem_mega > kLdsPerCu) return fail(m, LD_EINVAL, "stage tiles do not fit in LDS");
   // tile-flag mode: two consecutive stage kernels share each CU, so each
   // 512-thread workgroup gets at most half the LDS
   const size_t half = kLdsPerCu / 2;
   m->xcap_flags = (uint32_t)(half - scratch - best);
-  const size_t attn_half = attn_smem(D.group, D.d, D.split_len, D.max_splits, m->thr_flags);
+  const size_t attn_half = attn_smem(D.group, D.d, D.split_len, D.max_splits);
   m->smem_flags = scratch + std::max<size_t>(m->xcap_flags + best, attn_half);
-  const int tpp = (D.d / 8 + 7) / 8;
-  m->flags_ok = (kmax <= m->xcap_flags) && (m->smem_flags <= half) &&
-                (D.split_len * tpp <= m->thr_flags);
+  m->flags_ok = (kmax <= m->xcap_flags) && (m->smem_flags <= half);
   for (int nb = 1; nb <= maxnb; nb *= 2) {
     for (int st = 0; st <= kSLm; ++st) {
       const size_t sm = (st == 0) ? m->smem_mega : std::max(m->smem_wait, m->smem_flags);
@@ -491,6 +508,7 @@ static ld_status enqueue_step(ld_model* m, const int32_t* tokens, int32_t B, con
   P.S.logits = logits;
   P.S.next = next;
   P.S.B = B;
+  P.S.T = step_split_len(m->D.split_len, B);
   P.S.gu_variant = m->gu_variant[B];
   P.S.inject = m->inject_next;
   m->inject_next = 0;
@@ -613,6 +631,7 @@ static ld_status time_gu(ld_model* m, int B, int variant, int reps, float* ms_ou
   P.K.lm_ctr = m->tune_ctr + kStageCtrs * kCtrWords;
   P.K.split_ctr = P.K.lm_ctr + kCtrWords;
   P.S.B = B;
+  P.S.T = step_split_len(m->D.split_len, B);
   P.S.wait = 1;
   P.S.gu_variant = variant;
   P.S.x_cap = m->xcap_wait;

@@ -162,8 +162,8 @@ hipError_t set_max_dynamic_smem(int stage, int nb, size_t smem) {
 
 size_t scratch_bytes() { return kScratchBytes; }
 
-size_t attn_smem(int group, int d, int T, int max_splits, int threads) {
-  return attn_smem_bytes(group, d, T, max_splits, threads);
+size_t attn_smem(int group, int d, int T, int max_splits) {
+  return attn_smem_bytes(group, d, T, max_splits);
 }
 
 size_t best_bytes() { return kBestBytes; }

@@ -16,7 +16,7 @@ hipError_t launch_mega(const Params& P, int grid, int threads, size_t smem, hipS
 hipError_t occupancy(int stage, int nb, int threads, size_t smem, int* blocks_per_cu);
 hipError_t set_max_dynamic_smem(int stage, int nb, size_t smem);
 size_t scratch_bytes();
-size_t attn_smem(int group, int d, int T, int max_splits, int threads);
+size_t attn_smem(int group, int d, int T, int max_splits);
 size_t best_bytes();
 
 hipError_t launch_gen_normal(uint16_t* dst, int64_t n, uint64_t key, uint64_t index0, float kappa,

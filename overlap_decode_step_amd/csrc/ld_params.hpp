@@ -30,7 +30,7 @@ struct Dims {
   int L, H, nq, nkv, d, I, V, group;
   int qd, kvd, qkv_rows;
   int max_batch, max_seq;
-  int split_len, max_splits;
+  int split_len, max_splits;  // longest attention split (LDS tiles), splits per sequence at most
   int tied;
   float eps;
   float attn_scale;  // 1 / sqrt(head_dim)
@@ -79,6 +79,7 @@ struct Step {
   uint32_t t_qkv, t_attn, t_o, t_gu, t_d, t_lm;
   uint32_t inject;  // debug: added to one wait target to force a watchdog timeout
   uint32_t x_cap;   // bytes of LDS for staged input vectors
+  int T;            // attention split length of this step (<= Dims::split_len)
 };
 
 struct Params {

@@ -32,19 +32,6 @@ constexpr int kPairsGu = 1, kUcGu = 4;  // one (gate, up) row pair per task
 constexpr int kNrD = 1, kUcD = 8, kKsD = 2;  // Down: K split over two waves
 constexpr int kNrLm = 2, kUcLm = 4;
 
-// Attention LDS: rotated q [group][d], then a tile region holding the K and
-// V tiles (rows padded by one dword against bank conflicts) or, in the
-// combining workgroup, the split statistics, then scores [group][T] and the
-// split-local (max, sum) per head.
-__host__ __device__ constexpr int attn_tile_words(int group, int d, int T, int max_splits) {
-  return 2 * T * (d / 2 + 1) > 2 * group * max_splits + group ? 2 * T * (d / 2 + 1)
-                                                              : 2 * group * max_splits + group;
-}
-__host__ __device__ constexpr size_t attn_smem_bytes(int group, int d, int T, int max_splits) {
-  return (size_t)group * d * 4 + (size_t)attn_tile_words(group, d, T, max_splits) * 4 +
-         (size_t)group * T * 4 + (size_t)group * 2 * 4;
-}
-
 __device__ __forceinline__ const uint16_t* layer_w(const Params& P, int l, int64_t off) {
   return P.W.layer0 + (int64_t)l * P.W.layer_stride + off;
 }
@@ -136,100 +123,156 @@ __device__ void stage_qkv(const Params& P, int l, int wg, int nwg, char* smem) {
 //
 // Split-KV grouped-query decode attention.  A work item is (sequence b, kv
 // head, split s): positions [n0, n1) of 0..p, the splits of a sequence
-// balanced to at most T positions each.  One workgroup per item:
-//  - one round of loads: the group's q heads (rotated to p into LDS), each
-//    thread's K row into registers (one position per thread), each V row
-//    into LDS; the split holding p also rotates the new key, rounds k and v
-//    to bf16 and appends them to the cache;
-//  - scores (q . K_t) / sqrt(d) per position, the split's softmax statistics
-//    per head, and the unnormalised output sum_t e_t V_t;
+// balanced to at most T positions each.  T is chosen per step from the batch
+// size alone (the host never reads positions), so a batch-1 step spreads over
+// many workgroups.  One workgroup per item:
+//  - the split's cached K and V rows are copied into LDS with direct-to-LDS
+//    loads; they do not depend on this step's QKV outputs, so the first
+//    item's copies are issued before the readiness wait;
+//  - the group's q heads are rotated to p into LDS; the split holding p also
+//    rotates the new key, rounds k and v to bf16, appends them to the cache
+//    and places them in the tiles;
+//  - scores (q . K_t) / sqrt(d): one lane per (position, 8 channels), the
+//    8-channel partial dot products summed across the position's lanes;
+//  - the split's softmax statistics per head, then the unnormalised output
+//    sum_t e_t V_t over fixed position slices;
 //  - a single split writes o / l directly; otherwise each split stores
 //    (m, l, o) and the last-arriving split combines all splits in fixed order.
 
-__host__ __device__ constexpr size_t attn_tile_bytes(int group, int d, int T, int max_splits) {
-  // V tile [T][d] bf16, or the combining workgroup's split statistics
-  return (size_t)T * d * 2 > (size_t)(2 * group * max_splits + group) * 4
-             ? (size_t)T * d * 2
+// Position slices of the output sum: one (slice, head, 8 channels) item per
+// thread of a 512-thread workgroup, at most 16 slices.  It depends on the
+// shape only, so every mode adds the same numbers in the same order.
+__host__ __device__ constexpr int attn_parts(int group, int d) {
+  return 512 / (group * (d / 8)) < 1 ? 1 : 512 / (group * (d / 8)) > 16 ? 16 : 512 / (group * (d / 8));
+}
+__host__ __device__ constexpr size_t attn_tiles_bytes(int group, int d, int T, int max_splits) {
+  // K and V tiles [T][d] bf16, or the combining workgroup's split statistics
+  return (size_t)2 * T * d * 2 > (size_t)(2 * group * max_splits + group) * 4
+             ? (size_t)2 * T * d * 2
              : (size_t)(2 * group * max_splits + group) * 4;
 }
-__host__ __device__ constexpr size_t attn_smem_bytes(int group, int d, int T, int max_splits,
-                                                     int threads) {
-  return (size_t)group * d * 4                           /* rotated q */
-         + (attn_tile_bytes(group, d, T, max_splits) + 15) / 16 * 16
-         + (size_t)group * T * 4                         /* scores / weights */
-         + (size_t)8 * group * d * 4                     /* output partials per position slice */
-         + (size_t)group * 2 * 4                         /* (max, sum) per head */
-         + (size_t)d * 2 + 16;                           /* new key row */
+__host__ __device__ constexpr size_t attn_smem_bytes(int group, int d, int T, int max_splits) {
+  return (size_t)group * d * 4                                     /* rotated q */
+         + (attn_tiles_bytes(group, d, T, max_splits) + 15) / 16 * 16
+         + (size_t)group * T * 4                                   /* scores / weights */
+         + (size_t)attn_parts(group, d) * group * d * 4            /* output slices */
+         + (size_t)group * 2 * 4;                                  /* (max, sum) per head */
 }
 
-// Each thread holds up to 64 channels of one K row (kKw 16-byte words);
-// wider heads use tpp = ceil(d / 64) neighbouring threads per position.
-constexpr int kKw = 8;
-constexpr int kAttnParts = 8;  // position slices of the output sum (fixed: mode independent)
-constexpr int kMaxGroup = 8;   // query heads per kv head at most
+struct AttnItem {
+  int b, kvh, s, ns, p;
+};
 
-__device__ void attn_item(const Params& P, int l, int b, int kvh, int s, int nsplit, int p,
-                          char* smem) {
-  // head_dim is a power of two (checked on the host): index math uses shifts,
-  // which keeps this once-per-item code small
+// Item `it` of the step (sequence-major, then kv head, then split).
+__device__ __forceinline__ bool attn_item_at(const Params& P, const Scratch& sc, int T, int it,
+                                             AttnItem& a) {
+  int base = 0;
+  for (int b = 0; b < P.S.B; ++b) {
+    const int p = sc.pos[b], ns = (p + T) / T, cnt = P.D.nkv * ns;
+    if (it < base + cnt) {
+      a.b = b;
+      a.p = p;
+      a.ns = ns;
+      a.kvh = (it - base) / ns;
+      a.s = it - base - a.kvh * ns;
+      return true;
+    }
+    base += cnt;
+  }
+  return false;
+}
+
+struct AttnLds {
+  float* qs;     // [group][d] rotated q
+  uint16_t* Ks;  // [T][d]
+  uint16_t* Vs;  // [T][d]
+  float* Sc;     // [group][T]
+  float* op;     // [parts][group][d]
+  float* ml;     // [group][2]
+};
+
+__device__ __forceinline__ AttnLds attn_lds(const Dims& D, char* smem) {
+  AttnLds s;
+  char* base = smem + kScratchBytes;
+  const int T = D.split_len;
+  s.qs = reinterpret_cast<float*>(base);
+  s.Ks = reinterpret_cast<uint16_t*>(base + (size_t)D.group * D.d * 4);
+  s.Vs = s.Ks + (size_t)T * D.d;
+  char* after = reinterpret_cast<char*>(s.Ks) +
+                (attn_tiles_bytes(D.group, D.d, T, D.max_splits) + 15) / 16 * 16;
+  s.Sc = reinterpret_cast<float*>(after);
+  s.op = s.Sc + (size_t)D.group * T;
+  s.ml = s.op + (size_t)attn_parts(D.group, D.d) * D.group * D.d;
+  return s;
+}
+
+__device__ __forceinline__ int64_t attn_cache_off(const Params& P, int l, int b, int kvh) {
   const Dims& D = P.D;
-  const int d = D.d, half = d / 2, group = D.group, w8 = d / 8;
-  const int ld = 31 - __builtin_clz(d);
-  const int tpp = (w8 + kKw - 1) / kKw;  // threads per position (1, 2 or 4)
-  const int ltpp = 31 - __builtin_clz(tpp);
+  return ((((int64_t)l * D.max_batch + b) * D.nkv + kvh) * D.max_seq) * (int64_t)D.d;
+}
+
+// Copy the item's cached K and V rows into the LDS tiles (1 KB per wave
+// instruction, direct to LDS).  With skip_wave0 the polling wave issues none,
+// so its spin loads never wait behind these copies.
+__device__ void attn_copy_tiles(const Params& P, int l, const AttnItem& a, char* smem,
+                                bool skip_wave0) {
+  const Dims& D = P.D;
+  const AttnLds s = attn_lds(D, smem);
+  const int len = a.p + 1;
+  const int n0 = (a.s * len) / a.ns, n1 = ((a.s + 1) * len) / a.ns;
+  const int ncached = (n1 == len) ? n1 - n0 - 1 : n1 - n0;
+  const int bytes = ncached * D.d * 2;
+  const int nw = nwaves(), w0 = (skip_wave0 && nw > 1) ? 1 : 0, w = wave_id(), lane = lane_id();
+  if (w < w0 || bytes <= 0) return;
+  const int64_t off = attn_cache_off(P, l, a.b, a.kvh) + (int64_t)n0 * D.d;
+  const char* ksrc = reinterpret_cast<const char*>(P.K.kc + off);
+  const char* vsrc = reinterpret_cast<const char*>(P.K.vc + off);
+  const int chunks = (bytes + 1023) >> 10;
+  for (int c = w - w0; c < 2 * chunks; c += nw - w0) {
+    const bool isv = c >= chunks;
+    const int cb = (isv ? c - chunks : c) << 10;
+    const int o = cb + lane * 16;
+    char* dst = reinterpret_cast<char*>(isv ? s.Vs : s.Ks) + cb;
+    if (o < bytes)
+      __builtin_amdgcn_global_load_lds((isv ? vsrc : ksrc) + o,
+                                       (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+  }
+}
+
+// Sum over aligned groups of w lanes (w = 1..32, a power of two).  DPP row
+// rotations move data to higher lanes, so the total is valid in the last
+// lane of each group.
+__device__ __forceinline__ float lane_group_sum(float v, int w) {
+  if (w > 1) v += dpp_f<0xB1, 0xF>(0.f, v);     // + lane ^ 1
+  if (w > 2) v += dpp_f<0x4E, 0xF>(0.f, v);     // + lane ^ 2
+  if (w > 4) v += dpp_f<0x124, 0xF>(0.f, v);    // row_ror:4 (lane 7 of 8 gets lanes 0..3)
+  if (w > 8) v += dpp_f<0x128, 0xF>(0.f, v);    // row_ror:8 (lane 15 of 16 gets lanes 0..7)
+  if (w > 16) v += __shfl_up(v, 16, kWave);     // lane 31 of 32 gets lanes 0..15
+  return v;
+}
+
+__device__ void attn_item(const Params& P, int l, const AttnItem& a, char* smem) {
+  // head_dim is a power of two (checked on the host): index math uses shifts
+  const Dims& D = P.D;
+  const int d = D.d, half = d / 2, group = D.group, w8 = d / 8, T = D.split_len;
+  const int ld = 31 - __builtin_clz(d), lw8 = ld - 3;
   const int tid = threadIdx.x, nth = blockDim.x, lane = lane_id(), wave = wave_id();
   Scratch& sc = *reinterpret_cast<Scratch*>(smem);
-  char* base = smem + kScratchBytes;
-  float* qs = reinterpret_cast<float*>(base);                                   // [group][d]
-  uint16_t* Vs = reinterpret_cast<uint16_t*>(base + (size_t)group * d * 4);    // [T][d]
-  char* after_tile = reinterpret_cast<char*>(Vs) +
-                     (attn_tile_bytes(group, d, D.split_len, D.max_splits) + 15) / 16 * 16;
-  float* Sc = reinterpret_cast<float*>(after_tile);                             // [group][T]
-  float* op = Sc + group * D.split_len;                  // [kAttnParts][group][d]
-  float* ml = op + kAttnParts * group * d;                                      // [group][2]
-  uint16_t* Knew = reinterpret_cast<uint16_t*>(ml + group * 2);                 // [d]
-  const int T = D.split_len;
-
+  const AttnLds s = attn_lds(D, smem);
+  const int b = a.b, kvh = a.kvh, p = a.p, nsplit = a.ns;
   const int len = p + 1;
-  const int n0 = (s * len) / nsplit, n1 = ((s + 1) * len) / nsplit;
+  const int n0 = (a.s * len) / nsplit, n1 = ((a.s + 1) * len) / nsplit;
   const int n = n1 - n0;
   const bool has_new = (n1 == len);
-  const int ncached = has_new ? n - 1 : n;  // rows read from the cache
   const float* qkv = P.K.qkv + (int64_t)b * D.qkv_rows;
   const float* rope = P.K.rope + (int64_t)p * half * 2;
-  const int64_t cache_off =
-      ((((int64_t)l * D.max_batch + b) * D.nkv + kvh) * D.max_seq) * (int64_t)d;
+  const int64_t cache_off = attn_cache_off(P, l, b, kvh);
   uint16_t* kc = P.K.kc + cache_off;
   uint16_t* vc = P.K.vc + cache_off;
 
-  // ---- one round of loads, all issued before any is consumed
+  // ---- q heads of this group (one (head, pair) per thread: group * half <=
+  // 512) and, in the split holding p, the new k and v
   trace_ev(P, l, 6, 0, blockIdx.x);
-  // cached V rows [n0, n0 + ncached) are contiguous: copy them into LDS with
-  // direct-to-LDS loads, 1 KB per wave instruction
-  {
-    const int bytes = ncached * d * 2;
-    const char* src = reinterpret_cast<const char*>(vc + (int64_t)n0 * d);
-    char* dst = reinterpret_cast<char*>(Vs);
-    for (int c = wave * 1024; c < bytes; c += nwaves() * 1024) {
-      const int off = c + lane * 16;
-      if (off < bytes)
-        __builtin_amdgcn_global_load_lds(src + off,
-                                         (__attribute__((address_space(3))) void*)(dst + c), 16, 0,
-                                         0);
-    }
-  }
-  // this thread's slice of one position's K row into registers
-  const int t = tid >> ltpp, part = tid & (tpp - 1), j0 = part * kKw;
-  const bool mine = t < ncached;
-  u32x4 kr[kKw];
-  if (mine) {
-    const uint16_t* krow = kc + (int64_t)(n0 + t) * d + j0 * 8;
-#pragma unroll
-    for (int j = 0; j < kKw; ++j)
-      if (j0 + j < w8) kr[j] = *reinterpret_cast<const u32x4*>(krow + j * 8);
-  }
-  // q heads of this group (one (head, pair) per thread: group * half <= nth)
-  // and, in the split holding p, the new k and v
   const bool qthread = tid < group * half;
   const int qg = tid >> (ld - 1), qi = tid & (half - 1);
   float q0 = 0.f, q1 = 0.f, cq = 0.f, sq = 0.f;
@@ -251,123 +294,110 @@ __device__ void attn_item(const Params& P, int l, int b, int kvh, int s, int nsp
     v1 = ld_coh(vh + tid + half);
   }
   if (qthread) {  // rotate q (rotate-half pairs) into LDS
-    qs[qg * d + qi] = q0 * cq - q1 * sq;
-    qs[qg * d + qi + half] = q0 * sq + q1 * cq;
+    s.qs[qg * d + qi] = q0 * cq - q1 * sq;
+    s.qs[qg * d + qi + half] = q0 * sq + q1 * cq;
   }
   if (newrow) {
     // rotate the new key, round k and v to bf16, append them to the cache at p
     // (thread tid < half holds pair tid, whose cos/sin it loaded as a q thread)
-    const uint16_t a = f2bf(k0 * cq - k1 * sq), bb = f2bf(k0 * sq + k1 * cq);
-    const uint16_t e0 = f2bf(v0), e1 = f2bf(v1);
-    kc[(int64_t)p * d + tid] = a;
-    kc[(int64_t)p * d + tid + half] = bb;
-    vc[(int64_t)p * d + tid] = e0;
-    vc[(int64_t)p * d + tid + half] = e1;
-    Knew[tid] = a;
-    Knew[tid + half] = bb;
-    Vs[(int64_t)(n - 1) * d + tid] = e0;
-    Vs[(int64_t)(n - 1) * d + tid + half] = e1;
+    const uint16_t ka = f2bf(k0 * cq - k1 * sq), kb = f2bf(k0 * sq + k1 * cq);
+    const uint16_t va = f2bf(v0), vb = f2bf(v1);
+    kc[(int64_t)p * d + tid] = ka;
+    kc[(int64_t)p * d + tid + half] = kb;
+    vc[(int64_t)p * d + tid] = va;
+    vc[(int64_t)p * d + tid + half] = vb;
+    s.Ks[(n - 1) * d + tid] = ka;
+    s.Ks[(n - 1) * d + tid + half] = kb;
+    s.Vs[(n - 1) * d + tid] = va;
+    s.Vs[(n - 1) * d + tid + half] = vb;
   }
   wave_drain();  // direct-to-LDS copies have landed
   __syncthreads();
   trace_ev(P, l, 7, 0, blockIdx.x);
 
-  // ---- scores s_t = (q . K_t) * scale; a position's channel slices are
-  // added in ascending order across its tpp neighbouring lanes
-  if (t < n && !mine) {
-#pragma unroll
-    for (int j = 0; j < kKw; ++j)
-      if (j0 + j < w8) kr[j] = *reinterpret_cast<const u32x4*>(Knew + (j0 + j) * 8);
-  }
-  // one head at a time (a runtime loop keeps this code small: it runs once
-  // per item, so its instruction fetches are not amortised)
+  // ---- scores: lane (t, c8) takes channels [8 c8, 8 c8 + 8) of position t
+  // for every head; the w8 lanes of a position are aligned within a wave
+  for (int idx = tid; idx < n * w8; idx += nth) {
+    const int t = idx >> lw8, c8 = idx & (w8 - 1);
+    const u32x4 kw = *reinterpret_cast<const u32x4*>(s.Ks + t * d + c8 * 8);
+    const float kf[8] = {bf16lo(kw.x), bf16hi(kw.x), bf16lo(kw.y), bf16hi(kw.y),
+                         bf16lo(kw.z), bf16hi(kw.z), bf16lo(kw.w), bf16hi(kw.w)};
 #pragma clang loop unroll(disable)
-  for (int g = 0; g < group; ++g) {
-    float acc = 0.f;
-    if (t < n) {
-      const float* qgp = qs + g * d + j0 * 8;
-#pragma unroll
-      for (int j = 0; j < kKw; ++j) {
-        if (j0 + j < w8) {
-          const float4 qa = *reinterpret_cast<const float4*>(qgp + j * 8);
-          const float4 qb = *reinterpret_cast<const float4*>(qgp + j * 8 + 4);
-          acc = fmaf(qa.x, bf16lo(kr[j].x), acc);
-          acc = fmaf(qa.y, bf16hi(kr[j].x), acc);
-          acc = fmaf(qa.z, bf16lo(kr[j].y), acc);
-          acc = fmaf(qa.w, bf16hi(kr[j].y), acc);
-          acc = fmaf(qb.x, bf16lo(kr[j].z), acc);
-          acc = fmaf(qb.y, bf16hi(kr[j].z), acc);
-          acc = fmaf(qb.z, bf16lo(kr[j].w), acc);
-          acc = fmaf(qb.w, bf16hi(kr[j].w), acc);
-        }
-      }
+    for (int g = 0; g < group; ++g) {
+      const float4 qa = *reinterpret_cast<const float4*>(s.qs + g * d + c8 * 8);
+      const float4 qb = *reinterpret_cast<const float4*>(s.qs + g * d + c8 * 8 + 4);
+      float acc = qa.x * kf[0];
+      acc = fmaf(qa.y, kf[1], acc);
+      acc = fmaf(qa.z, kf[2], acc);
+      acc = fmaf(qa.w, kf[3], acc);
+      acc = fmaf(qb.x, kf[4], acc);
+      acc = fmaf(qb.y, kf[5], acc);
+      acc = fmaf(qb.z, kf[6], acc);
+      acc = fmaf(qb.w, kf[7], acc);
+      acc = lane_group_sum(acc, w8);
+      if (c8 == w8 - 1) s.Sc[g * T + t] = acc * D.attn_scale;
     }
-    for (int q2 = 1; q2 < tpp; ++q2) {
-      const float o = __shfl(acc, (lane & ~(tpp - 1)) + q2, kWave);
-      if (part == 0) acc += o;
-    }
-    if (t < n && part == 0) Sc[g * T + t] = acc * D.attn_scale;
   }
   __syncthreads();
   // ---- split-local softmax statistics per head
   for (int g = wave; g < group; g += nwaves()) {
     float m = -INFINITY;
-    for (int u = lane; u < n; u += kWave) m = fmaxf(m, Sc[g * T + u]);
+    for (int u = lane; u < n; u += kWave) m = fmaxf(m, s.Sc[g * T + u]);
     m = wave_max(m);
     float sum = 0.f;
     for (int u = lane; u < n; u += kWave) {
-      const float e = expf(Sc[g * T + u] - m);
-      Sc[g * T + u] = e;
+      const float e = expf(s.Sc[g * T + u] - m);
+      s.Sc[g * T + u] = e;
       sum += e;
     }
     sum = wave_sum(sum);
     if (lane == 0) {
-      ml[2 * g] = m;
-      ml[2 * g + 1] = sum;
+      s.ml[2 * g] = m;
+      s.ml[2 * g + 1] = sum;
     }
   }
   __syncthreads();
   trace_ev(P, l, 7, 1, blockIdx.x);
-  // ---- unnormalised output sum_t e_t V_t: each item is (position slice,
-  // head, 8 channels); per position one 16-byte V read and one broadcast
-  // weight, two independent accumulator sets; the kAttnParts slices are then
-  // added in fixed order
+  // ---- unnormalised output sum_t e_t V_t: item (position slice, head, 8
+  // channels); per position one 16-byte V read and one broadcast weight, two
+  // independent accumulator sets; the slices are then added in fixed order
+  const int parts = attn_parts(group, d);
   const int gd = group * d;
-  for (int it = tid; it < kAttnParts * group * w8; it += nth) {
+  for (int it = tid; it < parts * group * w8; it += nth) {
     const int c8 = it & (w8 - 1);
-    const int slg = it >> (ld - 3);  // slice * group + head
+    const int slg = it >> lw8;  // slice * group + head
     const int sl = slg / group, g = slg - sl * group;
-    const int u0 = (sl * n) / kAttnParts, u1 = ((sl + 1) * n) / kAttnParts;
-    const float* e = Sc + g * T;
-    const uint16_t* vcol = Vs + c8 * 8;
-    float a[8], c[8];
+    const int u0 = (sl * n) / parts, u1 = ((sl + 1) * n) / parts;
+    const float* e = s.Sc + g * T;
+    const uint16_t* vcol = s.Vs + c8 * 8;
+    float x[8], y[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) a[k] = c[k] = 0.f;
+    for (int k = 0; k < 8; ++k) x[k] = y[k] = 0.f;
     int u = u0;
     for (; u + 2 <= u1; u += 2) {
       const u32x4 va = *reinterpret_cast<const u32x4*>(vcol + u * d);
       const u32x4 vb = *reinterpret_cast<const u32x4*>(vcol + (u + 1) * d);
       const float ea = e[u], eb = e[u + 1];
-      a[0] = fmaf(ea, bf16lo(va.x), a[0]); a[1] = fmaf(ea, bf16hi(va.x), a[1]);
-      a[2] = fmaf(ea, bf16lo(va.y), a[2]); a[3] = fmaf(ea, bf16hi(va.y), a[3]);
-      a[4] = fmaf(ea, bf16lo(va.z), a[4]); a[5] = fmaf(ea, bf16hi(va.z), a[5]);
-      a[6] = fmaf(ea, bf16lo(va.w), a[6]); a[7] = fmaf(ea, bf16hi(va.w), a[7]);
-      c[0] = fmaf(eb, bf16lo(vb.x), c[0]); c[1] = fmaf(eb, bf16hi(vb.x), c[1]);
-      c[2] = fmaf(eb, bf16lo(vb.y), c[2]); c[3] = fmaf(eb, bf16hi(vb.y), c[3]);
-      c[4] = fmaf(eb, bf16lo(vb.z), c[4]); c[5] = fmaf(eb, bf16hi(vb.z), c[5]);
-      c[6] = fmaf(eb, bf16lo(vb.w), c[6]); c[7] = fmaf(eb, bf16hi(vb.w), c[7]);
+      x[0] = fmaf(ea, bf16lo(va.x), x[0]); x[1] = fmaf(ea, bf16hi(va.x), x[1]);
+      x[2] = fmaf(ea, bf16lo(va.y), x[2]); x[3] = fmaf(ea, bf16hi(va.y), x[3]);
+      x[4] = fmaf(ea, bf16lo(va.z), x[4]); x[5] = fmaf(ea, bf16hi(va.z), x[5]);
+      x[6] = fmaf(ea, bf16lo(va.w), x[6]); x[7] = fmaf(ea, bf16hi(va.w), x[7]);
+      y[0] = fmaf(eb, bf16lo(vb.x), y[0]); y[1] = fmaf(eb, bf16hi(vb.x), y[1]);
+      y[2] = fmaf(eb, bf16lo(vb.y), y[2]); y[3] = fmaf(eb, bf16hi(vb.y), y[3]);
+      y[4] = fmaf(eb, bf16lo(vb.z), y[4]); y[5] = fmaf(eb, bf16hi(vb.z), y[5]);
+      y[6] = fmaf(eb, bf16lo(vb.w), y[6]); y[7] = fmaf(eb, bf16hi(vb.w), y[7]);
     }
     if (u < u1) {
       const u32x4 va = *reinterpret_cast<const u32x4*>(vcol + u * d);
       const float ea = e[u];
-      a[0] = fmaf(ea, bf16lo(va.x), a[0]); a[1] = fmaf(ea, bf16hi(va.x), a[1]);
-      a[2] = fmaf(ea, bf16lo(va.y), a[2]); a[3] = fmaf(ea, bf16hi(va.y), a[3]);
-      a[4] = fmaf(ea, bf16lo(va.z), a[4]); a[5] = fmaf(ea, bf16hi(va.z), a[5]);
-      a[6] = fmaf(ea, bf16lo(va.w), a[6]); a[7] = fmaf(ea, bf16hi(va.w), a[7]);
+      x[0] = fmaf(ea, bf16lo(va.x), x[0]); x[1] = fmaf(ea, bf16hi(va.x), x[1]);
+      x[2] = fmaf(ea, bf16lo(va.y), x[2]); x[3] = fmaf(ea, bf16hi(va.y), x[3]);
+      x[4] = fmaf(ea, bf16lo(va.z), x[4]); x[5] = fmaf(ea, bf16hi(va.z), x[5]);
+      x[6] = fmaf(ea, bf16lo(va.w), x[6]); x[7] = fmaf(ea, bf16hi(va.w), x[7]);
     }
-    float4* o4 = reinterpret_cast<float4*>(op + sl * gd + g * d + c8 * 8);
-    o4[0] = make_float4(a[0] + c[0], a[1] + c[1], a[2] + c[2], a[3] + c[3]);
-    o4[1] = make_float4(a[4] + c[4], a[5] + c[5], a[6] + c[6], a[7] + c[7]);
+    float4* o4 = reinterpret_cast<float4*>(s.op + sl * gd + g * d + c8 * 8);
+    o4[0] = make_float4(x[0] + y[0], x[1] + y[1], x[2] + y[2], x[3] + y[3]);
+    o4[1] = make_float4(x[4] + y[4], x[5] + y[5], x[6] + y[6], x[7] + y[7]);
   }
   __syncthreads();
   float* out = P.K.ao + (int64_t)b * D.qd + kvh * gd;
@@ -375,15 +405,15 @@ __device__ void attn_item(const Params& P, int l, int b, int kvh, int s, int nsp
     const int g = r >> ld, i = r & (d - 1);
     float o = 0.f;
 #pragma clang loop unroll(disable)
-    for (int sl = 0; sl < kAttnParts; ++sl) o += op[sl * gd + r];
+    for (int sl = 0; sl < parts; ++sl) o += s.op[sl * gd + r];
     if (nsplit == 1) {
-      st_coh(out + r, o / ml[2 * g + 1]);
+      st_coh(out + r, o / s.ml[2 * g + 1]);
     } else {
-      float* pp = P.K.part + (((int64_t)b * D.nq + kvh * group + g) * D.max_splits + s) * (d + 2);
+      float* pp = P.K.part + (((int64_t)b * D.nq + kvh * group + g) * D.max_splits + a.s) * (d + 2);
       st_coh(pp + 2 + i, o);
       if (i == 0) {
-        st_coh(pp, ml[2 * g]);
-        st_coh(pp + 1, ml[2 * g + 1]);
+        st_coh(pp, s.ml[2 * g]);
+        st_coh(pp + 1, s.ml[2 * g + 1]);
       }
     }
   }
@@ -402,18 +432,18 @@ __device__ void attn_item(const Params& P, int l, int b, int kvh, int s, int nsp
     __syncthreads();
     trace_ev(P, l, 7, 3, blockIdx.x);
     if (!sc.flag[0]) return;
-    // split statistics of the group's heads -> LDS (over the V tile); then per
+    // split statistics of the group's heads -> LDS (over the tiles); then per
     // head M = max m_s, f_s = e^(m_s - M), L = sum l_s f_s
-    float* ms = reinterpret_cast<float*>(Vs);  // [group][nsplit] max, then weight f_s
-    float* ls = ms + group * nsplit;           // [group][nsplit] sums
-    float* Lg = ls + group * nsplit;           // [group] combined sums
+    float* ms = reinterpret_cast<float*>(s.Ks);  // [group][nsplit] max, then weight f_s
+    float* ls = ms + group * nsplit;             // [group][nsplit] sums
+    float* Lg = ls + group * nsplit;             // [group] combined sums
     const float* pbase = P.K.part + ((int64_t)b * D.nq + kvh * group) * D.max_splits * (d + 2);
-    for (int g = 0; g < group; ++g)
-      for (int sp = tid; sp < nsplit; sp += nth) {
-        const float* q = pbase + ((int64_t)g * D.max_splits + sp) * (d + 2);
-        ms[g * nsplit + sp] = ld_coh(q);
-        ls[g * nsplit + sp] = ld_coh(q + 1);
-      }
+    for (int i = tid; i < group * nsplit; i += nth) {
+      const int g = i / nsplit, sp = i - g * nsplit;
+      const float* q = pbase + ((int64_t)g * D.max_splits + sp) * (d + 2);
+      ms[i] = ld_coh(q);
+      ls[i] = ld_coh(q + 1);
+    }
     __syncthreads();
     for (int g = wave; g < group; g += nwaves()) {
       float M = -INFINITY;
@@ -449,36 +479,33 @@ __device__ void attn_item(const Params& P, int l, int b, int kvh, int s, int nsp
   signal_if(P, stage_ctr(P, l, kCAttn), b * D.nkv + kvh);
 }
 
-__device__ void attn_items(const Params& P, int l, int wg, int nwg, char* smem) {
+__device__ void stage_attn(const Params& P, int l, int wg, int nwg, char* smem) {
   const Dims& D = P.D;
-  const int T = D.split_len, B = P.S.B;
+  trace_ev(P, l, kSAttn, 0, wg);
   Scratch& sc = *reinterpret_cast<Scratch*>(smem);
   if (!sc.pos_ok) {  // positions of the step, read once per kernel
-    if (threadIdx.x < B) sc.pos[threadIdx.x] = clamp_pos(P, threadIdx.x);
+    if (threadIdx.x < P.S.B) sc.pos[threadIdx.x] = clamp_pos(P, threadIdx.x);
     __syncthreads();
     if (threadIdx.x == 0) sc.pos_ok = 1;
   }
-  int total = 0;
-  for (int b = 0; b < B; ++b) total += D.nkv * ((sc.pos[b] + T) / T);
-  for (int it = wg; it < total; it += nwg) {
-    int b = 0, base = 0, ns = 0, p = 0;
-    for (;; ++b) {
-      p = sc.pos[b];
-      ns = (p + T) / T;  // splits of at most T positions over 0..p
-      if (it < base + D.nkv * ns) break;
-      base += D.nkv * ns;
-    }
-    const int kvh = (it - base) / ns, s = (it - base) - kvh * ns;
-    attn_item(P, l, b, kvh, s, ns, p, smem);
-    __syncthreads();  // shared memory is reused by the next item
-  }
-}
-
-__device__ void stage_attn(const Params& P, int l, int wg, int nwg, char* smem) {
-  trace_ev(P, l, kSAttn, 0, wg);
+  const int T = P.S.T;
+  AttnItem a;
+  const bool any = attn_item_at(P, sc, T, wg, a);
+  // the first item's cached rows are copied while this stage's input is
+  // still being produced
+  if (any) attn_copy_tiles(P, l, a, smem, !P.S.wait);
   if (!P.S.wait) wg_wait(sync_of(P), stage_ctr(P, l, kCQkv), P.S.t_qkv + P.S.inject, kSAttn);
   trace_ev(P, l, kSAttn, 1, wg);
-  attn_items(P, l, wg, nwg, smem);
+  if (any) {
+    for (int it = wg;;) {
+      attn_item(P, l, a, smem);
+      __syncthreads();  // LDS is reused by the next item
+      it += nwg;
+      if (!attn_item_at(P, sc, T, it, a)) break;
+      attn_copy_tiles(P, l, a, smem, false);
+    }
+  }
+  (void)D;
   trace_ev(P, l, kSAttn, 3, wg);
 }
 
