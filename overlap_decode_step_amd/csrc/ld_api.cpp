@@ -43,7 +43,7 @@ struct ld_model {
   bool gu_tuned[65];
   // launch geometry per mode: grid, threads per workgroup, LDS bytes, LDS for staged inputs
   int grid_wait = 0, grid_flags = 0, grid_mega[9] = {0};  // grid_mega indexed by nb
-  int thr_wait = 1024, thr_flags = 512, thr_mega = 512;
+  int thr_wait = 512, thr_flags = 512, thr_mega = 512;
   size_t smem_wait = 0, smem_flags = 0, smem_mega = 0;
   uint32_t xcap_wait = 0, xcap_flags = 0, xcap_mega = 0;
   bool flags_ok = true;
@@ -95,6 +95,17 @@ static bool cfg_ok(const ld_config* c, std::string* why) {
   if (c->n_q_heads % c->n_kv_heads || c->n_q_heads / c->n_kv_heads > 8) {
     *why = "n_q_heads must be a multiple of n_kv_heads, with at most 8 query heads per group";
     return false;
+  }
+  {
+    // every weight matrix, and each layer's block, is read through one buffer
+    // resource with 32-bit offsets
+    const size_t H = c->hidden, I = c->intermediate;
+    const size_t qd = (size_t)c->n_q_heads * c->head_dim, kvd = (size_t)c->n_kv_heads * c->head_dim;
+    const size_t layer = 2 * (2 * H + (qd + 2 * kvd) * H + H * qd + 3 * I * H) + 7 * 256;
+    if (layer > kMaxWeightBuffer || (size_t)c->vocab * H * 2 > kMaxWeightBuffer) {
+      *why = "a layer's weights and the LM head must each be below 4 GB";
+      return false;
+    }
   }
   if (!(c->rms_eps >= 0.f) || !(c->rope_theta > 0.f)) {
     *why = "bad rms_eps or rope_theta";
@@ -355,8 +366,7 @@ static ld_status compute_grids(ld_model* m) {
   const int maxnb = nb_for_batch(D.max_batch);
   const size_t scratch = scratch_bytes(), best = best_bytes();
   const size_t kmax = (size_t)std::max(std::max(D.H, D.I), D.qd) * 4;  // longest staged input row
-  // whole-kernel wait and persistent modes: one workgroup per CU (1024 and
-  // 512 threads)
+  // whole-kernel wait and persistent modes: one 512-thread workgroup per CU
   const uint32_t xcap_full = 128 * 1024;
   if (kmax > xcap_full) return fail(m, LD_EINVAL, "input rows longer than the LDS staging area");
   m->xcap_wait = m->xcap_mega = xcap_full;

@@ -17,7 +17,8 @@ constexpr int kChunk = kWave * 8;          // bf16 elements covered by one 16-by
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ int nwaves() { return blockDim.x >> 6; }
-__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+// the wave index is uniform: keep it (and what is derived from it) scalar
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
 // ----------------------------------------------------------------- bf16

@@ -131,25 +131,45 @@ __device__ __forceinline__ void stage_x(const XSrc& src, int b0, int nb, int K,
   __syncthreads();
 }
 
+// Weights are read through buffer loads: the row's byte offset goes in the
+// scalar offset operand (it is the same for the whole wave), the lane's
+// column offset in a vector register shared by all rows of a block.  A masked
+// row uses a zero-length buffer, whose loads return zeros without touching
+// memory, so every wave issues the same loads on every path; that keeps the
+// compiler's memory-counter waits exact for a ring of blocks in flight.  A
+// lane whose columns lie past the row end rereads the row's last 16 bytes
+// (the FMA skips those lanes).  Cache policy: non-temporal (weights are
+// streamed once per step).
+constexpr uint32_t kOob = 0xFFFFFFFFu;  // row offset of a masked row
+constexpr int kRsrcWord3 = 0x00020000;  // 32-bit data format, raw (untyped) access
+constexpr int kNt = 2;                  // cache policy: non-temporal
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t weight_rsrc(const uint16_t* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), (short)0, (int)bytes,
+                                           kRsrcWord3);
+}
+
 // A block of weights held in registers: NR rows x UC chunks, one 16-byte
 // word per lane each.
 template <int NR, int UC>
 struct WBlock {
   u32x4 w[NR][UC];
 
-  // rows[r]: row r of the task (nullptr = masked row); columns >= kend masked.
-  __device__ __forceinline__ void load(const uint16_t* const (&rows)[NR], int kend, int c0,
-                                       int lane) {
+  // roff[r]: byte offset of row r in the buffer [base, base + bytes), or kOob
+  // (masked row); rows have K columns.
+  __device__ __forceinline__ void load(const uint16_t* base, uint32_t bytes,
+                                       const uint32_t (&roff)[NR], int K, int c0, int lane) {
+    uint32_t voff[UC];
+#pragma unroll
+    for (int u = 0; u < UC; ++u)
+      voff[u] = (uint32_t)min(((c0 + u) * kChunk + lane * 8) * 2, K * 2 - 16);
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
+      const bool ok = roff[r] != kOob;
+      const __amdgpu_buffer_rsrc_t rs = weight_rsrc(base, ok ? bytes : 0u);
+      const uint32_t so = ok ? roff[r] : 0u;
 #pragma unroll
-      for (int u = 0; u < UC; ++u) {
-        const int k = (c0 + u) * kChunk + lane * 8;
-        if (rows[r] != nullptr && k < kend)
-          w[r][u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rows[r] + k));
-        else
-          w[r][u] = u32x4{0u, 0u, 0u, 0u};
-      }
+      for (int u = 0; u < UC; ++u) w[r][u] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff[u], so, kNt);
     }
   }
 
@@ -178,111 +198,87 @@ struct WBlock {
 };
 
 // One GEMV stage for one workgroup.  Rows are split into tiles of NR rows
-// (RowFn(tile, rows) fills the row pointers) and the K dimension into KS
-// slices; a task is (tile, slice) and tasks are dealt to the waves of the
-// whole grid in rounds.  The KS slices of a tile land on KS neighbouring
-// waves of one workgroup and are added through LDS in fixed order.  The batch
-// is processed in tiles of at most `bw` rows that fit the LDS staging area.
+// (RowFn(tile, rows) fills the row pointers, nullptr for a masked row; all
+// rows lie in the buffer [wbase, wbase + wbytes)), one tile per task, and
+// tasks are dealt to the waves of the whole grid round-robin.  Each wave
+// streams its tasks' weights as one sequence of blocks of UC chunks and keeps
+// PF blocks in flight (a ring of registers); the first PF are issued before
+// the stage waits for its input, except in wave 0, which polls the readiness
+// counter (loads return in order, so weight loads in flight would delay every
+// poll).  The batch is processed in tiles of at most `bw` rows that fit the
+// LDS staging area; each batch tile streams the weights again.
 // Epi(tile, b0, nb, acc, scratch) consumes the reduced sums (every lane of the
-// calling wave holds every sum).  Wait(): the readiness wait, called once
-// after the first block has been issued.
-template <int NR, int UC, int NB, int KS, class RowFn, class WaitFn, class Epi>
-__device__ __forceinline__ void gemv_stage(const RowFn& rowfn, int ntile, int K, const XSrc& src,
+// calling wave holds every sum).
+template <int NR, int UC, int NB, int PF, class RowFn, class WaitFn, class Epi>
+__device__ __forceinline__ void gemv_stage(const RowFn& rowfn, int ntile, int K,
+                                           const uint16_t* wbase, uint32_t wbytes, const XSrc& src,
                                            const uint16_t* gain, bool norm, float eps, int B,
                                            int bw, const WaitFn& wait, Epi& epi, int wg, int nwg,
                                            char* smem) {
-  static_assert(NR * NB <= 8 || KS == 1, "K-split partials must fit the scratch row");
   Scratch& sc = *reinterpret_cast<Scratch*>(smem);
   float* xs = reinterpret_cast<float*>(smem + kScratchBytes);
   const int lane = lane_id(), wave = wave_id();
-  const int first = wg * nwaves() + wave, stride = nwg * nwaves();
   const int nch = (K + kChunk - 1) / kChunk;
-  const int nchp = (nch + KS - 1) / KS;  // chunks per K slice
-  const int ntask = ntile * KS;
-  const int rounds = (ntask + stride - 1) / stride;
+  const int bpt = (nch + UC - 1) / UC;  // blocks per task
+  // Round q deals tiles [q * stride, (q + 1) * stride) to the grid's waves in
+  // order, so at any time the whole grid streams one contiguous window of the
+  // matrix (measured faster than giving each XCD its own contiguous range).
+  const int first = wg * nwaves() + wave, stride = nwg * nwaves();
+  auto task_of = [&](int q) { return first + q * stride; };
+  const int ntask = first < ntile ? (ntile - 1 - first) / stride + 1 : 0;
+  const int nblk = ntask * bpt;         // this wave's blocks
   const int nbt = (B + bw - 1) / bw;
-  auto slice = [&](int t, int& c0, int& kend) {
-    const int kp = t % KS;
-    c0 = kp * nchp;
-    kend = min(K, (kp + 1) * nchp * kChunk);
+  WBlock<NR, UC> ring[PF];
+  // block i of this wave: task i / bpt, chunks from (i % bpt) * UC; past the
+  // end every row is masked
+  auto issue = [&](WBlock<NR, UC>& blk, int i) {
+    const int q = i / bpt;
+    uint32_t roff[NR];
+    const uint16_t* rows[NR];
+    rowfn(task_of(q), rows);
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+      roff[r] = __builtin_amdgcn_readfirstlane(
+          (i < nblk && rows[r] != nullptr)
+              ? (uint32_t)(reinterpret_cast<const char*>(rows[r]) - reinterpret_cast<const char*>(wbase))
+              : kOob);
+    blk.load(wbase, wbytes, roff, K, (i - q * bpt) * UC, lane);
   };
-  const uint16_t* rows[NR];
-  WBlock<NR, UC> blk;
-  bool have = false;  // blk holds block 0 of task `first`
-  // Prefetch across the wait, except in wave 0: it polls the readiness
-  // counter, and loads return in order, so weight loads in flight would delay
-  // every poll it makes.
-  if (first < ntask && wave != 0) {
-    int c0, kend;
-    slice(first, c0, kend);
-    rowfn(first / KS, rows);
-    blk.load(rows, kend, c0, lane);
-    have = true;
+  if (wave != 0) {
+#pragma unroll
+    for (int j = 0; j < PF; ++j) issue(ring[j], j);
   }
   wait();
   for (int bt = 0; bt < nbt; ++bt) {
     const int b0 = bt * bw, nb = min(bw, B - b0);
     stage_x<NB>(src, b0, nb, K, gain, norm, eps, xs, sc);
-    for (int r = 0; r < rounds; ++r) {
-      const int t = first + r * stride;
-      float acc[NR][NB];
+    if (bt > 0 || wave == 0) {
 #pragma unroll
-      for (int i = 0; i < NR; ++i)
+      for (int j = 0; j < PF; ++j) issue(ring[j], j);
+    }
+    float acc[NR][NB];
 #pragma unroll
-        for (int b = 0; b < NB; ++b) acc[i][b] = 0.f;
-      if (t < ntask) {
-        int c0, kend;
-        slice(t, c0, kend);
-        if (!have) {
-          rowfn(t / KS, rows);
-          blk.load(rows, kend, c0, lane);
+    for (int r = 0; r < NR; ++r)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) acc[r][b] = 0.f;
+    for (int i0 = 0; i0 < nblk; i0 += PF) {
+#pragma unroll
+      for (int j = 0; j < PF; ++j) {
+        const int i = i0 + j;
+        const int q = i / bpt, c = (i - q * bpt) * UC;
+        if (i < nblk) ring[j].template fma<NB>(xs, K, nb, K, c, lane, acc);
+        issue(ring[j], i + PF);
+        if (i < nblk && c + UC >= nch) {  // last block of task q
+#pragma unroll
+          for (int r = 0; r < NR; ++r)
+#pragma unroll
+            for (int b = 0; b < NB; ++b) acc[r][b] = wave_sum(acc[r][b]);
+          epi(task_of(q), b0, nb, acc, sc);
+#pragma unroll
+          for (int r = 0; r < NR; ++r)
+#pragma unroll
+            for (int b = 0; b < NB; ++b) acc[r][b] = 0.f;
         }
-        have = false;
-        const int cend = min(nch, c0 + nchp);
-        for (int c = c0;;) {
-          blk.template fma<NB>(xs, K, nb, kend, c, lane, acc);
-          c += UC;
-          if (c >= cend) break;
-          blk.load(rows, kend, c, lane);
-        }
-        // issue the next task's first block before reducing this one
-        const int tn = t + stride;
-        const int tnext = tn < ntask ? tn : ((bt + 1 < nbt) ? first : -1);
-        if (tnext >= 0) {
-          int c1, k1;
-          slice(tnext, c1, k1);
-          rowfn(tnext / KS, rows);
-          blk.load(rows, k1, c1, lane);
-          have = true;
-        }
-#pragma unroll
-        for (int i = 0; i < NR; ++i)
-#pragma unroll
-          for (int b = 0; b < NB; ++b) acc[i][b] = wave_sum(acc[i][b]);
-      }
-      if constexpr (KS == 1) {
-        if (t < ntask) epi(t, b0, nb, acc, sc);
-      } else {
-        // slices of one tile sit on waves wave - wave % KS .. + KS - 1
-        if (lane == 0) {
-#pragma unroll
-          for (int i = 0; i < NR; ++i)
-#pragma unroll
-            for (int b = 0; b < NB; ++b) sc.red[wave][i * NB + b] = acc[i][b];
-        }
-        __syncthreads();
-        if (t < ntask && wave % KS == 0) {
-#pragma unroll
-          for (int i = 0; i < NR; ++i)
-#pragma unroll
-            for (int b = 0; b < NB; ++b) {
-              float v = 0.f;
-              for (int q = 0; q < KS; ++q) v += sc.red[wave + q][i * NB + b];
-              acc[i][b] = v;
-            }
-          epi(t / KS, b0, nb, acc, sc);
-        }
-        __syncthreads();
       }
     }
     if (bt + 1 < nbt) __syncthreads();  // every wave is done with xs before restaging

@@ -16,51 +16,51 @@
 
 namespace ld {
 
-constexpr int kMaxThreads = kMaxWaves * kWave;
+// 512-thread workgroups.  The persistent kernel runs one per CU, so each wave
+// may hold up to 256 VGPRs (the weight-block rings of the GEMV engine live in
+// registers); the stage kernels are held to 128 (four waves per SIMD) so that
+// two of them fit on a CU side by side in the tile-flag mode.
+constexpr int kMaxThreads = 512;
+constexpr int kStageWavesPerSimd = 4;
 
 template <int NB>
-__global__ __launch_bounds__(kMaxThreads) void k_qkv(Params P, int l) {
+__global__ __launch_bounds__(kMaxThreads, kStageWavesPerSimd) void k_qkv(Params P, int l) {
   extern __shared__ __align__(16) char smem[];
   stage_qkv<NB>(P, l, blockIdx.x, gridDim.x, smem);
 }
 
-__global__ __launch_bounds__(kMaxThreads) void k_attn(Params P, int l) {
+__global__ __launch_bounds__(kMaxThreads, kStageWavesPerSimd) void k_attn(Params P, int l) {
   extern __shared__ __align__(16) char smem[];
   scratch_init(smem);
   stage_attn(P, l, blockIdx.x, gridDim.x, smem);
 }
 
 template <int NB>
-__global__ __launch_bounds__(kMaxThreads) void k_o(Params P, int l) {
+__global__ __launch_bounds__(kMaxThreads, kStageWavesPerSimd) void k_o(Params P, int l) {
   extern __shared__ __align__(16) char smem[];
   stage_o<NB>(P, l, blockIdx.x, gridDim.x, smem);
 }
 
 template <int NB>
-__global__ __launch_bounds__(kMaxThreads) void k_gu(Params P, int l) {
+__global__ __launch_bounds__(kMaxThreads, kStageWavesPerSimd) void k_gu(Params P, int l) {
   extern __shared__ __align__(16) char smem[];
   stage_gu<NB>(P, l, blockIdx.x, gridDim.x, smem);
 }
 
 template <int NB>
-__global__ __launch_bounds__(kMaxThreads) void k_d(Params P, int l) {
+__global__ __launch_bounds__(kMaxThreads, kStageWavesPerSimd) void k_d(Params P, int l) {
   extern __shared__ __align__(16) char smem[];
   stage_d<NB>(P, l, blockIdx.x, gridDim.x, smem);
 }
 
 template <int NB>
-__global__ __launch_bounds__(kMaxThreads) void k_lm(Params P, int l) {
+__global__ __launch_bounds__(kMaxThreads, kStageWavesPerSimd) void k_lm(Params P, int l) {
   extern __shared__ __align__(16) char smem[];
   stage_lm<NB>(P, blockIdx.x, gridDim.x, smem);
 }
 
-// 512 threads: two waves per SIMD, so each wave may hold 256 VGPRs; the
-// union of every stage's live state does not fit in the 128 of a 1024-thread
-// workgroup without spilling to scratch memory.
-constexpr int kMegaThreads = 512;
-
 template <int NB>
-__global__ __launch_bounds__(kMegaThreads) void k_mega(Params P) {
+__global__ __launch_bounds__(kMaxThreads) void k_mega(Params P) {
   extern __shared__ __align__(16) char smem[];
   scratch_init(smem);
   const int wg = blockIdx.x, nwg = gridDim.x;

@@ -37,6 +37,10 @@ struct Dims {
 };
 
 // Weight arena: every layer block has the same layout.
+// Largest weight buffer one buffer resource covers (32-bit byte offsets,
+// with room above for the out-of-range offset of masked loads).
+constexpr size_t kMaxWeightBuffer = 0xFFFF0000u;
+
 struct Weights {
   const uint16_t* embed;       // [V, H]
   const uint16_t* lm;          // [V, H] (== embed when tied)

@@ -25,12 +25,13 @@
 
 namespace ld {
 
-// Per-stage tile shapes of the VALU engine: NR rows x UC chunks per block.
-constexpr int kNrQkv = 1, kUcQkv = 4;
-constexpr int kNrO = 1, kUcO = 4;
-constexpr int kPairsGu = 1, kUcGu = 4;  // one (gate, up) row pair per task
-constexpr int kNrD = 1, kUcD = 8, kKsD = 2;  // Down: K split over two waves
-constexpr int kNrLm = 2, kUcLm = 4;
+// Per-stage tile shapes of the VALU engine: NR rows x UC chunks per block,
+// PF blocks in flight per wave.
+constexpr int kNrQkv = 1, kUcQkv = 4, kPfQkv = 2;
+constexpr int kNrO = 1, kUcO = 4, kPfO = 2;
+constexpr int kPairsGu = 1, kUcGu = 4, kPfGu = 2;  // one (gate, up) row pair per task
+constexpr int kNrD = 1, kUcD = 8, kPfD = 2;
+constexpr int kNrLm = 2, kUcLm = 4, kPfLm = 2;
 
 __device__ __forceinline__ const uint16_t* layer_w(const Params& P, int l, int64_t off) {
   return P.W.layer0 + (int64_t)l * P.W.layer_stride + off;
@@ -111,9 +112,10 @@ __device__ void stage_qkv(const Params& P, int l, int wg, int nwg, char* smem) {
           st_coh(out + (int64_t)(b0 + b) * rows_total + row, acc[r][b] * sc.rs[b]);
       }
   };
-  gemv_stage<NR, UC, NB, 1>(rowfn, (rows_total + NR - 1) / NR, K, src,
-                         layer_w(P, l, P.W.o_attn_norm), true, D.eps, B, batch_tile(P, K, NB),
-                         wait, epi, wg, nwg, smem);
+  gemv_stage<NR, UC, NB, kPfQkv>(rowfn, (rows_total + NR - 1) / NR, K, Wm,
+                                 (uint32_t)((int64_t)rows_total * K * 2), src,
+                                 layer_w(P, l, P.W.o_attn_norm), true, D.eps, B,
+                                 batch_tile(P, K, NB), wait, epi, wg, nwg, smem);
   trace_ev(P, l, kSQkv, 2, wg);
   signal_if(P, stage_ctr(P, l, kCQkv), wg);
   trace_ev(P, l, kSQkv, 3, wg);
@@ -146,10 +148,8 @@ __host__ __device__ constexpr int attn_parts(int group, int d) {
   return 512 / (group * (d / 8)) < 1 ? 1 : 512 / (group * (d / 8)) > 16 ? 16 : 512 / (group * (d / 8));
 }
 __host__ __device__ constexpr size_t attn_tiles_bytes(int group, int d, int T, int max_splits) {
-  // K and V tiles [T][d] bf16, or the combining workgroup's split statistics
-  return (size_t)2 * T * d * 2 > (size_t)(2 * group * max_splits + group) * 4
-             ? (size_t)2 * T * d * 2
-             : (size_t)(2 * group * max_splits + group) * 4;
+  // K and V tiles [T][d] bf16
+  return (void)group, (void)max_splits, (size_t)2 * T * d * 2;
 }
 __host__ __device__ constexpr size_t attn_smem_bytes(int group, int d, int T, int max_splits) {
   return (size_t)group * d * 4                                     /* rotated q */
@@ -162,6 +162,8 @@ __host__ __device__ constexpr size_t attn_smem_bytes(int group, int d, int T, in
 struct AttnItem {
   int b, kvh, s, ns, p;
 };
+
+constexpr int kCombBatch = 16;  // splits combined from registers in one round of loads
 
 // Item `it` of the step (sequence-major, then kv head, then split).
 __device__ __forceinline__ bool attn_item_at(const Params& P, const Scratch& sc, int T, int it,
@@ -322,7 +324,7 @@ __device__ void attn_item(const Params& P, int l, const AttnItem& a, char* smem)
     const u32x4 kw = *reinterpret_cast<const u32x4*>(s.Ks + t * d + c8 * 8);
     const float kf[8] = {bf16lo(kw.x), bf16hi(kw.x), bf16lo(kw.y), bf16hi(kw.y),
                          bf16lo(kw.z), bf16hi(kw.z), bf16lo(kw.w), bf16hi(kw.w)};
-#pragma clang loop unroll(disable)
+#pragma unroll 4
     for (int g = 0; g < group; ++g) {
       const float4 qa = *reinterpret_cast<const float4*>(s.qs + g * d + c8 * 8);
       const float4 qb = *reinterpret_cast<const float4*>(s.qs + g * d + c8 * 8 + 4);
@@ -404,7 +406,7 @@ __device__ void attn_item(const Params& P, int l, const AttnItem& a, char* smem)
   for (int r = tid; r < gd; r += nth) {
     const int g = r >> ld, i = r & (d - 1);
     float o = 0.f;
-#pragma clang loop unroll(disable)
+#pragma unroll 4
     for (int sl = 0; sl < parts; ++sl) o += s.op[sl * gd + r];
     if (nsplit == 1) {
       st_coh(out + r, o / s.ml[2 * g + 1]);
@@ -432,48 +434,42 @@ __device__ void attn_item(const Params& P, int l, const AttnItem& a, char* smem)
     __syncthreads();
     trace_ev(P, l, 7, 3, blockIdx.x);
     if (!sc.flag[0]) return;
-    // split statistics of the group's heads -> LDS (over the tiles); then per
-    // head M = max m_s, f_s = e^(m_s - M), L = sum l_s f_s
-    float* ms = reinterpret_cast<float*>(s.Ks);  // [group][nsplit] max, then weight f_s
-    float* ls = ms + group * nsplit;             // [group][nsplit] sums
-    float* Lg = ls + group * nsplit;             // [group] combined sums
+    // per output channel: M = max_s m_s, f_s = e^(m_s - M), L = sum_s l_s f_s,
+    // o = (sum_s o_s f_s) / L, splits in ascending order.  Up to kCombBatch
+    // splits' (m, l, o) are loaded in one round and kept in registers.
     const float* pbase = P.K.part + ((int64_t)b * D.nq + kvh * group) * D.max_splits * (d + 2);
-    for (int i = tid; i < group * nsplit; i += nth) {
-      const int g = i / nsplit, sp = i - g * nsplit;
-      const float* q = pbase + ((int64_t)g * D.max_splits + sp) * (d + 2);
-      ms[i] = ld_coh(q);
-      ls[i] = ld_coh(q + 1);
-    }
-    __syncthreads();
-    for (int g = wave; g < group; g += nwaves()) {
-      float M = -INFINITY;
-      for (int sp = lane; sp < nsplit; sp += kWave) M = fmaxf(M, ms[g * nsplit + sp]);
-      M = wave_max(M);
-      float L = 0.f;
-      for (int sp = lane; sp < nsplit; sp += kWave) {
-        const float f = expf(ms[g * nsplit + sp] - M);
-        ms[g * nsplit + sp] = f;
-        L = fmaf(ls[g * nsplit + sp], f, L);
-      }
-      L = wave_sum(L);
-      if (lane == 0) Lg[g] = L;
-    }
-    __syncthreads();
-    // weighted sum of the split outputs, four coherent loads in flight per thread
     for (int r = tid; r < gd; r += nth) {
       const int g = r >> ld, i = r & (d - 1);
-      const float* q = pbase + (int64_t)g * D.max_splits * (d + 2) + 2 + i;
-      const float* f = ms + g * nsplit;
-      float O = 0.f;
-      for (int s0 = 0; s0 < nsplit; s0 += 4) {
-        float v[4];
+      const float* q = pbase + (int64_t)g * D.max_splits * (d + 2);
+      float mv[kCombBatch], lv[kCombBatch], ov[kCombBatch];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) v[u] = (s0 + u < nsplit) ? ld_coh(q + (s0 + u) * (d + 2)) : 0.f;
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          if (s0 + u < nsplit) O = fmaf(v[u], f[s0 + u], O);
+      for (int u = 0; u < kCombBatch; ++u) {
+        if (u < nsplit) {
+          mv[u] = ld_coh(q + u * (d + 2));
+          lv[u] = ld_coh(q + u * (d + 2) + 1);
+          ov[u] = ld_coh(q + u * (d + 2) + 2 + i);
+        }
       }
-      st_coh(out + r, O / Lg[g]);
+      float M = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < kCombBatch; ++u)
+        if (u < nsplit) M = fmaxf(M, mv[u]);
+      for (int s0 = kCombBatch; s0 < nsplit; ++s0) M = fmaxf(M, ld_coh(q + s0 * (d + 2)));
+      float L = 0.f, O = 0.f;
+#pragma unroll
+      for (int u = 0; u < kCombBatch; ++u) {
+        if (u < nsplit) {
+          const float f = expf(mv[u] - M);
+          L = fmaf(lv[u], f, L);
+          O = fmaf(ov[u], f, O);
+        }
+      }
+      for (int s0 = kCombBatch; s0 < nsplit; ++s0) {
+        const float f = expf(ld_coh(q + s0 * (d + 2)) - M);
+        L = fmaf(ld_coh(q + s0 * (d + 2) + 1), f, L);
+        O = fmaf(ld_coh(q + s0 * (d + 2) + 2 + i), f, O);
+      }
+      st_coh(out + r, O / L);
     }
   }
   signal_if(P, stage_ctr(P, l, kCAttn), b * D.nkv + kvh);
@@ -556,8 +552,9 @@ __device__ void stage_o(const Params& P, int l, int wg, int nwg, char* smem) {
         }
       }
   };
-  gemv_stage<NR, UC, NB, 1>(rowfn, (rows_total + NR - 1) / NR, K, src, nullptr, false, D.eps, B,
-                         batch_tile(P, K, NB), wait, epi, wg, nwg, smem);
+  gemv_stage<NR, UC, NB, kPfO>(rowfn, (rows_total + NR - 1) / NR, K, Wm,
+                               (uint32_t)((int64_t)rows_total * K * 2), src, nullptr, false, D.eps,
+                               B, batch_tile(P, K, NB), wait, epi, wg, nwg, smem);
   trace_ev(P, l, kSO, 2, wg);
   signal_if(P, stage_ctr(P, l, kCO), wg);
   trace_ev(P, l, kSO, 3, wg);
@@ -607,8 +604,11 @@ __device__ void stage_gu(const Params& P, int l, int wg, int nwg, char* smem) {
       }
   };
   const int bw = (P.S.gu_variant == kGuRow) ? min(2, batch_tile(P, K, NB)) : batch_tile(P, K, NB);
-  gemv_stage<NR, UC, NB, 1>(rowfn, (I + NP - 1) / NP, K, src, layer_w(P, l, P.W.o_mlp_norm), true,
-                         D.eps, B, bw, wait, epi, wg, nwg, smem);
+  // gate and up rows lie in one layer block: one buffer covers both
+  gemv_stage<NR, UC, NB, kPfGu>(rowfn, (I + NP - 1) / NP, K, layer_w(P, l, 0),
+                                (uint32_t)(P.W.layer_stride * 2), src,
+                                layer_w(P, l, P.W.o_mlp_norm), true, D.eps, B, bw, wait, epi, wg,
+                                nwg, smem);
   trace_ev(P, l, kSGu, 2, wg);
   signal_if(P, stage_ctr(P, l, kCGu), wg);
   trace_ev(P, l, kSGu, 3, wg);
@@ -650,8 +650,9 @@ __device__ void stage_d(const Params& P, int l, int wg, int nwg, char* smem) {
         }
       }
   };
-  gemv_stage<NR, UC, NB, kKsD>(rowfn, (rows_total + NR - 1) / NR, K, src, nullptr, false, D.eps, B,
-                         batch_tile(P, K, NB), wait, epi, wg, nwg, smem);
+  gemv_stage<NR, UC, NB, kPfD>(rowfn, (rows_total + NR - 1) / NR, K, Wm,
+                               (uint32_t)((int64_t)rows_total * K * 2), src, nullptr, false, D.eps,
+                               B, batch_tile(P, K, NB), wait, epi, wg, nwg, smem);
   trace_ev(P, l, kSD, 2, wg);
   signal_if(P, stage_ctr(P, l, kCD), wg);
   trace_ev(P, l, kSD, 3, wg);
@@ -722,8 +723,9 @@ __device__ void stage_lm(const Params& P, int wg, int nwg, char* smem) {
       }
     }
   };
-  gemv_stage<NR, UC, NB, 1>(rowfn, (rows_total + NR - 1) / NR, K, src, P.W.final_norm, true, D.eps,
-                         B, batch_tile(P, K, NB), wait, epi, wg, nwg, smem);
+  gemv_stage<NR, UC, NB, kPfLm>(rowfn, (rows_total + NR - 1) / NR, K, Wm,
+                                (uint32_t)((int64_t)rows_total * K * 2), src, P.W.final_norm, true,
+                                D.eps, B, batch_tile(P, K, NB), wait, epi, wg, nwg, smem);
   trace_ev(P, D.L, kSLm, 2, wg);
   __syncthreads();
   // this workgroup's best per sequence -> partials
