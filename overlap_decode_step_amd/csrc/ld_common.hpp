@@ -16,10 +16,23 @@ constexpr int kChunk = kWave * 8;          // bf16 elements covered by one 16-by
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// Threads per workgroup of every decode kernel.
+constexpr int kBlockThreads = 512;
+
+// The thread index through an empty volatile asm: values derived from it
+// cannot be hoisted out of the persistent kernel's layer loop, where they
+// would stay live (in registers) across every stage.  Its range is restated
+// so that tests against it still fold.
+__device__ __forceinline__ int tid() {
+  int v = (int)threadIdx.x;
+  asm volatile("" : "+v"(v));
+  __builtin_assume(v >= 0 && v < kBlockThreads);
+  return v;
+}
 __device__ __forceinline__ int nwaves() { return blockDim.x >> 6; }
 // the wave index is uniform: keep it (and what is derived from it) scalar
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
-__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+__device__ __forceinline__ int lane_id() { return tid() & (kWave - 1); }
 
 // ----------------------------------------------------------------- bf16
 
@@ -152,27 +165,47 @@ __device__ __forceinline__ void raise_error(int* err, int code) {
 __device__ __forceinline__ void wave_drain() { __builtin_amdgcn_s_waitcnt(0); }
 
 // Workgroup-wide wait until the leaves of `ctr` sum to >= target.  Every
-// thread calls it.
+// thread calls it.  Wave 0 polls with kPollDepth loads in flight and a short
+// sleep between polls.  (Deeper polling, or polling without the sleep, was
+// measured slower: the extra coherent loads on the counter lines delay the
+// stages' own memory traffic more than they shorten the hand-off.)
+constexpr int kPollDepth = 1;
+
+// One poll: one load per lane, unconditional (a load under a lane mask, or a
+// second load whose value is needed at once, would make the compiler wait for
+// every poll in flight).  Lanes 0..15 read the leaves, lane 16 the device
+// error word, the others a leaf again (ignored).
+__device__ __forceinline__ uint32_t poll_once(const uint32_t* ctr, const int* err, int lane) {
+  const uint32_t* a = lane == kLeaves ? reinterpret_cast<const uint32_t*>(err)
+                                      : ctr + (lane & (kLeaves - 1)) * kLeafStride;
+  return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ __forceinline__ void wg_wait(const SyncArgs& s, const uint32_t* ctr, uint32_t target,
                                         int stage) {
-  if (threadIdx.x < kWave) {
-    const int lane = threadIdx.x;
+  // wave_id() is scalar, so the poll loop is uniform control flow with one
+  // exit per round; that lets the compiler wait for the oldest poll only
+  if (wave_id() == 0) {
+    const int lane = lane_id();
     const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-    for (;;) {
-      uint32_t v = lane < kLeaves
-                       ? __hip_atomic_load(ctr + lane * kLeafStride, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT)
-                       : 0u;
-      v = wave_sum_u32(v);
-      if (reached(v, target)) break;
-      if ((__hip_atomic_load(s.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & 0xFF) ==
-          kErrTimeout)
-        break;  // another workgroup already timed out: let the grid drain
-      if (__builtin_amdgcn_s_memrealtime() - t0 > s.watchdog) {
-        if (lane == 0) raise_error(s.err, kErrTimeout | (stage << 8));
-        break;
+    uint32_t v[kPollDepth];
+#pragma unroll
+    for (int j = 0; j < kPollDepth; ++j) v[j] = poll_once(ctr, s.err, lane);
+    bool done = false;
+    while (!done) {
+#pragma unroll
+      for (int j = 0; j < kPollDepth; ++j) {
+        const uint32_t sum = wave_sum_u32(lane < kLeaves ? v[j] : 0u);
+        const int e = __builtin_amdgcn_readlane((int)v[j], kLeaves);
+        // reached, or another workgroup already timed out (let the grid drain)
+        done = done || reached(sum, target) || (e & 0xFF) == kErrTimeout;
+        v[j] = poll_once(ctr, s.err, lane);
+        __builtin_amdgcn_s_sleep(1);
       }
-      __builtin_amdgcn_s_sleep(1);
+      if (!done && __builtin_amdgcn_s_memrealtime() - t0 > s.watchdog) {
+        if (lane == 0) raise_error(s.err, kErrTimeout | (stage << 8));
+        done = true;
+      }
     }
   }
   __syncthreads();

@@ -66,7 +66,7 @@ struct Scratch {
 // Every decode kernel starts with this (the scratch area persists across
 // the stages of the persistent kernel).
 __device__ __forceinline__ void scratch_init(char* smem) {
-  if (threadIdx.x == 0) reinterpret_cast<Scratch*>(smem)->pos_ok = 0;
+  if (tid() == 0) reinterpret_cast<Scratch*>(smem)->pos_ok = 0;
   __syncthreads();
 }
 constexpr int kScratchBytes = (int)((sizeof(Scratch) + 255) / 256 * 256);
@@ -87,8 +87,8 @@ __device__ __forceinline__ void stage_x(const XSrc& src, int b0, int nb, int K,
 #pragma unroll
   for (int b = 0; b < NB; ++b) ss[b] = 0.f;
   const int n8 = K >> 3;
-  if (threadIdx.x < kRedThreads) {
-    for (int j = threadIdx.x; j < n8; j += kRedThreads) {
+  if (tid() < kRedThreads) {
+    for (int j = tid(); j < n8; j += kRedThreads) {
       float g[8];
       if (gain) {
         const u32x4 gw = *reinterpret_cast<const u32x4*>(gain + j * 8);
@@ -114,7 +114,7 @@ __device__ __forceinline__ void stage_x(const XSrc& src, int b0, int nb, int K,
     }
   }
   if (norm) {
-    if (threadIdx.x < kRedThreads) {
+    if (tid() < kRedThreads) {
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
         const float s = wave_sum(ss[b]);
@@ -122,10 +122,10 @@ __device__ __forceinline__ void stage_x(const XSrc& src, int b0, int nb, int K,
       }
     }
     __syncthreads();
-    if (threadIdx.x < nb) {
+    if (tid() < nb) {
       float s = 0.f;
-      for (int w = 0; w < kRedThreads / kWave; ++w) s += sc.red[w][threadIdx.x];
-      sc.rs[threadIdx.x] = 1.0f / sqrtf(s / (float)K + eps);
+      for (int w = 0; w < kRedThreads / kWave; ++w) s += sc.red[w][tid()];
+      sc.rs[tid()] = 1.0f / sqrtf(s / (float)K + eps);
     }
   }
   __syncthreads();
@@ -197,45 +197,38 @@ struct WBlock {
   }
 };
 
-// One GEMV stage for one workgroup.  Rows are split into tiles of NR rows
-// (RowFn(tile, rows) fills the row pointers, nullptr for a masked row; all
-// rows lie in the buffer [wbase, wbase + wbytes)), one tile per task, and
-// tasks are dealt to the waves of the whole grid round-robin.  Each wave
-// streams its tasks' weights as one sequence of blocks of UC chunks and keeps
-// PF blocks in flight (a ring of registers); the first PF are issued before
-// the stage waits for its input, except in wave 0, which polls the readiness
-// counter (loads return in order, so weight loads in flight would delay every
-// poll).  The batch is processed in tiles of at most `bw` rows that fit the
-// LDS staging area; each batch tile streams the weights again.
-// Epi(tile, b0, nb, acc, scratch) consumes the reduced sums (every lane of the
-// calling wave holds every sum).
-template <int NR, int UC, int NB, int PF, class RowFn, class WaitFn, class Epi>
-__device__ __forceinline__ void gemv_stage(const RowFn& rowfn, int ntile, int K,
-                                           const uint16_t* wbase, uint32_t wbytes, const XSrc& src,
-                                           const uint16_t* gain, bool norm, float eps, int B,
-                                           int bw, const WaitFn& wait, Epi& epi, int wg, int nwg,
-                                           char* smem) {
-  Scratch& sc = *reinterpret_cast<Scratch*>(smem);
-  float* xs = reinterpret_cast<float*>(smem + kScratchBytes);
-  const int lane = lane_id(), wave = wave_id();
-  const int nch = (K + kChunk - 1) / kChunk;
-  const int bpt = (nch + UC - 1) / UC;  // blocks per task
-  // Round q deals tiles [q * stride, (q + 1) * stride) to the grid's waves in
-  // order, so at any time the whole grid streams one contiguous window of the
-  // matrix (measured faster than giving each XCD its own contiguous range).
-  const int first = wg * nwaves() + wave, stride = nwg * nwaves();
-  auto task_of = [&](int q) { return first + q * stride; };
-  const int ntask = first < ntile ? (ntile - 1 - first) / stride + 1 : 0;
-  const int nblk = ntask * bpt;         // this wave's blocks
-  const int nbt = (B + bw - 1) / bw;
-  WBlock<NR, UC> ring[PF];
-  // block i of this wave: task i / bpt, chunks from (i % bpt) * UC; past the
-  // end every row is masked
-  auto issue = [&](WBlock<NR, UC>& blk, int i) {
+// One wave's weight stream in a GEMV stage.  Rows are split into tiles of NR
+// rows (RowFn(tile, rows) fills the row pointers, nullptr for a masked row;
+// all rows lie in the buffer [wbase, wbase + wbytes)), one tile per task.
+// Round q deals tiles [q * stride, (q + 1) * stride) to the grid's waves in
+// order, so at any time the whole grid streams one contiguous window of the
+// matrix (measured faster than giving each XCD its own contiguous range).
+// The wave's tasks are streamed as one sequence of blocks of UC chunks.
+template <int NR, int UC, class RowFn>
+struct WStream {
+  const RowFn& rowfn;
+  const uint16_t* wbase;
+  uint32_t wbytes;
+  int K, nch, bpt, first, stride, nblk;
+
+  __device__ __forceinline__ WStream(const RowFn& f, int ntile, int K_, const uint16_t* base,
+                                     uint32_t bytes, int wg, int nwg)
+      : rowfn(f), wbase(base), wbytes(bytes), K(K_) {
+    nch = (K + kChunk - 1) / kChunk;
+    bpt = (nch + UC - 1) / UC;  // blocks per task
+    first = wg * nwaves() + wave_id();
+    stride = nwg * nwaves();
+    const int ntask = first < ntile ? (ntile - 1 - first) / stride + 1 : 0;
+    nblk = ntask * bpt;
+  }
+  __device__ __forceinline__ int task(int q) const { return first + q * stride; }
+
+  // Block i of the stream into blk; past the end every row is masked.
+  __device__ __forceinline__ void issue(WBlock<NR, UC>& blk, int i, int lane) const {
     const int q = i / bpt;
     uint32_t roff[NR];
     const uint16_t* rows[NR];
-    rowfn(task_of(q), rows);
+    rowfn(task(q), rows);
 #pragma unroll
     for (int r = 0; r < NR; ++r)
       roff[r] = __builtin_amdgcn_readfirstlane(
@@ -243,18 +236,47 @@ __device__ __forceinline__ void gemv_stage(const RowFn& rowfn, int ntile, int K,
               ? (uint32_t)(reinterpret_cast<const char*>(rows[r]) - reinterpret_cast<const char*>(wbase))
               : kOob);
     blk.load(wbase, wbytes, roff, K, (i - q * bpt) * UC, lane);
-  };
-  if (wave != 0) {
-#pragma unroll
-    for (int j = 0; j < PF; ++j) issue(ring[j], j);
   }
+};
+
+// Issue the first PF blocks of a stream into a ring, except in wave 0, which
+// polls readiness counters (loads return in order, so weight loads in flight
+// would delay every poll).  Called before the stage's readiness wait, or
+// earlier: the persistent kernel issues the SwiGLU stage's first blocks while
+// attention runs.
+template <int NR, int UC, int PF, class RowFn>
+__device__ __forceinline__ void gemv_prefetch(const WStream<NR, UC, RowFn>& ws,
+                                              WBlock<NR, UC> (&ring)[PF]) {
+  if (wave_id() != 0) {
+#pragma unroll
+    for (int j = 0; j < PF; ++j) ws.issue(ring[j], j, lane_id());
+  }
+}
+
+// One GEMV stage for one workgroup: each wave streams its blocks keeping PF
+// in flight (the ring); unless `prefetched`, the first PF are issued here
+// before the stage waits for its input.  The batch is processed in tiles of
+// at most `bw` rows that fit the LDS staging area; each batch tile streams
+// the weights again.  Epi(tile, b0, nb, acc, scratch) consumes the reduced
+// sums (every lane of the calling wave holds every sum).
+template <int NR, int UC, int NB, int PF, class RowFn, class WaitFn, class Epi>
+__device__ __forceinline__ void gemv_run(const WStream<NR, UC, RowFn>& ws,
+                                         WBlock<NR, UC> (&ring)[PF], bool prefetched,
+                                         const XSrc& src, const uint16_t* gain, bool norm, float eps,
+                                         int B, int bw, const WaitFn& wait, Epi& epi, char* smem) {
+  Scratch& sc = *reinterpret_cast<Scratch*>(smem);
+  float* xs = reinterpret_cast<float*>(smem + kScratchBytes);
+  const int lane = lane_id(), wave = wave_id();
+  const int K = ws.K, nch = ws.nch, bpt = ws.bpt, nblk = ws.nblk;
+  const int nbt = (B + bw - 1) / bw;
+  if (!prefetched) gemv_prefetch(ws, ring);
   wait();
   for (int bt = 0; bt < nbt; ++bt) {
     const int b0 = bt * bw, nb = min(bw, B - b0);
     stage_x<NB>(src, b0, nb, K, gain, norm, eps, xs, sc);
     if (bt > 0 || wave == 0) {
 #pragma unroll
-      for (int j = 0; j < PF; ++j) issue(ring[j], j);
+      for (int j = 0; j < PF; ++j) ws.issue(ring[j], j, lane);
     }
     float acc[NR][NB];
 #pragma unroll
@@ -267,13 +289,13 @@ __device__ __forceinline__ void gemv_stage(const RowFn& rowfn, int ntile, int K,
         const int i = i0 + j;
         const int q = i / bpt, c = (i - q * bpt) * UC;
         if (i < nblk) ring[j].template fma<NB>(xs, K, nb, K, c, lane, acc);
-        issue(ring[j], i + PF);
+        ws.issue(ring[j], i + PF, lane);
         if (i < nblk && c + UC >= nch) {  // last block of task q
 #pragma unroll
           for (int r = 0; r < NR; ++r)
 #pragma unroll
             for (int b = 0; b < NB; ++b) acc[r][b] = wave_sum(acc[r][b]);
-          epi(task_of(q), b0, nb, acc, sc);
+          epi(ws.task(q), b0, nb, acc, sc);
 #pragma unroll
           for (int r = 0; r < NR; ++r)
 #pragma unroll
@@ -283,6 +305,18 @@ __device__ __forceinline__ void gemv_stage(const RowFn& rowfn, int ntile, int K,
     }
     if (bt + 1 < nbt) __syncthreads();  // every wave is done with xs before restaging
   }
+}
+
+// A whole GEMV stage with its own ring.
+template <int NR, int UC, int NB, int PF, class RowFn, class WaitFn, class Epi>
+__device__ __forceinline__ void gemv_stage(const RowFn& rowfn, int ntile, int K,
+                                           const uint16_t* wbase, uint32_t wbytes, const XSrc& src,
+                                           const uint16_t* gain, bool norm, float eps, int B,
+                                           int bw, const WaitFn& wait, Epi& epi, int wg, int nwg,
+                                           char* smem) {
+  const WStream<NR, UC, RowFn> ws(rowfn, ntile, K, wbase, wbytes, wg, nwg);
+  WBlock<NR, UC> ring[PF];
+  gemv_run<NR, UC, NB, PF>(ws, ring, false, src, gain, norm, eps, B, bw, wait, epi, smem);
 }
 
 }  // namespace ld

@@ -20,7 +20,7 @@ namespace ld {
 // may hold up to 256 VGPRs (the weight-block rings of the GEMV engine live in
 // registers); the stage kernels are held to 128 (four waves per SIMD) so that
 // two of them fit on a CU side by side in the tile-flag mode.
-constexpr int kMaxThreads = 512;
+constexpr int kMaxThreads = kBlockThreads;
 constexpr int kStageWavesPerSimd = 4;
 
 template <int NB>
@@ -32,7 +32,7 @@ __global__ __launch_bounds__(kMaxThreads, kStageWavesPerSimd) void k_qkv(Params 
 __global__ __launch_bounds__(kMaxThreads, kStageWavesPerSimd) void k_attn(Params P, int l) {
   extern __shared__ __align__(16) char smem[];
   scratch_init(smem);
-  stage_attn(P, l, blockIdx.x, gridDim.x, smem);
+  stage_attn(P, l, blockIdx.x, gridDim.x, smem, [] {});
 }
 
 template <int NB>
@@ -44,7 +44,8 @@ __global__ __launch_bounds__(kMaxThreads, kStageWavesPerSimd) void k_o(Params P,
 template <int NB>
 __global__ __launch_bounds__(kMaxThreads, kStageWavesPerSimd) void k_gu(Params P, int l) {
   extern __shared__ __align__(16) char smem[];
-  stage_gu<NB>(P, l, blockIdx.x, gridDim.x, smem);
+  GuBlock ring[kPfGu];
+  stage_gu<NB>(P, l, blockIdx.x, gridDim.x, smem, ring, false);
 }
 
 template <int NB>
@@ -67,10 +68,17 @@ __global__ __launch_bounds__(kMaxThreads) void k_mega(Params P) {
 #pragma clang loop unroll(disable)
   for (int l = 0; l < P.D.L; ++l) {
     stage_qkv<NB>(P, l, wg, nwg, smem);
-    stage_attn(P, l, wg, nwg, smem);
+    // workgroups without an attention item load their first SwiGLU weight
+    // blocks while attention runs
+    GuBlock gring[kPfGu];
+    bool gpre = false;
+    stage_attn(P, l, wg, nwg, smem, [&] {
+      gu_prefetch(P, l, wg, nwg, gring);
+      gpre = true;
+    });
     __syncthreads();
     stage_o<NB>(P, l, wg, nwg, smem);
-    stage_gu<NB>(P, l, wg, nwg, smem);
+    stage_gu<NB>(P, l, wg, nwg, smem, gring, gpre);
     stage_d<NB>(P, l, wg, nwg, smem);
   }
   stage_lm<NB>(P, wg, nwg, smem);

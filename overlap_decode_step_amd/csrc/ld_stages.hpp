@@ -70,7 +70,7 @@ __device__ __forceinline__ void signal_if(const Params& P, uint32_t* ctr, int wh
 // trace[((layer * 8 + stage) * 4 + ev) * kTraceWgs + wg].
 constexpr int kTraceWgs = 1024;
 __device__ __forceinline__ void trace_ev(const Params& P, int l, int stage, int ev, int wg) {
-  if (P.K.trace != nullptr && threadIdx.x == 0 && wg < kTraceWgs)
+  if (P.K.trace != nullptr && tid() == 0 && wg < kTraceWgs)
     P.K.trace[(((int64_t)l * 8 + stage) * 4 + ev) * kTraceWgs + wg] = __builtin_amdgcn_s_memrealtime();
 }
 
@@ -90,8 +90,8 @@ __device__ void stage_qkv(const Params& P, int l, int wg, int nwg, char* smem) {
       rows[r] = row < rows_total ? Wm + (int64_t)row * K : nullptr;
     }
   };
-  if (l == 0 && wg == 0 && threadIdx.x < B) {
-    const int t = P.S.tokens[threadIdx.x], p = P.S.pos[threadIdx.x];
+  if (l == 0 && wg == 0 && tid() < B) {
+    const int t = P.S.tokens[tid()], p = P.S.pos[tid()];
     if ((unsigned)t >= (unsigned)D.V) raise_error(P.K.err, kErrToken);
     if ((unsigned)p >= (unsigned)D.max_seq) raise_error(P.K.err, kErrPos);
   }
@@ -258,7 +258,7 @@ __device__ void attn_item(const Params& P, int l, const AttnItem& a, char* smem)
   const Dims& D = P.D;
   const int d = D.d, half = d / 2, group = D.group, w8 = d / 8, T = D.split_len;
   const int ld = 31 - __builtin_clz(d), lw8 = ld - 3;
-  const int tid = threadIdx.x, nth = blockDim.x, lane = lane_id(), wave = wave_id();
+  const int tid = ld::tid(), nth = blockDim.x, lane = lane_id(), wave = wave_id();
   Scratch& sc = *reinterpret_cast<Scratch*>(smem);
   const AttnLds s = attn_lds(D, smem);
   const int b = a.b, kvh = a.kvh, p = a.p, nsplit = a.ns;
@@ -475,14 +475,19 @@ __device__ void attn_item(const Params& P, int l, const AttnItem& a, char* smem)
   signal_if(P, stage_ctr(P, l, kCAttn), b * D.nkv + kvh);
 }
 
-__device__ void stage_attn(const Params& P, int l, int wg, int nwg, char* smem) {
+// `idle_hook()` runs in a workgroup that has no attention item, once the
+// stage's input is ready (the persistent kernel issues the SwiGLU stage's
+// first weight loads there, while the memory system is otherwise quiet).
+template <class Hook>
+__device__ void stage_attn(const Params& P, int l, int wg, int nwg, char* smem,
+                           const Hook& idle_hook) {
   const Dims& D = P.D;
   trace_ev(P, l, kSAttn, 0, wg);
   Scratch& sc = *reinterpret_cast<Scratch*>(smem);
   if (!sc.pos_ok) {  // positions of the step, read once per kernel
-    if (threadIdx.x < P.S.B) sc.pos[threadIdx.x] = clamp_pos(P, threadIdx.x);
+    if (tid() < P.S.B) sc.pos[tid()] = clamp_pos(P, tid());
     __syncthreads();
-    if (threadIdx.x == 0) sc.pos_ok = 1;
+    if (tid() == 0) sc.pos_ok = 1;
   }
   const int T = P.S.T;
   AttnItem a;
@@ -492,6 +497,7 @@ __device__ void stage_attn(const Params& P, int l, int wg, int nwg, char* smem) 
   if (any) attn_copy_tiles(P, l, a, smem, !P.S.wait);
   if (!P.S.wait) wg_wait(sync_of(P), stage_ctr(P, l, kCQkv), P.S.t_qkv + P.S.inject, kSAttn);
   trace_ev(P, l, kSAttn, 1, wg);
+  if (!any) idle_hook();
   if (any) {
     for (int it = wg;;) {
       attn_item(P, l, a, smem);
@@ -568,22 +574,49 @@ __device__ void stage_o(const Params& P, int l, int wg, int nwg, char* smem) {
 // batch is cut into tiles of at most two rows, each kept in LDS while every
 // weight tile streams past it.  At batch <= 2 both tilings issue the same
 // loads.
+// SwiGLU task t: gate rows and up rows t * kPairsGu .. + kPairsGu (gate and
+// up lie in one layer block, so one buffer covers both).
+struct GuRows {
+  const uint16_t* Wg;
+  const uint16_t* Wu;
+  int I, K;
+  __device__ __forceinline__ void operator()(int t, const uint16_t* (&rows)[2 * kPairsGu]) const {
+#pragma unroll
+    for (int r = 0; r < kPairsGu; ++r) {
+      const int row = t * kPairsGu + r;
+      rows[r] = row < I ? Wg + (int64_t)row * K : nullptr;
+      rows[kPairsGu + r] = row < I ? Wu + (int64_t)row * K : nullptr;
+    }
+  }
+};
+using GuBlock = WBlock<2 * kPairsGu, kUcGu>;
+using GuStream = WStream<2 * kPairsGu, kUcGu, GuRows>;
+
+__device__ __forceinline__ GuRows gu_rows(const Params& P, int l) {
+  return GuRows{layer_w(P, l, P.W.o_wg), layer_w(P, l, P.W.o_wu), P.D.I, P.D.H};
+}
+__device__ __forceinline__ int gu_tiles(const Params& P) { return (P.D.I + kPairsGu - 1) / kPairsGu; }
+
+// Issue this wave's first SwiGLU weight blocks of layer l (the persistent
+// kernel calls it while attention runs).
+__device__ __forceinline__ void gu_prefetch(const Params& P, int l, int wg, int nwg,
+                                            GuBlock (&ring)[kPfGu]) {
+  const GuRows rows = gu_rows(P, l);
+  const GuStream ws(rows, gu_tiles(P), P.D.H, layer_w(P, l, 0), (uint32_t)(P.W.layer_stride * 2),
+                    wg, nwg);
+  gemv_prefetch(ws, ring);
+}
+
 template <int NB>
-__device__ void stage_gu(const Params& P, int l, int wg, int nwg, char* smem) {
-  constexpr int NP = kPairsGu, NR = 2 * kPairsGu, UC = kUcGu;
+__device__ void stage_gu(const Params& P, int l, int wg, int nwg, char* smem,
+                         GuBlock (&ring)[kPfGu], bool prefetched) {
+  constexpr int NP = kPairsGu, NR = 2 * kPairsGu;
   const Dims& D = P.D;
   const int lane = lane_id();
   const int I = D.I, K = D.H, B = P.S.B;
-  const uint16_t* Wg = layer_w(P, l, P.W.o_wg);
-  const uint16_t* Wu = layer_w(P, l, P.W.o_wu);
-  auto rowfn = [&](int t, const uint16_t* (&rows)[NR]) {
-#pragma unroll
-    for (int r = 0; r < NP; ++r) {
-      const int row = t * NP + r;
-      rows[r] = row < I ? Wg + (int64_t)row * K : nullptr;
-      rows[NP + r] = row < I ? Wu + (int64_t)row * K : nullptr;
-    }
-  };
+  const GuRows rows = gu_rows(P, l);
+  const GuStream ws(rows, gu_tiles(P), K, layer_w(P, l, 0), (uint32_t)(P.W.layer_stride * 2), wg,
+                    nwg);
   trace_ev(P, l, kSGu, 0, wg);
   auto wait = [&]() {
     if (!P.S.wait) wg_wait(sync_of(P), stage_ctr(P, l, kCO), P.S.t_o, kSGu);
@@ -604,11 +637,8 @@ __device__ void stage_gu(const Params& P, int l, int wg, int nwg, char* smem) {
       }
   };
   const int bw = (P.S.gu_variant == kGuRow) ? min(2, batch_tile(P, K, NB)) : batch_tile(P, K, NB);
-  // gate and up rows lie in one layer block: one buffer covers both
-  gemv_stage<NR, UC, NB, kPfGu>(rowfn, (I + NP - 1) / NP, K, layer_w(P, l, 0),
-                                (uint32_t)(P.W.layer_stride * 2), src,
-                                layer_w(P, l, P.W.o_mlp_norm), true, D.eps, B, bw, wait, epi, wg,
-                                nwg, smem);
+  gemv_run<NR, kUcGu, NB, kPfGu>(ws, ring, prefetched, src, layer_w(P, l, P.W.o_mlp_norm), true,
+                                 D.eps, B, bw, wait, epi, smem);
   trace_ev(P, l, kSGu, 2, wg);
   signal_if(P, stage_ctr(P, l, kCGu), wg);
   trace_ev(P, l, kSGu, 3, wg);
@@ -729,7 +759,7 @@ __device__ void stage_lm(const Params& P, int wg, int nwg, char* smem) {
   trace_ev(P, D.L, kSLm, 2, wg);
   __syncthreads();
   // this workgroup's best per sequence -> partials
-  for (int b = threadIdx.x; b < B; b += blockDim.x) {
+  for (int b = tid(); b < B; b += blockDim.x) {
     float bv = bs.v[0][b];
     int bi = bs.i[0][b];
     for (int w = 1; w < nwaves(); ++w)
@@ -742,7 +772,7 @@ __device__ void stage_lm(const Params& P, int wg, int nwg, char* smem) {
   }
   wave_drain();
   __syncthreads();
-  if (threadIdx.x == 0) sc.flag[1] = last_arriver(P.K.lm_ctr, wg, nwg);
+  if (tid() == 0) sc.flag[1] = last_arriver(P.K.lm_ctr, wg, nwg);
   __syncthreads();
   trace_ev(P, D.L, kSLm, 3, wg);
   if (!sc.flag[1] || P.S.next == nullptr) return;
@@ -750,7 +780,7 @@ __device__ void stage_lm(const Params& P, int wg, int nwg, char* smem) {
   for (int b = 0; b < B; ++b) {
     float bv = -INFINITY;
     int bi = 0x7FFFFFFF;
-    for (int w = threadIdx.x; w < nwg; w += blockDim.x) {
+    for (int w = tid(); w < nwg; w += blockDim.x) {
       const float v = ld_coh(P.K.lm_val + (int64_t)w * D.max_batch + b);
       const int i = ld_coh_i(P.K.lm_idx + (int64_t)w * D.max_batch + b);
       if (better(v, i, bv, bi)) {
@@ -772,7 +802,7 @@ __device__ void stage_lm(const Params& P, int wg, int nwg, char* smem) {
       bs.i[wave][0] = bi;
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
+    if (tid() == 0) {
       for (int w = 1; w < nwaves(); ++w)
         if (better(bs.v[w][0], bs.i[w][0], bv, bi)) {
           bv = bs.v[w][0];
