@@ -93,6 +93,59 @@ def cpu_baseline(shape, prefill, steps):
                       f"same shape and seeds; {wall:.1f} s wall, {cpu:.1f} s CPU (one thread)"}
 
 
+def batch_sweep(runs=4, steps=64, batches=(1, 4, 16, 64)):
+    """Short-context batch sweep of the Llama-1B shape: per-sequence KV length
+    drawn from U[256, 1024] (seeded), `steps` greedy steps, every mode; each
+    configuration timed `runs` times (median, min, max of tokens/s)."""
+    import statistics
+    import torch
+    from overlap_decode_step_amd import ld
+    from synth import workloads as W
+    shape = W.LLAMA_1B
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    m = ld.Model(shape, seed=W.SEED_WEIGHTS, w_std=0.02)
+    maxb = max(batches)
+    m.alloc_kv(maxb, 1024 + steps + 8)
+    stream = torch.cuda.current_stream()
+    table = {}
+    for B in batches:
+        prefill = W.kv_lengths(B, 256, 1024)
+        logits = torch.empty((B, shape["vocab"]), dtype=torch.float32, device=dev)
+        toks = torch.tensor(W.first_tokens(B, shape["vocab"]), dtype=torch.int32, device=dev)
+        pos_all = [torch.tensor([p + i for p in prefill], dtype=torch.int32, device=dev)
+                   for i in range(steps)]
+        row = {}
+        for mode in ("wait", "flags", "mega"):
+            m.set_mode(mode)
+            rates = []
+            fill = prefill + [0] * (maxb - B)  # one length per cache slot
+            for _ in range(runs):
+                m.fill_kv(W.SEED_KV, 1.0, fill)
+                tbuf = [toks.clone(), torch.empty_like(toks)]
+                for i in range(3):  # warm-up, then the cache is refilled
+                    m.step(tbuf[i & 1], pos_all[i], logits, tbuf[(i + 1) & 1])
+                m.fill_kv(W.SEED_KV, 1.0, fill)
+                tbuf = [toks.clone(), torch.empty_like(toks)]
+                torch.cuda.synchronize()
+                ev0 = torch.cuda.Event(enable_timing=True)
+                ev1 = torch.cuda.Event(enable_timing=True)
+                ev0.record(stream)
+                for i in range(steps):
+                    m.step(tbuf[i & 1], pos_all[i], logits, tbuf[(i + 1) & 1])
+                ev1.record(stream)
+                torch.cuda.synchronize()
+                if m.device_error() != 0:
+                    raise RuntimeError(f"device error at batch {B} mode {mode}")
+                rates.append(B * steps * 1000.0 / ev0.elapsed_time(ev1))
+            row[mode] = {"median": statistics.median(rates), "min": min(rates), "max": max(rates)}
+            print(f"# sweep batch={B} mode={mode} tok/s median={row[mode]['median']:.1f} "
+                  f"min={row[mode]['min']:.1f} max={row[mode]['max']:.1f}", file=sys.stderr, flush=True)
+        table[B] = row
+    m.free()
+    return table
+
+
 def copy_calibration():
     import torch
     n = 1 << 30
@@ -117,6 +170,8 @@ def main():
     ap.add_argument("--cpu-steps", type=int, default=4, help="oracle steps in the CPU baseline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 1 GiB buffer (counter calibration)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="also run the batch sweep (1, 4, 16, 64; KV ~U[256,1024]; every mode)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU only; --gpus must be 1", file=sys.stderr)
@@ -193,6 +248,7 @@ def main():
     if not args.no_cpu:
         cpu = cpu_baseline(shape, prefill, args.cpu_steps)
         print(f"# cpu_baseline {cpu}", file=sys.stderr, flush=True)
+    sweep = batch_sweep() if args.sweep else None
     kernel = {"mega": "k_mega (persistent, one launch per step)",
               "wait": "all stage kernels of one step", "flags": "all stage kernels of one step"}
     out = {
@@ -217,6 +273,8 @@ def main():
         "cpu_baseline": cpu,
         "modes_ms_per_step": results,
     }
+    if sweep is not None:
+        out["batch_sweep_tokens_per_s"] = sweep
     print(json.dumps(out), flush=True)
 
 

@@ -42,7 +42,7 @@ struct ld_model {
   int gu_variant[65];
   bool gu_tuned[65];
   // launch geometry per mode: grid, threads per workgroup, LDS bytes, LDS for staged inputs
-  int grid_wait = 0, grid_flags = 0, grid_mega[9] = {0};  // grid_mega indexed by nb
+  int grid_wait = 0, grid_flags = 0, grid_mega[65] = {0};  // grid_mega indexed by nb
   int thr_wait = 512, thr_flags = 512, thr_mega = 512;
   size_t smem_wait = 0, smem_flags = 0, smem_mega = 0;
   uint32_t xcap_wait = 0, xcap_flags = 0, xcap_mega = 0;
@@ -367,7 +367,7 @@ static ld_status compute_grids(ld_model* m) {
   const size_t scratch = scratch_bytes(), best = best_bytes();
   const size_t kmax = (size_t)std::max(std::max(D.H, D.I), D.qd) * 4;  // longest staged input row
   // whole-kernel wait and persistent modes: one 512-thread workgroup per CU
-  const uint32_t xcap_full = 128 * 1024;
+  const uint32_t xcap_full = (uint32_t)((kLdsPerCu - scratch - best) / 256 * 256);
   if (kmax > xcap_full) return fail(m, LD_EINVAL, "input rows longer than the LDS staging area");
   m->xcap_wait = m->xcap_mega = xcap_full;
   const size_t attn_full = attn_smem(D.group, D.d, D.split_len, D.max_splits);

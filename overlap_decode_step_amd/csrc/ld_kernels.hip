@@ -69,12 +69,14 @@ __global__ __launch_bounds__(kMaxThreads) void k_mega(Params P) {
   for (int l = 0; l < P.D.L; ++l) {
     stage_qkv<NB>(P, l, wg, nwg, smem);
     // workgroups without an attention item load their first SwiGLU weight
-    // blocks while attention runs
+    // blocks while attention runs (VALU engine)
     GuBlock gring[kPfGu];
     bool gpre = false;
     stage_attn(P, l, wg, nwg, smem, [&] {
-      gu_prefetch(P, l, wg, nwg, gring);
-      gpre = true;
+      if constexpr (NB < kMfmaMinBatch) {
+        gu_prefetch(P, l, wg, nwg, gring);
+        gpre = true;
+      }
     });
     __syncthreads();
     stage_o<NB>(P, l, wg, nwg, smem);
@@ -134,11 +136,19 @@ static const void* kernel_ptr(int stage, int nb) {
     case 1: return stage_fn<1>(stage);
     case 2: return stage_fn<2>(stage);
     case 4: return stage_fn<4>(stage);
-    default: return stage_fn<8>(stage);
+    case 8: return stage_fn<8>(stage);
+    case 16: return stage_fn<16>(stage);
+    case 32: return stage_fn<32>(stage);
+    default: return stage_fn<64>(stage);
   }
 }
 
-int nb_for_batch(int B) { return B <= 1 ? 1 : B <= 2 ? 2 : B <= 4 ? 4 : 8; }
+// Kernel variant per batch size: the VALU engine holds up to 8 batch rows per
+// pass (batches 9..15 take two passes); from 16 on the MFMA engine takes the
+// batch in 16-row tiles.
+int nb_for_batch(int B) {
+  return B <= 1 ? 1 : B <= 2 ? 2 : B <= 4 ? 4 : B < kMfmaMinBatch ? 8 : B <= 16 ? 16 : B <= 32 ? 32 : 64;
+}
 
 hipError_t launch_stage(int stage, const Params& P, int l, int grid, int threads, size_t smem,
                         hipStream_t s) {

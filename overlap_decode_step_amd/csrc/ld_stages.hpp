@@ -21,6 +21,7 @@
 
 #include "ld_common.hpp"
 #include "ld_gemv.hpp"
+#include "ld_mfma.hpp"
 #include "ld_params.hpp"
 
 namespace ld {
@@ -77,7 +78,7 @@ __device__ __forceinline__ void trace_ev(const Params& P, int l, int stage, int 
 // ----------------------------------------------------------------- QKV
 
 template <int NB>
-__device__ void stage_qkv(const Params& P, int l, int wg, int nwg, char* smem) {
+__device__ __forceinline__ void stage_qkv(const Params& P, int l, int wg, int nwg, char* smem) {
   constexpr int NR = kNrQkv, UC = kUcQkv;
   const Dims& D = P.D;
   const int lane = lane_id();
@@ -112,10 +113,21 @@ __device__ void stage_qkv(const Params& P, int l, int wg, int nwg, char* smem) {
           st_coh(out + (int64_t)(b0 + b) * rows_total + row, acc[r][b] * sc.rs[b]);
       }
   };
-  gemv_stage<NR, UC, NB, kPfQkv>(rowfn, (rows_total + NR - 1) / NR, K, Wm,
-                                 (uint32_t)((int64_t)rows_total * K * 2), src,
-                                 layer_w(P, l, P.W.o_attn_norm), true, D.eps, B,
-                                 batch_tile(P, K, NB), wait, epi, wg, nwg, smem);
+  const uint32_t wbytes = (uint32_t)((int64_t)rows_total * K * 2);
+  if constexpr (NB >= kMfmaMinBatch) {
+    Scratch& sc = *reinterpret_cast<Scratch*>(smem);
+    auto epe = [&](int tile, int r, int b, int bl, int, const float* v) {
+      const int row = tile * 16 + r;
+      if (row < rows_total) st_coh(out + (int64_t)b * rows_total + row, v[0] * sc.rs[bl]);
+    };
+    mfma_stage<kMfmaNbt<NB>, 1>(MatRows{Wm, {Wm, Wm}, rows_total, K}, (rows_total + 15) / 16, K, Wm,
+                           wbytes, src, layer_w(P, l, P.W.o_attn_norm), true, D.eps, B, P.S.x_cap,
+                           wait, epe, [](int, int) {}, wg, nwg, smem);
+  } else {
+    gemv_stage<NR, UC, NB, kPfQkv>(rowfn, (rows_total + NR - 1) / NR, K, Wm, wbytes, src,
+                                   layer_w(P, l, P.W.o_attn_norm), true, D.eps, B,
+                                   batch_tile(P, K, NB), wait, epi, wg, nwg, smem);
+  }
   trace_ev(P, l, kSQkv, 2, wg);
   signal_if(P, stage_ctr(P, l, kCQkv), wg);
   trace_ev(P, l, kSQkv, 3, wg);
@@ -216,7 +228,7 @@ __device__ __forceinline__ int64_t attn_cache_off(const Params& P, int l, int b,
 // Copy the item's cached K and V rows into the LDS tiles (1 KB per wave
 // instruction, direct to LDS).  With skip_wave0 the polling wave issues none,
 // so its spin loads never wait behind these copies.
-__device__ void attn_copy_tiles(const Params& P, int l, const AttnItem& a, char* smem,
+__device__ __forceinline__ void attn_copy_tiles(const Params& P, int l, const AttnItem& a, char* smem,
                                 bool skip_wave0) {
   const Dims& D = P.D;
   const AttnLds s = attn_lds(D, smem);
@@ -253,7 +265,7 @@ __device__ __forceinline__ float lane_group_sum(float v, int w) {
   return v;
 }
 
-__device__ void attn_item(const Params& P, int l, const AttnItem& a, char* smem) {
+__device__ __forceinline__ void attn_item(const Params& P, int l, const AttnItem& a, char* smem) {
   // head_dim is a power of two (checked on the host): index math uses shifts
   const Dims& D = P.D;
   const int d = D.d, half = d / 2, group = D.group, w8 = d / 8, T = D.split_len;
@@ -479,7 +491,7 @@ __device__ void attn_item(const Params& P, int l, const AttnItem& a, char* smem)
 // stage's input is ready (the persistent kernel issues the SwiGLU stage's
 // first weight loads there, while the memory system is otherwise quiet).
 template <class Hook>
-__device__ void stage_attn(const Params& P, int l, int wg, int nwg, char* smem,
+__device__ __forceinline__ void stage_attn(const Params& P, int l, int wg, int nwg, char* smem,
                            const Hook& idle_hook) {
   const Dims& D = P.D;
   trace_ev(P, l, kSAttn, 0, wg);
@@ -514,7 +526,7 @@ __device__ void stage_attn(const Params& P, int l, int wg, int nwg, char* smem,
 // ----------------------------------------------------------- O-proj
 
 template <int NB>
-__device__ void stage_o(const Params& P, int l, int wg, int nwg, char* smem) {
+__device__ __forceinline__ void stage_o(const Params& P, int l, int wg, int nwg, char* smem) {
   constexpr int NR = kNrO, UC = kUcO;
   const Dims& D = P.D;
   const int lane = lane_id();
@@ -558,9 +570,28 @@ __device__ void stage_o(const Params& P, int l, int wg, int nwg, char* smem) {
         }
       }
   };
-  gemv_stage<NR, UC, NB, kPfO>(rowfn, (rows_total + NR - 1) / NR, K, Wm,
-                               (uint32_t)((int64_t)rows_total * K * 2), src, nullptr, false, D.eps,
-                               B, batch_tile(P, K, NB), wait, epi, wg, nwg, smem);
+  const uint32_t wbytes = (uint32_t)((int64_t)rows_total * K * 2);
+  if constexpr (NB >= kMfmaMinBatch) {
+    auto epe = [&](int tile, int r, int b, int, int, const float* v) {
+      const int row = tile * 16 + r;
+      if (row >= rows_total) return;
+      float res;
+      if (l == 0) {
+        int tk = tok[b];
+        tk = ((unsigned)tk < (unsigned)D.V) ? tk : 0;
+        res = bf16f(emb[(int64_t)tk * D.H + row]);
+      } else {
+        res = ld_coh(xa + (int64_t)b * D.H + row);
+      }
+      st_coh(xb + (int64_t)b * D.H + row, res + v[0]);
+    };
+    mfma_stage<kMfmaNbt<NB>, 1>(MatRows{Wm, {Wm, Wm}, rows_total, K}, (rows_total + 15) / 16, K, Wm,
+                           wbytes, src, nullptr, false, D.eps, B, P.S.x_cap, wait, epe,
+                           [](int, int) {}, wg, nwg, smem);
+  } else {
+    gemv_stage<NR, UC, NB, kPfO>(rowfn, (rows_total + NR - 1) / NR, K, Wm, wbytes, src, nullptr,
+                                 false, D.eps, B, batch_tile(P, K, NB), wait, epi, wg, nwg, smem);
+  }
   trace_ev(P, l, kSO, 2, wg);
   signal_if(P, stage_ctr(P, l, kCO), wg);
   trace_ev(P, l, kSO, 3, wg);
@@ -608,7 +639,7 @@ __device__ __forceinline__ void gu_prefetch(const Params& P, int l, int wg, int 
 }
 
 template <int NB>
-__device__ void stage_gu(const Params& P, int l, int wg, int nwg, char* smem,
+__device__ __forceinline__ void stage_gu(const Params& P, int l, int wg, int nwg, char* smem,
                          GuBlock (&ring)[kPfGu], bool prefetched) {
   constexpr int NP = kPairsGu, NR = 2 * kPairsGu;
   const Dims& D = P.D;
@@ -637,8 +668,25 @@ __device__ void stage_gu(const Params& P, int l, int wg, int nwg, char* smem,
       }
   };
   const int bw = (P.S.gu_variant == kGuRow) ? min(2, batch_tile(P, K, NB)) : batch_tile(P, K, NB);
-  gemv_run<NR, kUcGu, NB, kPfGu>(ws, ring, prefetched, src, layer_w(P, l, P.W.o_mlp_norm), true,
-                                 D.eps, B, bw, wait, epi, smem);
+  if constexpr (NB >= kMfmaMinBatch) {
+    (void)ring;
+    (void)prefetched;
+    (void)bw;
+    Scratch& sc = *reinterpret_cast<Scratch*>(smem);
+    auto epe = [&](int tile, int r, int b, int bl, int, const float* v) {
+      const int row = tile * 16 + r;
+      if (row >= I) return;
+      const float a = v[0] * sc.rs[bl], u = v[1] * sc.rs[bl];
+      st_coh(h + (int64_t)b * I + row, a / (1.0f + expf(-a)) * u);
+    };
+    mfma_stage<kMfmaNbt<NB>, 2>(MatRows{layer_w(P, l, 0), {rows.Wg, rows.Wu}, I, K}, (I + 15) / 16, K,
+                           layer_w(P, l, 0), (uint32_t)(P.W.layer_stride * 2), src,
+                           layer_w(P, l, P.W.o_mlp_norm), true, D.eps, B, P.S.x_cap, wait, epe,
+                           [](int, int) {}, wg, nwg, smem);
+  } else {
+    gemv_run<NR, kUcGu, NB, kPfGu>(ws, ring, prefetched, src, layer_w(P, l, P.W.o_mlp_norm), true,
+                                   D.eps, B, bw, wait, epi, smem);
+  }
   trace_ev(P, l, kSGu, 2, wg);
   signal_if(P, stage_ctr(P, l, kCGu), wg);
   trace_ev(P, l, kSGu, 3, wg);
@@ -647,7 +695,7 @@ __device__ void stage_gu(const Params& P, int l, int wg, int nwg, char* smem,
 // ---------------------------------------------------------- Down-proj
 
 template <int NB>
-__device__ void stage_d(const Params& P, int l, int wg, int nwg, char* smem) {
+__device__ __forceinline__ void stage_d(const Params& P, int l, int wg, int nwg, char* smem) {
   constexpr int NR = kNrD, UC = kUcD;
   const Dims& D = P.D;
   const int lane = lane_id();
@@ -680,9 +728,21 @@ __device__ void stage_d(const Params& P, int l, int wg, int nwg, char* smem) {
         }
       }
   };
-  gemv_stage<NR, UC, NB, kPfD>(rowfn, (rows_total + NR - 1) / NR, K, Wm,
-                               (uint32_t)((int64_t)rows_total * K * 2), src, nullptr, false, D.eps,
-                               B, batch_tile(P, K, NB), wait, epi, wg, nwg, smem);
+  const uint32_t wbytes = (uint32_t)((int64_t)rows_total * K * 2);
+  if constexpr (NB >= kMfmaMinBatch) {
+    auto epe = [&](int tile, int r, int b, int, int, const float* v) {
+      const int row = tile * 16 + r;
+      if (row >= rows_total) return;
+      const int64_t o = (int64_t)b * D.H + row;
+      st_coh(xa + o, ld_coh(xb + o) + v[0]);
+    };
+    mfma_stage<kMfmaNbt<NB>, 1>(MatRows{Wm, {Wm, Wm}, rows_total, K}, (rows_total + 15) / 16, K, Wm,
+                           wbytes, src, nullptr, false, D.eps, B, P.S.x_cap, wait, epe,
+                           [](int, int) {}, wg, nwg, smem);
+  } else {
+    gemv_stage<NR, UC, NB, kPfD>(rowfn, (rows_total + NR - 1) / NR, K, Wm, wbytes, src, nullptr,
+                                 false, D.eps, B, batch_tile(P, K, NB), wait, epi, wg, nwg, smem);
+  }
   trace_ev(P, l, kSD, 2, wg);
   signal_if(P, stage_ctr(P, l, kCD), wg);
   trace_ev(P, l, kSD, 3, wg);
@@ -702,7 +762,7 @@ struct Best {
 constexpr int kBestBytes = (int)sizeof(Best);
 
 template <int NB>
-__device__ void stage_lm(const Params& P, int wg, int nwg, char* smem) {
+__device__ __forceinline__ void stage_lm(const Params& P, int wg, int nwg, char* smem) {
   constexpr int NR = kNrLm, UC = kUcLm;
   const Dims& D = P.D;
   Scratch& sc = *reinterpret_cast<Scratch*>(smem);
@@ -753,9 +813,60 @@ __device__ void stage_lm(const Params& P, int wg, int nwg, char* smem) {
       }
     }
   };
-  gemv_stage<NR, UC, NB, kPfLm>(rowfn, (rows_total + NR - 1) / NR, K, Wm,
-                                (uint32_t)((int64_t)rows_total * K * 2), src, P.W.final_norm, true,
-                                D.eps, B, batch_tile(P, K, NB), wait, epi, wg, nwg, smem);
+  const uint32_t wbytes = (uint32_t)((int64_t)rows_total * K * 2);
+  if constexpr (NB >= kMfmaMinBatch) {
+    // logits, and each lane's running best per batch tile (the lane holds one
+    // batch row of each tile); merged into the wave's slots per batch pass
+    constexpr int NBT = kMfmaNbt<NB>;
+    float bv[NBT];
+    int bi[NBT];
+#pragma unroll
+    for (int bt = 0; bt < NBT; ++bt) {
+      bv[bt] = -INFINITY;
+      bi[bt] = 0x7FFFFFFF;
+    }
+    auto epe = [&](int tile, int r, int b, int bl, int bt, const float* v) {
+      const int row = tile * 16 + r;
+      if (row >= rows_total) return;
+      const float val = v[0] * sc.rs[bl];
+      logits[(int64_t)b * D.V + row] = val;
+      if (better(val, row, bv[bt], bi[bt])) {
+        bv[bt] = val;
+        bi[bt] = row;
+      }
+    };
+    auto pass_end = [&](int b0, int nb) {
+#pragma unroll
+      for (int bt = 0; bt < NBT; ++bt) {
+        float v = bv[bt];
+        int i = bi[bt];
+        // lanes l, l ^ 16, l ^ 32, l ^ 48 hold the same batch row
+#pragma unroll
+        for (int off = 16; off <= 32; off <<= 1) {
+          const float ov = __shfl_xor(v, off, kWave);
+          const int oi = __shfl_xor(i, off, kWave);
+          if (better(ov, oi, v, i)) {
+            v = ov;
+            i = oi;
+          }
+        }
+        const int bl = bt * 16 + lane;
+        if (lane < 16 && bl < nb) {
+          bs.v[wave][b0 + bl] = v;
+          bs.i[wave][b0 + bl] = i;
+        }
+        bv[bt] = -INFINITY;
+        bi[bt] = 0x7FFFFFFF;
+      }
+    };
+    mfma_stage<NBT, 1>(MatRows{Wm, {Wm, Wm}, rows_total, K}, (rows_total + 15) / 16, K, Wm, wbytes,
+                       src, P.W.final_norm, true, D.eps, B, P.S.x_cap, wait, epe, pass_end, wg,
+                       nwg, smem);
+  } else {
+    gemv_stage<NR, UC, NB, kPfLm>(rowfn, (rows_total + NR - 1) / NR, K, Wm, wbytes, src,
+                                  P.W.final_norm, true, D.eps, B, batch_tile(P, K, NB), wait, epi,
+                                  wg, nwg, smem);
+  }
   trace_ev(P, D.L, kSLm, 2, wg);
   __syncthreads();
   // this workgroup's best per sequence -> partials
