@@ -96,6 +96,18 @@ __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
+// Sum over aligned groups of w lanes (w = 1..32, a power of two).  DPP row
+// rotations move data to higher lanes, so the total is valid in the last
+// lane of each group.
+__device__ __forceinline__ float lane_group_sum(float v, int w) {
+  if (w > 1) v += dpp_f<0xB1, 0xF>(0.f, v);     // + lane ^ 1
+  if (w > 2) v += dpp_f<0x4E, 0xF>(0.f, v);     // + lane ^ 2
+  if (w > 4) v += dpp_f<0x124, 0xF>(0.f, v);    // row_ror:4 (lane 7 of 8 gets lanes 0..3)
+  if (w > 8) v += dpp_f<0x128, 0xF>(0.f, v);    // row_ror:8 (lane 15 of 16 gets lanes 0..7)
+  if (w > 16) v += __shfl_up(v, 16, kWave);     // lane 31 of 32 gets lanes 0..15
+  return v;
+}
+
 // ------------------------------------------- coherent (agent-scope) access
 //
 // Activations, partial results and counters pass between workgroups that may

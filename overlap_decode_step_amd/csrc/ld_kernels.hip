@@ -67,7 +67,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_mega(Params P) {
   const int wg = blockIdx.x, nwg = gridDim.x;
 #pragma clang loop unroll(disable)
   for (int l = 0; l < P.D.L; ++l) {
-    stage_qkv<NB>(P, l, wg, nwg, smem);
+    stage_qkv<NB, kMfmaRingBig>(P, l, wg, nwg, smem);
     // workgroups without an attention item load their first SwiGLU weight
     // blocks while attention runs (VALU engine)
     GuBlock gring[kPfGu];
@@ -79,11 +79,11 @@ __global__ __launch_bounds__(kMaxThreads) void k_mega(Params P) {
       }
     });
     __syncthreads();
-    stage_o<NB>(P, l, wg, nwg, smem);
-    stage_gu<NB>(P, l, wg, nwg, smem, gring, gpre);
-    stage_d<NB>(P, l, wg, nwg, smem);
+    stage_o<NB, kMfmaRingBig>(P, l, wg, nwg, smem);
+    stage_gu<NB, kMfmaRingBig>(P, l, wg, nwg, smem, gring, gpre);
+    stage_d<NB, kMfmaRingBig>(P, l, wg, nwg, smem);
   }
-  stage_lm<NB>(P, wg, nwg, smem);
+  stage_lm<NB, kMfmaRingBig>(P, wg, nwg, smem);
 }
 
 // ---------------------------------------------------------- generators

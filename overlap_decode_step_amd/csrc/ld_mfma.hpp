@@ -29,12 +29,16 @@ namespace ld {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kMfmaMinBatch = 16;  // batches from here on take this engine
 constexpr int kMfmaTileMats = 2;   // 16-row tiles x matrices a wave accumulates at once
-constexpr int kMfmaRing = 4;       // K steps of weight fragments in flight per wave
-constexpr int kMfmaPad = 8;        // bf16 elements of padding per staged row
+// K steps of weight fragments in flight per wave: the persistent kernel has
+// 256 VGPRs per wave, the stage kernels 128
+constexpr int kMfmaRingBig = 8, kMfmaRingSmall = 4;
+constexpr int kMfmaPad = 4;        // 4-byte elements of padding per staged row (16 bytes)
 constexpr int kMfmaMinChunk = 512; // smallest K chunk (a wave's 64 lanes stage one row)
+constexpr int kSc1 = 16;           // cache policy: agent-coherent (sc1)
 
 // Batch tiles of 16 a wave accumulates at once for a kernel built for NB
 // batch rows: at most 2 (32 rows) within 128 VGPRs; larger batches take
@@ -63,7 +67,6 @@ __host__ __device__ constexpr int mfma_chunk(int rows, int K, uint32_t cap) {
              : (K + kMfmaMinChunk - 1) / kMfmaMinChunk * kMfmaMinChunk;
 }
 
-__device__ __forceinline__ uint16_t bf16_rn(float f) { return f2bf(f); }
 
 // Rows of NT weight matrices in one buffer: tile t, matrix j, row r (0..15).
 struct MatRows {
@@ -82,11 +85,12 @@ struct MatRows {
 // It is called only for b < B, by the lanes that hold the values; rows past
 // the matrix end are the callee's to skip.  PassEnd(b0, nb) runs (in every
 // thread) after each batch pass.
-template <int NBT, int NT, class WaitFn, class Epe, class PassEnd>
+template <int NBT, int NT, int RING, class WaitFn, class Epe, class PassEnd>
 __device__ __forceinline__ void mfma_stage(const MatRows& mr, int ntile, int K, const uint16_t* wbase,
-                           uint32_t wbytes, const XSrc& src, const uint16_t* gain, bool norm,
-                           float eps, int B, uint32_t x_cap, const WaitFn& wait, Epe& epe,
-                           const PassEnd& pass_end, int wg, int nwg, char* smem) {
+                                           uint32_t wbytes, const XSrc& src, const uint16_t* gain,
+                                           bool norm, float eps, int B, uint32_t x_cap,
+                                           const WaitFn& wait, Epe& epe, const PassEnd& pass_end,
+                                           int wg, int nwg, char* smem) {
   constexpr int MT = kMfmaTileMats / NT;  // tiles per wave per tile pass
   Scratch& sc = *reinterpret_cast<Scratch*>(smem);
   char* xbase = smem + kScratchBytes;
@@ -98,25 +102,139 @@ __device__ __forceinline__ void mfma_stage(const MatRows& mr, int ntile, int K, 
   const int WK = nw / WR, wr = wave % WR, wk = wave / WR;
   const int cnt = wg < ntile ? (ntile - 1 - wg) / nwg + 1 : 0;     // this workgroup's tiles
   const int mt = cnt > wr ? (cnt - 1 - wr) / WR + 1 : 0;            // this wave's tiles
-  const int ntpass = ((tpw + WR - 1) / WR + MT - 1) / MT;  // tile passes
-  const int prow = min(mfma_pass_rows(B, x_cap), NBT * 16);        // batch rows per pass
+  const int ntpass = ((tpw + WR - 1) / WR + MT - 1) / MT;            // tile passes
+  const int prow = min(mfma_pass_rows(B, x_cap), NBT * 16);         // batch rows per pass
   const int nbpass = (B + prow - 1) / prow;
-  const int KC = mfma_chunk(prow, K, x_cap), ldx = KC + kMfmaPad;
+  const int KC = mfma_chunk(prow, K, x_cap), ldx = KC + kMfmaPad;  // row stride (4-byte words)
   const int nchunk = (K + KC - 1) / KC;
-  uint16_t* xh = reinterpret_cast<uint16_t*>(xbase);
-  uint16_t* xl = xh + (size_t)prow * ldx;
+  const int cs = KC / 32;                 // 32-wide K steps per chunk
+  const int spc = (cs + WK - 1) / WK;     // this wave's step slots per chunk (wave wk takes
+                                          // steps wk, wk + WK, ...)
+  const int nslot = nchunk * spc;
+  // staged rows [prow][ldx] of 4-byte words: the fp32 inputs as copied, then
+  // each word rewritten in place as the pair (bf16 hi | bf16 lo << 16)
+  uint32_t* xw = reinterpret_cast<uint32_t*>(xbase);
+  float* ssw = reinterpret_cast<float*>(xbase + (size_t)prow * ldx * 4);  // [prow] row sums
   float* red = reinterpret_cast<float*>(xbase);  // WK partial tiles (after the K loop)
+  const __amdgpu_buffer_rsrc_t rs = weight_rsrc(wbase, wbytes);
 
+  uint32_t roff[MT][NT];
+  auto set_tiles = [&](int m0) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+        roff[m][j] = (m0 + m < mt) ? mr(wg + (wr + (m0 + m) * WR) * nwg, j, lane & 15) : kOob;
+  };
+  // weight fragments of slot i (chunk i / spc, step wk + WK * (i % spc));
+  // past the end, or past K, the loads are masked
+  auto issue = [&](u32x4 (&f)[MT][NT], int i) {
+    const int c = i / spc, st = wk + (i - c * spc) * WK;
+    const int k = c * KC + st * 32 + (lane >> 4) * 8;
+    const bool ok = i < nslot && st < cs;
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        const uint32_t off = (ok && roff[m][j] != kOob && k < K) ? roff[m][j] + 2u * k : kOob;
+        f[m][j] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kNt);
+      }
+  };
+  float ssacc = 0.f;  // thread t < nb: row b0 + t's running sum of squares
+  // ---- stage rows [b0, b0 + prow) x columns [kc0, kc0 + KC) of chunk c
+  auto stage_chunk = [&](int b0, int nb, int c, bool sums) {
+    const int kc0 = c * KC;
+    __syncthreads();  // the previous chunk's pairs and partial sums are consumed
+    const int gpr = KC / 8;  // 8-column groups per row (a multiple of 64)
+    const int ngroup = prow * gpr;
+    if (src.x != nullptr) {
+      // fp32 activations: direct-to-LDS copies of 1 KB per wave instruction,
+      // all issued before any wait (agent-coherent: other workgroups wrote
+      // them during this step)
+      const int kn = min(KC, K - kc0), pieces = (kn + 255) / 256;
+      for (int i = wave; i < nb * pieces; i += nw) {
+        const int b = i / pieces, pc = i - b * pieces;
+        const int k = pc * 256 + lane * 4;
+        char* dst = reinterpret_cast<char*>(xw + (size_t)b * ldx + pc * 256);
+        if (k < kn)
+          __builtin_amdgcn_global_load_lds(src.x + (int64_t)(b0 + b) * src.ldx + kc0 + k,
+                                           (__attribute__((address_space(3))) void*)dst, 16, 0,
+                                           kSc1);
+      }
+      wave_drain();
+      __syncthreads();
+    }
+    // thread (row b, j) of the tpr threads per row takes the row's 8-column
+    // groups j, j + tpr, ...: inputs (from the copy, or the bf16 embedding
+    // rows of the first layer) -> norm partial sum, gain, and each element
+    // rewritten as the pair (bf16 hi, bf16 lo) by the hardware conversion
+    // (round to nearest even); rows past the batch and columns past K become
+    // zeros
+    const int tpr = nth / prow, b = t / tpr, j = t - b * tpr;
+    float s2 = 0.f;
+    for (int kk = j * 8; kk < KC; kk += tpr * 8) {
+      const int k = kc0 + kk;
+      uint32_t* w = xw + (size_t)b * ldx + kk;
+      float v[8];
+      if (b < nb && k < K) {
+        if (src.x != nullptr) {
+          const u32x4 p0 = *reinterpret_cast<const u32x4*>(w);
+          const u32x4 p1 = *reinterpret_cast<const u32x4*>(w + 4);
+          v[0] = __uint_as_float(p0.x); v[1] = __uint_as_float(p0.y);
+          v[2] = __uint_as_float(p0.z); v[3] = __uint_as_float(p0.w);
+          v[4] = __uint_as_float(p1.x); v[5] = __uint_as_float(p1.y);
+          v[6] = __uint_as_float(p1.z); v[7] = __uint_as_float(p1.w);
+        } else {
+          src.raw8(b0 + b, k, v);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = 0.f;
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s2 = fmaf(v[i], v[i], s2);
+      if (gain && k < K) {
+        const u32x4 gw = *reinterpret_cast<const u32x4*>(gain + k);
+        v[0] *= bf16lo(gw.x); v[1] *= bf16hi(gw.x); v[2] *= bf16lo(gw.y); v[3] *= bf16hi(gw.y);
+        v[4] *= bf16lo(gw.z); v[5] *= bf16hi(gw.z); v[6] *= bf16lo(gw.w); v[7] *= bf16hi(gw.w);
+      }
+      uint32_t pr[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float hi = (float)(__bf16)v[i];
+        const bf16x2 hl = {(__bf16)v[i], (__bf16)(v[i] - hi)};
+        pr[i] = __builtin_bit_cast(uint32_t, hl);
+      }
+      *reinterpret_cast<u32x4*>(w) = u32x4{pr[0], pr[1], pr[2], pr[3]};
+      *reinterpret_cast<u32x4*>(w + 4) = u32x4{pr[4], pr[5], pr[6], pr[7]};
+    }
+    if (sums) {
+      // the row's partial sums over its tpr aligned lanes, in fixed order
+      s2 = lane_group_sum(s2, tpr);
+      if (j == tpr - 1) ssw[b] = s2;
+    }
+    __syncthreads();
+    if (sums && t < nb) ssacc += ssw[t];  // chunks in order
+  };
+
+  u32x4 ring[RING][MT][NT];
+  set_tiles(0);
+  if (wave != 0) {  // weight loads across the wait, except in the polling wave
+#pragma unroll
+    for (int j = 0; j < RING; ++j) issue(ring[j], j);
+  }
   wait();
   for (int bp = 0; bp < nbpass; ++bp) {
     const int b0 = bp * prow, nb = min(prow, B - b0);
-    // deferred-norm sums of squares of this pass's rows, accumulated over the
-    // chunks in fixed order: per chunk, wave w's share of row b goes to
-    // ssw[b * nw + w] (one value per wave) and is added in wave order
-    float* ssw = reinterpret_cast<float*>(xbase + (size_t)prow * ldx * 4);  // [prow][16]
-    float ssacc = 0.f;  // thread t < nb keeps row b0 + t's running sum
+    ssacc = 0.f;
     for (int tp = 0; tp < ntpass; ++tp) {
       const int m0 = tp * MT;
+      const bool sums = norm && tp == 0;
+      if (bp > 0 || tp > 0) set_tiles(m0);
+      if (bp > 0 || tp > 0 || wave == 0) {
+#pragma unroll
+        for (int j = 0; j < RING; ++j) issue(ring[j], j);
+      }
       f32x4 acc[MT][NT][NBT];
 #pragma unroll
       for (int m = 0; m < MT; ++m)
@@ -124,113 +242,52 @@ __device__ __forceinline__ void mfma_stage(const MatRows& mr, int ntile, int K, 
         for (int j = 0; j < NT; ++j)
 #pragma unroll
           for (int bt = 0; bt < NBT; ++bt) acc[m][j][bt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      uint32_t roff[MT][NT];
+      stage_chunk(b0, nb, 0, sums);
+      // ---- one ring over the whole K stream; a chunk boundary restages the
+      // inputs while the next chunk's weight loads are already in flight
+      for (int i0 = 0; i0 < nslot; i0 += RING) {
 #pragma unroll
-      for (int m = 0; m < MT; ++m)
+        for (int jj = 0; jj < RING; ++jj) {
+          const int i = i0 + jj;
+          const int c = i / spc, st = wk + (i - c * spc) * WK;
+          if (i < nslot && i == c * spc && c > 0) stage_chunk(b0, nb, c, sums);
+          if (i < nslot && st < cs && c * KC + st * 32 < K) {
+            const int kl = st * 32 + (lane >> 4) * 8;  // column in the chunk
 #pragma unroll
-        for (int j = 0; j < NT; ++j)
-          roff[m][j] = (m0 + m < mt) ? mr(wg + (wr + (m0 + m) * WR) * nwg, j, lane & 15) : kOob;
-      const __amdgpu_buffer_rsrc_t rs = weight_rsrc(wbase, wbytes);
-      for (int c = 0; c < nchunk; ++c) {
-        const int kc0 = c * KC;
-        // ---- stage rows [b0, b0 + prow) x columns [kc0, kc0 + KC): x * gain as
-        // bf16 hi and lo; one 8-column group per thread per round (KC / 8 >=
-        // 64 threads per row, so a wave's lanes share a row in each round)
-        __syncthreads();  // the previous chunk's tiles and partial sums are consumed
-        const int gpr = KC / 8;  // groups per row
-        for (int g = t; g < prow * gpr; g += nth) {
-          const int b = g / gpr, k = kc0 + (g - b * gpr) * 8;
-          float v[8];
-          float s2 = 0.f;
-          if (b < nb && k < K) {
-            src.raw8(b0 + b, k, v);
+            for (int bt = 0; bt < NBT; ++bt) {
+              if (bt * 16 < prow) {
+                // this batch tile's hi and lo fragments, used by every tile
+                const uint32_t* w = xw + (size_t)(bt * 16 + (lane & 15)) * ldx + kl;
+                const u32x4 p0 = *reinterpret_cast<const u32x4*>(w);
+                const u32x4 p1 = *reinterpret_cast<const u32x4*>(w + 4);
+                // (hi | lo << 16) pairs -> 8 hi halves, 8 lo halves
+                const u32x4 hh{(p0.x & 0xFFFFu) | (p0.y << 16), (p0.z & 0xFFFFu) | (p0.w << 16),
+                               (p1.x & 0xFFFFu) | (p1.y << 16), (p1.z & 0xFFFFu) | (p1.w << 16)};
+                const u32x4 ll{(p0.x >> 16) | (p0.y & 0xFFFF0000u),
+                               (p0.z >> 16) | (p0.w & 0xFFFF0000u),
+                               (p1.x >> 16) | (p1.y & 0xFFFF0000u),
+                               (p1.z >> 16) | (p1.w & 0xFFFF0000u)};
+                const bf16x8 bh = __builtin_bit_cast(bf16x8, hh);
+                const bf16x8 bl = __builtin_bit_cast(bf16x8, ll);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) s2 = fmaf(v[i], v[i], s2);
-            if (gain) {
-              const u32x4 gw = *reinterpret_cast<const u32x4*>(gain + k);
-              v[0] *= bf16lo(gw.x); v[1] *= bf16hi(gw.x); v[2] *= bf16lo(gw.y); v[3] *= bf16hi(gw.y);
-              v[4] *= bf16lo(gw.z); v[5] *= bf16hi(gw.z); v[6] *= bf16lo(gw.w); v[7] *= bf16hi(gw.w);
-            }
-          } else {
+                for (int m = 0; m < MT; ++m) {
+                  if (m0 + m < mt) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) v[i] = 0.f;
-          }
-          uint16_t h[8], lo[8];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            h[i] = bf16_rn(v[i]);
-            lo[i] = bf16_rn(v[i] - bf16f(h[i]));
-          }
-          const int o = b * ldx + (k - kc0);
-          *reinterpret_cast<u32x4*>(xh + o) =
-              u32x4{h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16),
-                    h[4] | ((uint32_t)h[5] << 16), h[6] | ((uint32_t)h[7] << 16)};
-          *reinterpret_cast<u32x4*>(xl + o) =
-              u32x4{lo[0] | ((uint32_t)lo[1] << 16), lo[2] | ((uint32_t)lo[3] << 16),
-                    lo[4] | ((uint32_t)lo[5] << 16), lo[6] | ((uint32_t)lo[7] << 16)};
-          if (norm && tp == 0) {
-            // a round covers whole rows per wave: the wave's lanes share row b
-            const float ws = wave_sum(s2);
-            if (lane == 0) ssw[b * 16 + (g - b * gpr) / kWave] = ws;
-          }
-        }
-        __syncthreads();
-        if (norm && tp == 0 && t < nb) {
-          // this chunk's per-wave shares of row b0 + t, in fixed order
-          const int waves_per_row = gpr / kWave;
-          float s = 0.f;
-          for (int w = 0; w < waves_per_row; ++w) s += ssw[t * 16 + w];
-          ssacc += s;
-        }
-        // ---- this wave's K steps of the chunk: s = wk, wk + WK, ...
-        const int ns = min(KC, K - kc0 + 31) / 32;  // steps in this chunk
-        const int nq = ns > wk ? (ns - 1 - wk) / WK + 1 : 0;
-        u32x4 ring[kMfmaRing][MT][NT];
-        auto issue = [&](u32x4 (&f)[MT][NT], int q) {
-          const int k = kc0 + (wk + q * WK) * 32 + (lane >> 4) * 8;
-#pragma unroll
-          for (int m = 0; m < MT; ++m)
-#pragma unroll
-            for (int j = 0; j < NT; ++j) {
-              const uint32_t off = (q < nq && roff[m][j] != kOob && k < K) ? roff[m][j] + 2u * k : kOob;
-              f[m][j] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kNt);
-            }
-        };
-#pragma unroll
-        for (int j = 0; j < kMfmaRing; ++j) issue(ring[j], j);
-        for (int q0 = 0; q0 < nq; q0 += kMfmaRing) {
-#pragma unroll
-          for (int jj = 0; jj < kMfmaRing; ++jj) {
-            const int q = q0 + jj;
-            if (q < nq) {
-              const int kl = (wk + q * WK) * 32 + (lane >> 4) * 8;  // column in the chunk
-#pragma unroll
-              for (int bt = 0; bt < NBT; ++bt) {
-                if (bt * 16 < prow) {
-                  // this batch tile's hi and lo fragments, used by every tile
-                  const int o = (bt * 16 + (lane & 15)) * ldx + kl;
-                  const bf16x8 bh = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xh + o));
-                  const bf16x8 bl = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xl + o));
-#pragma unroll
-                  for (int m = 0; m < MT; ++m) {
-                    if (m0 + m < mt) {
-#pragma unroll
-                      for (int j = 0; j < NT; ++j) {
-                        const bf16x8 a = __builtin_bit_cast(bf16x8, ring[jj][m][j]);
-                        acc[m][j][bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh, acc[m][j][bt], 0, 0, 0);
-                        acc[m][j][bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl, acc[m][j][bt], 0, 0, 0);
-                      }
+                    for (int j = 0; j < NT; ++j) {
+                      const bf16x8 a = __builtin_bit_cast(bf16x8, ring[jj][m][j]);
+                      acc[m][j][bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh, acc[m][j][bt], 0, 0, 0);
+                      acc[m][j][bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl, acc[m][j][bt], 0, 0, 0);
                     }
                   }
                 }
               }
             }
-            issue(ring[jj], q + kMfmaRing);
           }
+          issue(ring[jj], i + RING);
         }
       }
       // ---- norms of this batch pass (first tile pass only)
-      if (norm && tp == 0) {
+      if (sums) {
         __syncthreads();
         if (t < nb) sc.rs[t] = 1.0f / sqrtf(ssacc / (float)K + eps);
       }
@@ -238,8 +295,8 @@ __device__ __forceinline__ void mfma_stage(const MatRows& mr, int ntile, int K, 
       __syncthreads();  // LDS staging area is free
       const int tiles_here = min(MT, max(0, mt - m0));
       if (WK > 1) {
-        // wave (wr, wk) stores its partial tiles; the tile count per wave is
-        // at most 1 when WK > 1 (WR >= tiles per workgroup)
+        // wave (wr, wk) stores its partial tile; a wave has at most one tile
+        // when WK > 1 (WR >= tiles per workgroup)
         const int per = NT * NBT * 4 * kWave;  // floats per wave
         float* mine = red + (size_t)wave * per;
         if (tiles_here > 0) {
@@ -258,10 +315,10 @@ __device__ __forceinline__ void mfma_stage(const MatRows& mr, int ntile, int K, 
             for (int bt = 0; bt < NBT; ++bt)
 #pragma unroll
               for (int i = 0; i < 4; ++i) {
-                float s = acc[0][j][bt][i];
+                float sum = acc[0][j][bt][i];
                 for (int q = 1; q < WK; ++q)
-                  s += red[(size_t)(wr + q * WR) * per + ((j * NBT + bt) * 4 + i) * kWave + lane];
-                acc[0][j][bt][i] = s;
+                  sum += red[(size_t)(wr + q * WR) * per + ((j * NBT + bt) * 4 + i) * kWave + lane];
+                acc[0][j][bt][i] = sum;
               }
         }
       }

@@ -77,7 +77,7 @@ __device__ __forceinline__ void trace_ev(const Params& P, int l, int stage, int 
 
 // ----------------------------------------------------------------- QKV
 
-template <int NB>
+template <int NB, int MR = kMfmaRingSmall>
 __device__ __forceinline__ void stage_qkv(const Params& P, int l, int wg, int nwg, char* smem) {
   constexpr int NR = kNrQkv, UC = kUcQkv;
   const Dims& D = P.D;
@@ -120,7 +120,7 @@ __device__ __forceinline__ void stage_qkv(const Params& P, int l, int wg, int nw
       const int row = tile * 16 + r;
       if (row < rows_total) st_coh(out + (int64_t)b * rows_total + row, v[0] * sc.rs[bl]);
     };
-    mfma_stage<kMfmaNbt<NB>, 1>(MatRows{Wm, {Wm, Wm}, rows_total, K}, (rows_total + 15) / 16, K, Wm,
+    mfma_stage<kMfmaNbt<NB>, 1, MR>(MatRows{Wm, {Wm, Wm}, rows_total, K}, (rows_total + 15) / 16, K, Wm,
                            wbytes, src, layer_w(P, l, P.W.o_attn_norm), true, D.eps, B, P.S.x_cap,
                            wait, epe, [](int, int) {}, wg, nwg, smem);
   } else {
@@ -251,18 +251,6 @@ __device__ __forceinline__ void attn_copy_tiles(const Params& P, int l, const At
       __builtin_amdgcn_global_load_lds((isv ? vsrc : ksrc) + o,
                                        (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
   }
-}
-
-// Sum over aligned groups of w lanes (w = 1..32, a power of two).  DPP row
-// rotations move data to higher lanes, so the total is valid in the last
-// lane of each group.
-__device__ __forceinline__ float lane_group_sum(float v, int w) {
-  if (w > 1) v += dpp_f<0xB1, 0xF>(0.f, v);     // + lane ^ 1
-  if (w > 2) v += dpp_f<0x4E, 0xF>(0.f, v);     // + lane ^ 2
-  if (w > 4) v += dpp_f<0x124, 0xF>(0.f, v);    // row_ror:4 (lane 7 of 8 gets lanes 0..3)
-  if (w > 8) v += dpp_f<0x128, 0xF>(0.f, v);    // row_ror:8 (lane 15 of 16 gets lanes 0..7)
-  if (w > 16) v += __shfl_up(v, 16, kWave);     // lane 31 of 32 gets lanes 0..15
-  return v;
 }
 
 __device__ __forceinline__ void attn_item(const Params& P, int l, const AttnItem& a, char* smem) {
@@ -525,7 +513,7 @@ __device__ __forceinline__ void stage_attn(const Params& P, int l, int wg, int n
 
 // ----------------------------------------------------------- O-proj
 
-template <int NB>
+template <int NB, int MR = kMfmaRingSmall>
 __device__ __forceinline__ void stage_o(const Params& P, int l, int wg, int nwg, char* smem) {
   constexpr int NR = kNrO, UC = kUcO;
   const Dims& D = P.D;
@@ -585,7 +573,7 @@ __device__ __forceinline__ void stage_o(const Params& P, int l, int wg, int nwg,
       }
       st_coh(xb + (int64_t)b * D.H + row, res + v[0]);
     };
-    mfma_stage<kMfmaNbt<NB>, 1>(MatRows{Wm, {Wm, Wm}, rows_total, K}, (rows_total + 15) / 16, K, Wm,
+    mfma_stage<kMfmaNbt<NB>, 1, MR>(MatRows{Wm, {Wm, Wm}, rows_total, K}, (rows_total + 15) / 16, K, Wm,
                            wbytes, src, nullptr, false, D.eps, B, P.S.x_cap, wait, epe,
                            [](int, int) {}, wg, nwg, smem);
   } else {
@@ -638,7 +626,7 @@ __device__ __forceinline__ void gu_prefetch(const Params& P, int l, int wg, int 
   gemv_prefetch(ws, ring);
 }
 
-template <int NB>
+template <int NB, int MR = kMfmaRingSmall>
 __device__ __forceinline__ void stage_gu(const Params& P, int l, int wg, int nwg, char* smem,
                          GuBlock (&ring)[kPfGu], bool prefetched) {
   constexpr int NP = kPairsGu, NR = 2 * kPairsGu;
@@ -679,7 +667,7 @@ __device__ __forceinline__ void stage_gu(const Params& P, int l, int wg, int nwg
       const float a = v[0] * sc.rs[bl], u = v[1] * sc.rs[bl];
       st_coh(h + (int64_t)b * I + row, a / (1.0f + expf(-a)) * u);
     };
-    mfma_stage<kMfmaNbt<NB>, 2>(MatRows{layer_w(P, l, 0), {rows.Wg, rows.Wu}, I, K}, (I + 15) / 16, K,
+    mfma_stage<kMfmaNbt<NB>, 2, MR>(MatRows{layer_w(P, l, 0), {rows.Wg, rows.Wu}, I, K}, (I + 15) / 16, K,
                            layer_w(P, l, 0), (uint32_t)(P.W.layer_stride * 2), src,
                            layer_w(P, l, P.W.o_mlp_norm), true, D.eps, B, P.S.x_cap, wait, epe,
                            [](int, int) {}, wg, nwg, smem);
@@ -694,7 +682,7 @@ __device__ __forceinline__ void stage_gu(const Params& P, int l, int wg, int nwg
 
 // ---------------------------------------------------------- Down-proj
 
-template <int NB>
+template <int NB, int MR = kMfmaRingSmall>
 __device__ __forceinline__ void stage_d(const Params& P, int l, int wg, int nwg, char* smem) {
   constexpr int NR = kNrD, UC = kUcD;
   const Dims& D = P.D;
@@ -736,7 +724,7 @@ __device__ __forceinline__ void stage_d(const Params& P, int l, int wg, int nwg,
       const int64_t o = (int64_t)b * D.H + row;
       st_coh(xa + o, ld_coh(xb + o) + v[0]);
     };
-    mfma_stage<kMfmaNbt<NB>, 1>(MatRows{Wm, {Wm, Wm}, rows_total, K}, (rows_total + 15) / 16, K, Wm,
+    mfma_stage<kMfmaNbt<NB>, 1, MR>(MatRows{Wm, {Wm, Wm}, rows_total, K}, (rows_total + 15) / 16, K, Wm,
                            wbytes, src, nullptr, false, D.eps, B, P.S.x_cap, wait, epe,
                            [](int, int) {}, wg, nwg, smem);
   } else {
@@ -761,7 +749,7 @@ struct Best {
 };
 constexpr int kBestBytes = (int)sizeof(Best);
 
-template <int NB>
+template <int NB, int MR = kMfmaRingSmall>
 __device__ __forceinline__ void stage_lm(const Params& P, int wg, int nwg, char* smem) {
   constexpr int NR = kNrLm, UC = kUcLm;
   const Dims& D = P.D;
@@ -859,7 +847,7 @@ __device__ __forceinline__ void stage_lm(const Params& P, int wg, int nwg, char*
         bi[bt] = 0x7FFFFFFF;
       }
     };
-    mfma_stage<NBT, 1>(MatRows{Wm, {Wm, Wm}, rows_total, K}, (rows_total + 15) / 16, K, Wm, wbytes,
+    mfma_stage<NBT, 1, MR>(MatRows{Wm, {Wm, Wm}, rows_total, K}, (rows_total + 15) / 16, K, Wm, wbytes,
                        src, P.W.final_norm, true, D.eps, B, P.S.x_cap, wait, epe, pass_end, wg,
                        nwg, smem);
   } else {
