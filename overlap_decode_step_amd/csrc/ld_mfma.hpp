@@ -53,18 +53,18 @@ __host__ __device__ constexpr size_t mfma_row_bytes(int kc) {
   return (size_t)(kc + kMfmaPad) * 4 + 16 * 4;
 }
 // Staged rows of one batch pass (a multiple of 16) for a staging area of
-// `cap` bytes, and the K chunk (a multiple of kMfmaMinChunk, no longer than K
-// needs).
+// `cap` bytes, and the K chunk.
 __host__ __device__ constexpr int mfma_pass_rows(int B, uint32_t cap) {
   return (int)(cap / mfma_row_bytes(kMfmaMinChunk)) / 16 * 16 < ((B + 15) / 16) * 16
              ? (int)(cap / mfma_row_bytes(kMfmaMinChunk)) / 16 * 16
              : ((B + 15) / 16) * 16;
 }
 __host__ __device__ constexpr int mfma_chunk(int rows, int K, uint32_t cap) {
-  return (int)((cap / rows - 16 * 4) / 4 - kMfmaPad) / kMfmaMinChunk * kMfmaMinChunk <
-                 (K + kMfmaMinChunk - 1) / kMfmaMinChunk * kMfmaMinChunk
-             ? (int)((cap / rows - 16 * 4) / 4 - kMfmaPad) / kMfmaMinChunk * kMfmaMinChunk
-             : (K + kMfmaMinChunk - 1) / kMfmaMinChunk * kMfmaMinChunk;
+  // a power of two from kMfmaMinChunk up: the largest that fits, and no
+  // longer than K needs (the staging maps 512 threads onto its 8-column groups)
+  int kc = kMfmaMinChunk;
+  while (kc < K && (size_t)rows * mfma_row_bytes(2 * kc) <= cap && 2 * kc <= 4096) kc *= 2;
+  return kc;
 }
 
 
@@ -164,16 +164,24 @@ __device__ __forceinline__ void mfma_stage(const MatRows& mr, int ntile, int K, 
       wave_drain();
       __syncthreads();
     }
-    // thread (row b, j) of the tpr threads per row takes the row's 8-column
-    // groups j, j + tpr, ...: inputs (from the copy, or the bf16 embedding
-    // rows of the first layer) -> norm partial sum, gain, and each element
-    // rewritten as the pair (bf16 hi, bf16 lo) by the hardware conversion
-    // (round to nearest even); rows past the batch and columns past K become
-    // zeros
-    const int tpr = nth / prow, b = t / tpr, j = t - b * tpr;
-    float s2 = 0.f;
-    for (int kk = j * 8; kk < KC; kk += tpr * 8) {
-      const int k = kc0 + kk;
+    // thread t takes 8-column group j = t % gpr of the rows h, h + tpc, ...
+    // (h = t / gpr, tpc = threads per column group), so it loads its gain
+    // once: inputs (from the copy, or the bf16 embedding rows of the first
+    // layer) -> norm partial sums, gain, and each element rewritten as the
+    // pair (bf16 hi, bf16 lo) by the hardware conversion (round to nearest
+    // even); rows past the batch and columns past K become zeros
+    const int tpc = nth / gpr, j = t % gpr, h = t / gpr;
+    const int kk = j * 8, k = kc0 + kk;
+    float g8[8];
+    if (gain && k < K) {
+      const u32x4 gw = *reinterpret_cast<const u32x4*>(gain + k);
+      g8[0] = bf16lo(gw.x); g8[1] = bf16hi(gw.x); g8[2] = bf16lo(gw.y); g8[3] = bf16hi(gw.y);
+      g8[4] = bf16lo(gw.z); g8[5] = bf16hi(gw.z); g8[6] = bf16lo(gw.w); g8[7] = bf16hi(gw.w);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) g8[i] = 1.f;
+    }
+    for (int b = h; b < prow; b += tpc) {
       uint32_t* w = xw + (size_t)b * ldx + kk;
       float v[8];
       if (b < nb && k < K) {
@@ -191,31 +199,34 @@ __device__ __forceinline__ void mfma_stage(const MatRows& mr, int ntile, int K, 
 #pragma unroll
         for (int i = 0; i < 8; ++i) v[i] = 0.f;
       }
+      if (sums) {
+        float s2 = 0.f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) s2 = fmaf(v[i], v[i], s2);
-      if (gain && k < K) {
-        const u32x4 gw = *reinterpret_cast<const u32x4*>(gain + k);
-        v[0] *= bf16lo(gw.x); v[1] *= bf16hi(gw.x); v[2] *= bf16lo(gw.y); v[3] *= bf16hi(gw.y);
-        v[4] *= bf16lo(gw.z); v[5] *= bf16hi(gw.z); v[6] *= bf16lo(gw.w); v[7] *= bf16hi(gw.w);
+        for (int i = 0; i < 8; ++i) s2 = fmaf(v[i], v[i], s2);
+        // the wave's 64 lanes hold 64 column groups of row b
+        s2 = wave_sum(s2);
+        if (lane == 0) ssw[b * 16 + (j >> 6)] = s2;
       }
       uint32_t pr[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float hi = (float)(__bf16)v[i];
-        const bf16x2 hl = {(__bf16)v[i], (__bf16)(v[i] - hi)};
+        const float x = v[i] * g8[i];
+        const float hi = (float)(__bf16)x;
+        const bf16x2 hl = {(__bf16)x, (__bf16)(x - hi)};
         pr[i] = __builtin_bit_cast(uint32_t, hl);
       }
       *reinterpret_cast<u32x4*>(w) = u32x4{pr[0], pr[1], pr[2], pr[3]};
       *reinterpret_cast<u32x4*>(w + 4) = u32x4{pr[4], pr[5], pr[6], pr[7]};
     }
-    if (sums) {
-      // the row's partial sums over its tpr aligned lanes, in fixed order
-      s2 = lane_group_sum(s2, tpr);
-      if (j == tpr - 1) ssw[b] = s2;
-    }
     __syncthreads();
-    if (sums && t < nb) ssacc += ssw[t];  // chunks in order
+    if (sums && t < nb) {
+      // the row's per-wave shares, in fixed order
+      float sr = 0.f;
+      for (int q = 0; q < gpr / kWave; ++q) sr += ssw[t * 16 + q];
+      ssacc += sr;
+    }
   };
+
 
   u32x4 ring[RING][MT][NT];
   set_tiles(0);
