@@ -26,9 +26,14 @@
  *                   signalled ready (MegaOps summary, "Keep kernels
  *                   separate"; multi-streaming and prefetch, "What the
  *                   control can show").
- *   LD_MODE_MEGA  - one persistent cooperative kernel per step whose
- *                   workgroups walk the stages in order, synchronising on the
- *                   same counters (the megakernel of the Hazy post).
+ *   LD_MODE_MEGA  - one persistent kernel per step whose workgroups walk
+ *                   the stages in order, synchronising on the same counters
+ *                   (the megakernel of the Hazy post).  Its grid is one
+ *                   workgroup per CU and all of them must run at once: the
+ *                   GPU must not be shared with other work during the step
+ *                   (otherwise the step ends in LD_ETIMEOUT, not a hang).
+ *                   The tile-flag mode assumes the same of its two
+ *                   co-resident stage kernels.
  *
  * Conventions.
  *  - Every pointer documented "dev" is device memory on the current HIP

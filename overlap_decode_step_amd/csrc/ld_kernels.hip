@@ -3,10 +3,10 @@
 //
 //  k_qkv / k_attn / k_o / k_gu / k_d / k_lm : one kernel per stage, used by
 //      the whole-kernel-wait and tile-flag modes;
-//  k_mega : one persistent cooperative kernel per step whose workgroups run
-//      every stage of every layer in order, synchronising on the same
-//      readiness counters (the single-kernel decode of Hazy Research, "Look
-//      Ma, No Bubbles! Designing a Low-Latency Megakernel for Llama-1B");
+//  k_mega : one persistent kernel per step whose workgroups run every stage
+//      of every layer in order, synchronising on the same readiness counters
+//      (the single-kernel decode of Hazy Research, "Look Ma, No Bubbles!
+//      Designing a Low-Latency Megakernel for Llama-1B");
 //  k_gen_normal / k_fill16 / k_gen_kv : seeded synthetic inputs.
 // All decode kernels use dynamic LDS: a scratch area, then the staged input
 // vectors or the attention tiles.
@@ -159,11 +159,17 @@ hipError_t launch_stage(int stage, const Params& P, int l, int grid, int threads
   return hipLaunchKernel(fn, dim3(grid), dim3(threads), args, smem, s);
 }
 
+// The persistent kernel needs every workgroup resident at once (they wait on
+// each other).  The grid is the occupancy limit of an otherwise idle GPU, so
+// an ordinary launch places them all; it was measured about 18 us per step
+// cheaper than a cooperative launch.  If other work shares the GPU and some
+// workgroups cannot start, the resident ones run into the watchdog and the
+// step ends with LD_ETIMEOUT rather than hanging.
 hipError_t launch_mega(const Params& P, int grid, int threads, size_t smem, hipStream_t s) {
   const void* fn = kernel_ptr(0, nb_for_batch(P.S.B));
   Params p = P;
   void* args[] = {&p};
-  return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(threads), args, (unsigned)smem, s);
+  return hipLaunchKernel(fn, dim3(grid), dim3(threads), args, smem, s);
 }
 
 hipError_t occupancy(int stage, int nb, int threads, size_t smem, int* blocks_per_cu) {
