@@ -173,6 +173,16 @@ struct WBlock {
     }
   }
 
+  // A block copied to LDS by WStream::copy_to_lds (chunk (r, u) at
+  // (r * UC + u) KB, 16 bytes per lane).
+  __device__ __forceinline__ void load_lds(const char* src, int lane) {
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+#pragma unroll
+      for (int u = 0; u < UC; ++u)
+        w[r][u] = *reinterpret_cast<const u32x4*>(src + (r * UC + u) * 1024 + lane * 16);
+  }
+
   // acc[r][b] += W[r, block] . xs[b, block] for b < nb; inputs in LDS with
   // row stride ldx; columns >= kend skipped.
   template <int NB>
@@ -237,7 +247,33 @@ struct WStream {
               : kOob);
     blk.load(wbase, wbytes, roff, K, (i - q * bpt) * UC, lane);
   }
+
+  // Block i copied straight into LDS at dst (NR * UC KB, laid out for
+  // WBlock::load_lds), with direct-to-LDS loads; nothing for masked rows,
+  // columns past K or blocks past the end.
+  __device__ __forceinline__ void copy_to_lds(int i, char* dst, int lane) const {
+    if (i >= nblk) return;
+    const int q = i / bpt, c0 = (i - q * bpt) * UC;
+    const uint16_t* rows[NR];
+    rowfn(task(q), rows);
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+#pragma unroll
+      for (int u = 0; u < UC; ++u) {
+        const int k = (c0 + u) * kChunk + lane * 8;
+        if (rows[r] != nullptr && k < K)
+          __builtin_amdgcn_global_load_lds(rows[r] + k,
+                                           (__attribute__((address_space(3))) void*)(
+                                               dst + (r * UC + u) * 1024),
+                                           16, 0, kNt);
+      }
+    }
+  }
 };
+
+// LDS bytes of one block of NR rows x UC chunks.
+template <int NR, int UC>
+constexpr int kBlockLdsBytes = NR * UC * 1024;
 
 // Issue the first PF blocks of a stream into a ring, except in wave 0, which
 // polls readiness counters (loads return in order, so weight loads in flight
@@ -255,24 +291,35 @@ __device__ __forceinline__ void gemv_prefetch(const WStream<NR, UC, RowFn>& ws,
 
 // One GEMV stage for one workgroup: each wave streams its blocks keeping PF
 // in flight (the ring); unless `prefetched`, the first PF are issued here
-// before the stage waits for its input.  The batch is processed in tiles of
-// at most `bw` rows that fit the LDS staging area; each batch tile streams
-// the weights again.  Epi(tile, b0, nb, acc, scratch) consumes the reduced
-// sums (every lane of the calling wave holds every sum).
+// before the stage waits for its input.  With `lds`, this wave's blocks PF ..
+// PF + nl - 1 were already copied to LDS there (WStream::copy_to_lds, long
+// before): blocks are consumed in stream order, the first PF from the ring,
+// then those from LDS, then the rest streamed through the ring.  The batch is
+// processed in tiles of at most `bw` rows that fit the LDS staging area; each
+// batch tile streams the weights again (LDS blocks are used by a single batch
+// tile only).  Epi(tile, b0, nb, acc, scratch) consumes the reduced sums
+// (every lane of the calling wave holds every sum).
 template <int NR, int UC, int NB, int PF, class RowFn, class WaitFn, class Epi>
 __device__ __forceinline__ void gemv_run(const WStream<NR, UC, RowFn>& ws,
                                          WBlock<NR, UC> (&ring)[PF], bool prefetched,
                                          const XSrc& src, const uint16_t* gain, bool norm, float eps,
-                                         int B, int bw, const WaitFn& wait, Epi& epi, char* smem) {
+                                         int B, int bw, const WaitFn& wait, Epi& epi, char* smem,
+                                         const char* lds = nullptr, int nl_req = 0) {
   Scratch& sc = *reinterpret_cast<Scratch*>(smem);
   float* xs = reinterpret_cast<float*>(smem + kScratchBytes);
   const int lane = lane_id(), wave = wave_id();
   const int K = ws.K, nch = ws.nch, bpt = ws.bpt, nblk = ws.nblk;
   const int nbt = (B + bw - 1) / bw;
+  // blocks taken from LDS, and the register stream: block regblk(r)
+  const int nl = (lds != nullptr && nbt == 1) ? max(0, min(nl_req, nblk - PF)) : 0;
+  const int nreg = nblk - nl;
+  auto regblk = [&](int r) { return r < nreg ? (r < PF ? r : r + nl) : nblk; };
   if (!prefetched) gemv_prefetch(ws, ring);
   wait();
   for (int bt = 0; bt < nbt; ++bt) {
     const int b0 = bt * bw, nb = min(bw, B - b0);
+    // (its input loads also wait for any earlier loads of this wave: the
+    // copies to LDS have landed once this returns)
     stage_x<NB>(src, b0, nb, K, gain, norm, eps, xs, sc);
     if (bt > 0 || wave == 0) {
 #pragma unroll
@@ -283,26 +330,38 @@ __device__ __forceinline__ void gemv_run(const WStream<NR, UC, RowFn>& ws,
     for (int r = 0; r < NR; ++r)
 #pragma unroll
       for (int b = 0; b < NB; ++b) acc[r][b] = 0.f;
-    for (int i0 = 0; i0 < nblk; i0 += PF) {
+    auto consume = [&](const WBlock<NR, UC>& blk, int i) {
+      const int q = i / bpt, c = (i - q * bpt) * UC;
+      blk.template fma<NB>(xs, K, nb, K, c, lane, acc);
+      if (c + UC >= nch) {  // last block of task q
+#pragma unroll
+        for (int r = 0; r < NR; ++r)
+#pragma unroll
+          for (int b = 0; b < NB; ++b) acc[r][b] = wave_sum(acc[r][b]);
+        epi(ws.task(q), b0, nb, acc, sc);
+#pragma unroll
+        for (int r = 0; r < NR; ++r)
+#pragma unroll
+          for (int b = 0; b < NB; ++b) acc[r][b] = 0.f;
+      }
+    };
+    auto lds_blocks = [&]() {
+      for (int q = 0; q < nl; ++q) {
+        WBlock<NR, UC> blk;
+        blk.load_lds(lds + q * kBlockLdsBytes<NR, UC>, lane);
+        consume(blk, PF + q);
+      }
+    };
+    for (int r0 = 0; r0 < nreg; r0 += PF) {
+      if (r0 == PF) lds_blocks();
 #pragma unroll
       for (int j = 0; j < PF; ++j) {
-        const int i = i0 + j;
-        const int q = i / bpt, c = (i - q * bpt) * UC;
-        if (i < nblk) ring[j].template fma<NB>(xs, K, nb, K, c, lane, acc);
-        ws.issue(ring[j], i + PF, lane);
-        if (i < nblk && c + UC >= nch) {  // last block of task q
-#pragma unroll
-          for (int r = 0; r < NR; ++r)
-#pragma unroll
-            for (int b = 0; b < NB; ++b) acc[r][b] = wave_sum(acc[r][b]);
-          epi(ws.task(q), b0, nb, acc, sc);
-#pragma unroll
-          for (int r = 0; r < NR; ++r)
-#pragma unroll
-            for (int b = 0; b < NB; ++b) acc[r][b] = 0.f;
-        }
+        const int r = r0 + j;
+        if (r < nreg) consume(ring[j], regblk(r));
+        ws.issue(ring[j], regblk(r + PF), lane);
       }
     }
+    if (nreg <= PF) lds_blocks();
     if (bt + 1 < nbt) __syncthreads();  // every wave is done with xs before restaging
   }
 }

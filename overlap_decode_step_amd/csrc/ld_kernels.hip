@@ -69,18 +69,19 @@ __global__ __launch_bounds__(kMaxThreads) void k_mega(Params P) {
   for (int l = 0; l < P.D.L; ++l) {
     stage_qkv<NB, kMfmaRingBig>(P, l, wg, nwg, smem);
     // workgroups without an attention item load their first SwiGLU weight
-    // blocks while attention runs (VALU engine)
+    // blocks while attention runs, into registers and LDS (VALU engine)
     GuBlock gring[kPfGu];
     bool gpre = false;
+    int gnl = 0;
     stage_attn(P, l, wg, nwg, smem, [&] {
       if constexpr (NB < kMfmaMinBatch) {
-        gu_prefetch(P, l, wg, nwg, gring);
+        gnl = gu_prefetch<NB>(P, l, wg, nwg, gring, smem);
         gpre = true;
       }
     });
     __syncthreads();
     stage_o<NB, kMfmaRingBig>(P, l, wg, nwg, smem);
-    stage_gu<NB, kMfmaRingBig>(P, l, wg, nwg, smem, gring, gpre);
+    stage_gu<NB, kMfmaRingBig>(P, l, wg, nwg, smem, gring, gpre, gnl);
     stage_d<NB, kMfmaRingBig>(P, l, wg, nwg, smem);
   }
   stage_lm<NB, kMfmaRingBig>(P, wg, nwg, smem);

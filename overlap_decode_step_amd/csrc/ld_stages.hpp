@@ -616,19 +616,44 @@ __device__ __forceinline__ GuRows gu_rows(const Params& P, int l) {
 }
 __device__ __forceinline__ int gu_tiles(const Params& P) { return (P.D.I + kPairsGu - 1) / kPairsGu; }
 
-// Issue this wave's first SwiGLU weight blocks of layer l (the persistent
-// kernel calls it while attention runs).
-__device__ __forceinline__ void gu_prefetch(const Params& P, int l, int wg, int nwg,
-                                            GuBlock (&ring)[kPfGu]) {
+// Idle-time SwiGLU blocks of the persistent kernel: besides the register
+// ring, up to kGuLdsBlocks more blocks per wave are copied into the top of
+// the LDS staging area, as far as the staged input rows of the O and SwiGLU
+// stages leave room (those rows sit at the bottom of the same area).
+constexpr int kGuLdsBlocks = 2;
+constexpr int kGuBlockBytes = kBlockLdsBytes<2 * kPairsGu, kUcGu>;
+
+template <int NB>
+__device__ __forceinline__ int gu_lds_blocks(const Params& P) {
+  const Dims& D = P.D;
+  const size_t need = max((size_t)batch_tile(P, D.H, NB) * D.H, (size_t)batch_tile(P, D.qd, NB) * D.qd) * 4;
+  const size_t room = P.S.x_cap > need ? P.S.x_cap - need : 0;
+  return min(kGuLdsBlocks, (int)(room / ((size_t)kGuBlockBytes * nwaves())));
+}
+__device__ __forceinline__ char* gu_lds_base(const Params& P, char* smem, int nl) {
+  const size_t per_wave = (size_t)nl * kGuBlockBytes;
+  return smem + kScratchBytes + P.S.x_cap - nwaves() * per_wave + wave_id() * per_wave;
+}
+
+// Issue this wave's first SwiGLU weight blocks of layer l into the ring and
+// copy the next ones into LDS (the persistent kernel calls it while attention
+// runs).  Returns the number of blocks per wave placed in LDS.
+template <int NB>
+__device__ __forceinline__ int gu_prefetch(const Params& P, int l, int wg, int nwg,
+                                           GuBlock (&ring)[kPfGu], char* smem) {
   const GuRows rows = gu_rows(P, l);
   const GuStream ws(rows, gu_tiles(P), P.D.H, layer_w(P, l, 0), (uint32_t)(P.W.layer_stride * 2),
                     wg, nwg);
   gemv_prefetch(ws, ring);
+  const int nl = gu_lds_blocks<NB>(P);
+  char* dst = gu_lds_base(P, smem, nl);
+  for (int q = 0; q < nl; ++q) ws.copy_to_lds(kPfGu + q, dst + q * kGuBlockBytes, lane_id());
+  return nl;
 }
 
 template <int NB, int MR = kMfmaRingSmall>
 __device__ __forceinline__ void stage_gu(const Params& P, int l, int wg, int nwg, char* smem,
-                         GuBlock (&ring)[kPfGu], bool prefetched) {
+                         GuBlock (&ring)[kPfGu], bool prefetched, int lds_blocks = 0) {
   constexpr int NP = kPairsGu, NR = 2 * kPairsGu;
   const Dims& D = P.D;
   const int lane = lane_id();
@@ -673,7 +698,9 @@ __device__ __forceinline__ void stage_gu(const Params& P, int l, int wg, int nwg
                            [](int, int) {}, wg, nwg, smem);
   } else {
     gemv_run<NR, kUcGu, NB, kPfGu>(ws, ring, prefetched, src, layer_w(P, l, P.W.o_mlp_norm), true,
-                                   D.eps, B, bw, wait, epi, smem);
+                                   D.eps, B, bw, wait, epi, smem,
+                                   lds_blocks > 0 ? gu_lds_base(P, smem, lds_blocks) : nullptr,
+                                   lds_blocks);
   }
   trace_ev(P, l, kSGu, 2, wg);
   signal_if(P, stage_ctr(P, l, kCGu), wg);
