@@ -212,8 +212,10 @@ struct WBlock {
 // all rows lie in the buffer [wbase, wbase + wbytes)), one tile per task.
 // Round q deals tiles [q * stride, (q + 1) * stride) to the grid's waves in
 // order, so at any time the whole grid streams one contiguous window of the
-// matrix (measured faster than giving each XCD its own contiguous range).
-// The wave's tasks are streamed as one sequence of blocks of UC chunks.
+// matrix (measured faster than giving each XCD its own contiguous range;
+// dealing fewer tiles to the workgroups busy with attention was measured
+// slower too).  The wave's tasks are streamed as one sequence of blocks of UC
+// chunks.
 template <int NR, int UC, class RowFn>
 struct WStream {
   const RowFn& rowfn;
@@ -275,23 +277,24 @@ struct WStream {
 template <int NR, int UC>
 constexpr int kBlockLdsBytes = NR * UC * 1024;
 
-// Issue the first PF blocks of a stream into a ring, except in wave 0, which
-// polls readiness counters (loads return in order, so weight loads in flight
-// would delay every poll).  Called before the stage's readiness wait, or
-// earlier: the persistent kernel issues the SwiGLU stage's first blocks while
-// attention runs.
+// Issue the first PF blocks of a stream into a ring.  Called right before the
+// stage's readiness wait it skips wave 0, which polls the counters (loads
+// return in order, so weight loads in flight would delay every poll); called
+// long before (`all_waves`: the persistent kernel issues the SwiGLU stage's
+// first blocks while attention runs) every wave takes part.
 template <int NR, int UC, int PF, class RowFn>
 __device__ __forceinline__ void gemv_prefetch(const WStream<NR, UC, RowFn>& ws,
-                                              WBlock<NR, UC> (&ring)[PF]) {
-  if (wave_id() != 0) {
+                                              WBlock<NR, UC> (&ring)[PF], bool all_waves = false) {
+  if (all_waves || wave_id() != 0) {
 #pragma unroll
     for (int j = 0; j < PF; ++j) ws.issue(ring[j], j, lane_id());
   }
 }
 
 // One GEMV stage for one workgroup: each wave streams its blocks keeping PF
-// in flight (the ring); unless `prefetched`, the first PF are issued here
-// before the stage waits for its input.  With `lds`, this wave's blocks PF ..
+// in flight (the ring); unless `prefetched` (by gemv_prefetch with all_waves),
+// the first PF are issued here, before the stage waits for its input in waves
+// other than 0 and after it in wave 0.  With `lds`, this wave's blocks PF ..
 // PF + nl - 1 were already copied to LDS there (WStream::copy_to_lds, long
 // before): blocks are consumed in stream order, the first PF from the ring,
 // then those from LDS, then the rest streamed through the ring.  The batch is
@@ -321,7 +324,7 @@ __device__ __forceinline__ void gemv_run(const WStream<NR, UC, RowFn>& ws,
     // (its input loads also wait for any earlier loads of this wave: the
     // copies to LDS have landed once this returns)
     stage_x<NB>(src, b0, nb, K, gain, norm, eps, xs, sc);
-    if (bt > 0 || wave == 0) {
+    if (bt > 0 || (wave == 0 && !prefetched)) {
 #pragma unroll
       for (int j = 0; j < PF; ++j) ws.issue(ring[j], j, lane);
     }

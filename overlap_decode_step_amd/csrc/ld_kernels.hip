@@ -60,31 +60,51 @@ __global__ __launch_bounds__(kMaxThreads, kStageWavesPerSimd) void k_lm(Params P
   stage_lm<NB>(P, blockIdx.x, gridDim.x, smem);
 }
 
+// The persistent kernel reads its argument block for every stage straight
+// from the kernel-argument segment (invariant constant memory), so the
+// compiler reloads fields with scalar loads where a stage uses them.  (Kept in
+// one value across the layer loop, the ~100 dwords of fields did not fit the
+// scalar registers and were spilled to vector-register lanes: some 2000 lane
+// reads in the loop body.  Forcing a reload of every field at each stage
+// start was measured slower than letting the compiler choose.)
+__device__ __forceinline__ Params fresh_params() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  using ConstParams = const __attribute__((address_space(4))) Params;
+  return *(ConstParams*)__builtin_amdgcn_kernarg_segment_ptr();
+#else
+  return Params{};  // host pass: never called
+#endif
+}
+
 template <int NB>
-__global__ __launch_bounds__(kMaxThreads) void k_mega(Params P) {
+__global__ __launch_bounds__(kMaxThreads) void k_mega(Params P0) {
   extern __shared__ __align__(16) char smem[];
   scratch_init(smem);
   const int wg = blockIdx.x, nwg = gridDim.x;
+  const int L = P0.D.L;
 #pragma clang loop unroll(disable)
-  for (int l = 0; l < P.D.L; ++l) {
-    stage_qkv<NB, kMfmaRingBig>(P, l, wg, nwg, smem);
+  for (int l = 0; l < L; ++l) {
+    stage_qkv<NB, kMfmaRingBig>(fresh_params(), l, wg, nwg, smem);
     // workgroups without an attention item load their first SwiGLU weight
     // blocks while attention runs, into registers and LDS (VALU engine)
     GuBlock gring[kPfGu];
     bool gpre = false;
     int gnl = 0;
-    stage_attn(P, l, wg, nwg, smem, [&] {
-      if constexpr (NB < kMfmaMinBatch) {
-        gnl = gu_prefetch<NB>(P, l, wg, nwg, gring, smem);
-        gpre = true;
-      }
-    });
+    {
+      const Params P = fresh_params();
+      stage_attn(P, l, wg, nwg, smem, [&] {
+        if constexpr (NB < kMfmaMinBatch) {
+          gnl = gu_prefetch<NB>(P, l, wg, nwg, gring, smem);
+          gpre = true;
+        }
+      });
+    }
     __syncthreads();
-    stage_o<NB, kMfmaRingBig>(P, l, wg, nwg, smem);
-    stage_gu<NB, kMfmaRingBig>(P, l, wg, nwg, smem, gring, gpre, gnl);
-    stage_d<NB, kMfmaRingBig>(P, l, wg, nwg, smem);
+    stage_o<NB, kMfmaRingBig>(fresh_params(), l, wg, nwg, smem);
+    stage_gu<NB, kMfmaRingBig>(fresh_params(), l, wg, nwg, smem, gring, gpre, gnl);
+    stage_d<NB, kMfmaRingBig>(fresh_params(), l, wg, nwg, smem);
   }
-  stage_lm<NB, kMfmaRingBig>(P, wg, nwg, smem);
+  stage_lm<NB, kMfmaRingBig>(fresh_params(), wg, nwg, smem);
 }
 
 // ---------------------------------------------------------- generators

@@ -644,7 +644,7 @@ __device__ __forceinline__ int gu_prefetch(const Params& P, int l, int wg, int n
   const GuRows rows = gu_rows(P, l);
   const GuStream ws(rows, gu_tiles(P), P.D.H, layer_w(P, l, 0), (uint32_t)(P.W.layer_stride * 2),
                     wg, nwg);
-  gemv_prefetch(ws, ring);
+  gemv_prefetch(ws, ring, true);
   const int nl = gu_lds_blocks<NB>(P);
   char* dst = gu_lds_base(P, smem, nl);
   for (int q = 0; q < nl; ++q) ws.copy_to_lds(kPfGu + q, dst + q * kGuBlockBytes, lane_id());
