@@ -254,6 +254,103 @@ def test_llama1b_batch_sweep_sampled(ld, orc, llama1b, B):
     m.free()
 
 
+# -------------------------------------- 8B and 70B widths, two layers
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name,w_std", [("llama8b", 0.02), ("llama70b", 0.01)])
+def test_wide_shapes_two_layers(ld, orc, name, w_std):
+    # The Llama-8B and Llama-70B shapes at full width (hidden size, heads of
+    # 128, SwiGLU width, 128256-token vocabulary, untied LM head) with two
+    # layers, so the oracle finishes in seconds; KV length 1024 as in those
+    # workloads.  Batch 1 in every mode, then batch 16 (the MFMA engine) with
+    # sequences 0 and 15 checked.  At the 70B width the tile-flag mode is
+    # refused (the Down stage's staged input row, 28672 fp32, does not fit in
+    # half the LDS, so two stage kernels cannot share a CU): that refusal is
+    # checked instead.
+    shape = dict(W.SHAPES[name], n_layers=2)
+    modes = MODES if name != "llama70b" else ("wait", "mega")
+    print(f"{name} x2 layers: oracle weights", flush=True)
+    om = orc.model(shape, seed=W.SEED_WEIGHTS, w_std=w_std)
+    okv = orc.kv(shape, 1, 1040, seed=W.SEED_KV, kv_std=1.0, prefill=[1024])
+    tok0 = W.first_tokens(1, shape["vocab"])[0]
+    ref = oracle_trajectory(orc, om, okv, tok0, 1024, 1)
+    print(f"{name} x2 layers: GPU model", flush=True)
+    m = gpu_model(ld, shape, 16, 1040, [1024] * 16, w_std=w_std)
+    if "flags" not in modes:
+        with pytest.raises(ld.LdError) as ei:
+            m.set_mode("flags")
+        assert ei.value.status == ld.LD_EINVAL
+    run = GpuRunner(m, shape["vocab"], 1)
+    for mode in modes:
+        m.fill_kv(W.SEED_KV, 1.0, [1024] * 16)
+        m.set_mode(mode)
+        tok, pos, lg_ref, nref = ref[0]
+        lg, nx = run.step([tok], [pos])
+        err, rel, _ = check_row(lg[0], lg_ref, nx[0], nref, f"{name} B=1 mode={mode}")
+        print(f"{name} x2 B=1 mode={mode} max_abs={err:.2e} rel={rel:.2e}", flush=True)
+    B = 16
+    toks = W.first_tokens(B, shape["vocab"])
+    refs = {}
+    for b in (0, B - 1):
+        okv_b = orc.kv(shape, 1, 1040, seed=W.SEED_KV, kv_std=1.0, prefill=[1024], seq0=b)
+        refs[b] = orc.decode_one(om, okv_b, 0, toks[b], 1024)
+    run16 = GpuRunner(m, shape["vocab"], B)
+    for mode in modes[1:]:
+        m.fill_kv(W.SEED_KV, 1.0, [1024] * B)
+        m.set_mode(mode)
+        lg, nx = run16.step(toks, [1024] * B)
+        for b, (lg_ref, nref) in refs.items():
+            err, rel, _ = check_row(lg[b], lg_ref, nx[b], nref, f"{name} B={B} mode={mode} seq={b}")
+            print(f"{name} x2 B={B} mode={mode} seq={b} max_abs={err:.2e} rel={rel:.2e}", flush=True)
+    m.free()
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name,w_std,batches", [("llama8b", 0.02, (1, 2, 16, 64)),
+                                                ("llama70b", 0.01, (1, 4, 16))])
+def test_full_depth_properties(ld, name, w_std, batches):
+    # The Llama-8B (32 layers) and Llama-70B (80 layers, about 141 GB of bf16
+    # weights) shapes at full depth, KV length 1024, at the batch sizes of
+    # their workloads.  Too large for the oracle, so properties that hold at
+    # any size are checked: the logits are finite, every next token is the
+    # argmax of its row with the lowest index on ties, and the modes agree.
+    # Below batch 16 (VALU engine: each row's dot product stays in one wave)
+    # every mode adds the same numbers in the same order, so they agree
+    # bitwise.  From batch 16 the MFMA engine splits each tile's K steps over
+    # a number of waves chosen from the tiles per workgroup, which depends on
+    # the mode's grid, so the modes agree to rounding only (relative L2 within
+    # 1e-4, a tenth of the bar against the oracle).
+    shape = W.SHAPES[name]
+    Bmax = max(batches)
+    print(f"{name}: GPU model ({Bmax} sequences)", flush=True)
+    m = gpu_model(ld, shape, Bmax, 1040, [1024] * Bmax, w_std=w_std)
+    run = GpuRunner(m, shape["vocab"], Bmax)
+    modes = MODES if name != "llama70b" else ("wait", "mega")
+    for B in batches:
+        toks = W.first_tokens(B, shape["vocab"])
+        outs = {}
+        for mode in modes:
+            m.fill_kv(W.SEED_KV, 1.0, [1024] * Bmax)
+            m.set_mode(mode)
+            lg, nx = run.step(toks, [1024] * B)
+            assert np.all(np.isfinite(lg)), f"{name} B={B} mode={mode}: non-finite logits"
+            top = lg.max(axis=1, keepdims=True)
+            first = np.argmax(lg == top, axis=1)
+            assert np.array_equal(nx, first), f"{name} B={B} mode={mode}: next token is not the argmax"
+            outs[mode] = (lg, nx)
+        ref_lg = outs[modes[0]][0]
+        for mode in modes[1:]:
+            lg = outs[mode][0]
+            if B < 16:
+                assert np.array_equal(ref_lg, lg), f"{name} B={B}: {mode} differs"
+            else:
+                rel = np.linalg.norm(lg - ref_lg) / np.linalg.norm(ref_lg)
+                assert rel <= 1e-4, f"{name} B={B}: {mode} differs (rel L2 {rel:.2e})"
+        how = "bitwise equal" if B < 16 else "equal to rounding"
+        print(f"{name} B={B}: {'/'.join(modes)} {how}, next = argmax", flush=True)
+    m.free()
+
+
 # ------------------------------------------------------ errors and faults
 
 def test_host_argument_errors(ld):
