@@ -172,6 +172,10 @@ def main():
                     help="only copy a 1 GiB buffer (counter calibration)")
     ap.add_argument("--sweep", action="store_true",
                     help="also run the batch sweep (1, 4, 16, 64; KV ~U[256,1024]; every mode)")
+    ap.add_argument("--shape", default="llama1b", choices=["llama1b", "llama8b", "llama70b"],
+                    help="decoder shape (the 8B and 70B shapes skip the CPU baseline)")
+    ap.add_argument("--prefill", type=int, default=None,
+                    help="KV prefill per sequence (default 512 for llama1b, else 1024)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU only; --gpus must be 1", file=sys.stderr)
@@ -185,14 +189,16 @@ def main():
     from overlap_decode_step_amd import ld
     from synth import workloads as W
 
-    shape = W.LLAMA_1B
+    shape = W.SHAPES[args.shape]
+    w_std = W.WORKLOADS["llama70b"]["w_std"] if args.shape == "llama70b" else 0.02
+    headline = args.shape == "llama1b"
     B = args.batch
-    prefill = 512
+    prefill = args.prefill if args.prefill is not None else (512 if headline else 1024)
     steps, warmup = args.steps, args.warmup
     max_seq = prefill + max(steps, warmup) + 8
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    m = ld.Model(shape, seed=W.SEED_WEIGHTS, w_std=0.02)
+    m = ld.Model(shape, seed=W.SEED_WEIGHTS, w_std=w_std)
     m.alloc_kv(B, max_seq)
     m.fill_kv(W.SEED_KV, 1.0, [prefill] * B)
     torch.cuda.synchronize()
@@ -227,6 +233,12 @@ def main():
     results = {}
     modes = ["wait", "flags", "mega"] if args.all_modes else [args.mode]
     for mode in modes:
+        if mode != args.mode:
+            try:
+                m.set_mode(mode)
+            except ld.LdError as e:  # e.g. the tile-flag mode at the 70B width
+                print(f"# mode={mode} batch={B} refused: {e}", file=sys.stderr, flush=True)
+                continue
         run(mode, warmup, False)
         ms = run(mode, steps, True)
         results[mode] = ms
@@ -245,14 +257,17 @@ def main():
     print(f"# kernel_source_digest={digest} algorithmic_bytes_per_step={bytes_avg:.0f}",
           file=sys.stderr, flush=True)
     cpu = None
-    if not args.no_cpu:
+    if not args.no_cpu and headline:
         cpu = cpu_baseline(shape, prefill, args.cpu_steps)
         print(f"# cpu_baseline {cpu}", file=sys.stderr, flush=True)
     sweep = batch_sweep() if args.sweep else None
     kernel = {"mega": "k_mega (persistent, one launch per step)",
               "wait": "all stage kernels of one step", "flags": "all stage kernels of one step"}
+    metric = "decode tokens/s + achieved HBM GB/s vs peak, Llama-1B shape, batch 1"
+    if not (headline and B == 1):
+        metric = f"decode tokens/s + achieved HBM GB/s vs peak, {args.shape} shape, batch {B}"
     out = {
-        "metric": "decode tokens/s + achieved HBM GB/s vs peak, Llama-1B shape, batch 1",
+        "metric": metric,
         "value": B * 1000.0 / ms,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -264,11 +279,12 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"llama1b-shape decode, batch {B}, KV prefill {prefill}, "
+        "config": {"workload": f"{args.shape}-shape decode, batch {B}, KV prefill {prefill}, "
                                f"positions {prefill}..{prefill + steps - 1}",
                    "mode": args.mode, "batch": B},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": read_traffic(args.mode, B),
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": read_traffic(args.mode, B) if headline else None,
                      "kernel": kernel[args.mode], "algorithmic_bytes": bytes_avg},
         "cpu_baseline": cpu,
         "modes_ms_per_step": results,
