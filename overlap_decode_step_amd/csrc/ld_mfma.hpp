@@ -37,6 +37,11 @@ constexpr int kMfmaTileMats = 2;   // 16-row tiles x matrices a wave accumulates
 // 256 VGPRs per wave, the stage kernels 128
 constexpr int kMfmaRingBig = 8, kMfmaRingSmall = 4;
 constexpr int kMfmaPad = 4;        // 4-byte elements of padding per staged row (16 bytes)
+// Tiles per workgroup at least: a stage with fewer tiles than this many per
+// workgroup runs on ntile / kMfmaMinTiles workgroups, the others skip it.
+// Every participating workgroup stages the whole input, so this trades
+// staging traffic (B x K x 4 bytes per workgroup) against streaming lanes.
+constexpr int kMfmaMinTiles = 1;
 constexpr int kMfmaMinChunk = 512; // smallest K chunk (a wave's 64 lanes stage one row)
 constexpr int kSc1 = 16;           // cache policy: agent-coherent (sc1)
 
@@ -96,6 +101,8 @@ __device__ __forceinline__ void mfma_stage(const MatRows& mr, int ntile, int K, 
   char* xbase = smem + kScratchBytes;
   const int lane = lane_id(), wave = wave_id(), nw = nwaves(), t = tid(), nth = blockDim.x;
   // ---- decomposition (uniform across the grid)
+  nwg = min(nwg, max(1, ntile / kMfmaMinTiles));
+  if (wg >= nwg) return;
   const int tpw = (ntile + nwg - 1) / nwg;
   int WR = 1;
   while (WR < tpw && WR < nw) WR *= 2;
