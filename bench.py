@@ -115,24 +115,36 @@ def batch_sweep(runs=4, steps=64, batches=(1, 4, 16, 64)):
         toks = torch.tensor(W.first_tokens(B, shape["vocab"]), dtype=torch.int32, device=dev)
         pos_all = [torch.tensor([p + i for p in prefill], dtype=torch.int32, device=dev)
                    for i in range(steps)]
+        pbuf = torch.empty_like(pos_all[0])
+        tbuf = [toks.clone(), torch.empty_like(toks)]
+
+        def step(mode, i):
+            if mode == "graph":
+                # a captured step replays fixed addresses: the positions are
+                # updated in place (timed with the step)
+                pbuf.copy_(pos_all[i])
+                m.step(tbuf[i & 1], pbuf, logits, tbuf[(i + 1) & 1])
+            else:
+                m.step(tbuf[i & 1], pos_all[i], logits, tbuf[(i + 1) & 1])
+
         row = {}
-        for mode in ("wait", "flags", "mega"):
+        for mode in ("wait", "flags", "mega", "graph"):
             m.set_mode(mode)
             rates = []
             fill = prefill + [0] * (maxb - B)  # one length per cache slot
             for _ in range(runs):
                 m.fill_kv(W.SEED_KV, 1.0, fill)
-                tbuf = [toks.clone(), torch.empty_like(toks)]
+                tbuf[0].copy_(toks)
                 for i in range(3):  # warm-up, then the cache is refilled
-                    m.step(tbuf[i & 1], pos_all[i], logits, tbuf[(i + 1) & 1])
+                    step(mode, i)
                 m.fill_kv(W.SEED_KV, 1.0, fill)
-                tbuf = [toks.clone(), torch.empty_like(toks)]
+                tbuf[0].copy_(toks)
                 torch.cuda.synchronize()
                 ev0 = torch.cuda.Event(enable_timing=True)
                 ev1 = torch.cuda.Event(enable_timing=True)
                 ev0.record(stream)
                 for i in range(steps):
-                    m.step(tbuf[i & 1], pos_all[i], logits, tbuf[(i + 1) & 1])
+                    step(mode, i)
                 ev1.record(stream)
                 torch.cuda.synchronize()
                 if m.device_error() != 0:
@@ -163,7 +175,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=128)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--mode", default="mega", choices=["wait", "flags", "mega"])
+    ap.add_argument("--mode", default="mega", choices=["wait", "flags", "mega", "graph"])
     ap.add_argument("--batch", type=int, default=1)
     ap.add_argument("--all-modes", action="store_true", help="also time the other modes")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -211,17 +223,26 @@ def main():
     # stream and joins it back before the step returns)
     stream = torch.cuda.current_stream()
 
+    # token buffers (ping-ponged) and, for graph mode, one position buffer:
+    # fixed addresses, so that a captured step replays
+    tbuf = [toks.clone(), torch.empty_like(toks)]
+    pbuf = torch.empty_like(pos_all[0])
+
     def run(mode, n, timed):
         # greedy decode: the next tokens of step i are the inputs of step i + 1
         m.set_mode(mode)
         m.fill_kv(W.SEED_KV, 1.0, [prefill] * B)
-        tbuf = [toks.clone(), torch.empty_like(toks)]
+        tbuf[0].copy_(toks)
         torch.cuda.synchronize()
         if timed:
             ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             ev0.record(stream)
         for i in range(n):
-            m.step(tbuf[i & 1], pos_all[i], logits, tbuf[(i + 1) & 1])
+            if mode == "graph":
+                pbuf.copy_(pos_all[i])  # in place, timed with the step
+                m.step(tbuf[i & 1], pbuf, logits, tbuf[(i + 1) & 1])
+            else:
+                m.step(tbuf[i & 1], pos_all[i], logits, tbuf[(i + 1) & 1])
         if timed:
             ev1.record(stream)
         torch.cuda.synchronize()
@@ -231,7 +252,7 @@ def main():
         return ev0.elapsed_time(ev1) / n if timed else None
 
     results = {}
-    modes = ["wait", "flags", "mega"] if args.all_modes else [args.mode]
+    modes = ["wait", "flags", "mega", "graph"] if args.all_modes else [args.mode]
     for mode in modes:
         if mode != args.mode:
             try:
@@ -262,7 +283,8 @@ def main():
         print(f"# cpu_baseline {cpu}", file=sys.stderr, flush=True)
     sweep = batch_sweep() if args.sweep else None
     kernel = {"mega": "k_mega (persistent, one launch per step)",
-              "wait": "all stage kernels of one step", "flags": "all stage kernels of one step"}
+              "wait": "all stage kernels of one step", "flags": "all stage kernels of one step",
+              "graph": "all stage kernels of one step (graph replay)"}
     metric = "decode tokens/s + achieved HBM GB/s vs peak, Llama-1B shape, batch 1"
     if not (headline and B == 1):
         metric = f"decode tokens/s + achieved HBM GB/s vs peak, {args.shape} shape, batch {B}"

@@ -34,6 +34,18 @@
  *                   (otherwise the step ends in LD_ETIMEOUT, not a hang).
  *                   The tile-flag mode assumes the same of its two
  *                   co-resident stage kernels.
+ *   LD_MODE_GRAPH - the whole-kernel-wait step captured into a HIP graph
+ *                   and replayed (the graph-of-kernels alternative to a
+ *                   megakernel argued in "Megakernel Debate Sparks CUDA
+ *                   Infrastructure Community Feud").  A step is captured on
+ *                   the library's own stream the first time it is called
+ *                   with a given (batch, tokens, positions, logits,
+ *                   next_tokens) and SwiGLU tiling, and later steps with the
+ *                   same arguments replay it on the caller's stream, so the
+ *                   contents of those buffers may change between steps but
+ *                   not their addresses.  Up to 8 argument sets are kept
+ *                   (least recently captured dropped first); they are
+ *                   released by ld_free.  A capture failure returns LD_EHIP.
  *
  * Conventions.
  *  - Every pointer documented "dev" is device memory on the current HIP
@@ -73,7 +85,7 @@ typedef enum {
   LD_EDEVICE = -6   /* device input error (bad token or position) */
 } ld_status;
 
-typedef enum { LD_MODE_WAIT = 0, LD_MODE_FLAGS = 1, LD_MODE_MEGA = 2 } ld_mode;
+typedef enum { LD_MODE_WAIT = 0, LD_MODE_FLAGS = 1, LD_MODE_MEGA = 2, LD_MODE_GRAPH = 3 } ld_mode;
 
 /* Model shape.  Weights are bf16 row-major [out, in]; norm gains bf16. */
 typedef struct {

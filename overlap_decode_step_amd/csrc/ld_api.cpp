@@ -36,6 +36,16 @@ struct ld_model {
   int n_cu = 0;
   hipStream_t s1 = nullptr;
   hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+  // graph mode: captured whole-kernel-wait steps, keyed by their arguments
+  struct StepGraph {
+    int B, variant;
+    const void *tokens, *pos;
+    void *logits, *next;
+    hipGraph_t graph;
+    hipGraphExec_t exec;
+  };
+  std::vector<StepGraph> graphs;
+  hipStream_t s_cap = nullptr;  // capture stream (the caller's may be the legacy default)
   // cumulative counter totals (what every layer's counter will read once all
   // enqueued steps have finished)
   uint32_t tot_qkv = 0, tot_attn = 0, tot_o = 0, tot_gu = 0, tot_d = 0;
@@ -255,6 +265,7 @@ static ld_status setup_launch(ld_model* m) {
     m->wall_khz = (double)khz;
   m->watchdog_ticks = (uint64_t)(m->wall_khz * 1000.0 * 2.0);  // 2 s
   HIPCHK(m, hipStreamCreateWithFlags(&m->s1, hipStreamNonBlocking));
+  HIPCHK(m, hipStreamCreateWithFlags(&m->s_cap, hipStreamNonBlocking));
   HIPCHK(m, hipEventCreateWithFlags(&m->ev_fork, hipEventDisableTiming));
   HIPCHK(m, hipEventCreateWithFlags(&m->ev_join, hipEventDisableTiming));
   for (int b = 0; b <= 64; ++b) {
@@ -493,7 +504,8 @@ extern "C" ld_status ld_fill_kv(ld_model* m, uint64_t seed, float kv_std,
 
 extern "C" ld_status ld_set_mode(ld_model* m, ld_mode mode) {
   if (!m) return fail(nullptr, LD_EINVAL, "null model");
-  if (mode != LD_MODE_WAIT && mode != LD_MODE_FLAGS && mode != LD_MODE_MEGA)
+  if (mode != LD_MODE_WAIT && mode != LD_MODE_FLAGS && mode != LD_MODE_MEGA &&
+      mode != LD_MODE_GRAPH)
     return fail(m, LD_EINVAL, "unknown mode");
   if (mode == LD_MODE_FLAGS && m->kv_ready && !m->flags_ok)
     return fail(m, LD_EINVAL, "tile-flag mode cannot keep two stage kernels of this shape on a CU");
@@ -507,6 +519,30 @@ static Params make_params(ld_model* m) {
   P.W = m->W;
   P.K = m->K;
   return P;
+}
+
+// Captured steps bake in the weight and work arena addresses (fixed once the
+// KV arena exists) and the SwiGLU tiling (part of the key); they are released
+// with the model.
+static void drop_graphs(ld_model* m) {
+  for (auto& g : m->graphs) {
+    (void)hipGraphExecDestroy(g.exec);
+    (void)hipGraphDestroy(g.graph);
+  }
+  m->graphs.clear();
+}
+constexpr size_t kMaxGraphs = 8;  // captured argument sets kept per model
+
+// The whole-kernel-wait step: one kernel per stage, in order, on one stream.
+static hipError_t enqueue_wait_kernels(ld_model* m, const Params& P, hipStream_t s) {
+  const int L = m->D.L;
+  for (int l = 0; l < L; ++l) {
+    for (int stage : {kSQkv, kSAttn, kSO, kSGu, kSD}) {
+      const hipError_t e = launch_stage(stage, P, l, m->grid_wait, m->thr_wait, m->smem_wait, s);
+      if (e != hipSuccess) return e;
+    }
+  }
+  return launch_stage(kSLm, P, 0, m->grid_wait, m->thr_wait, m->smem_wait, s);
 }
 
 // Enqueue one step in the current mode.
@@ -544,6 +580,40 @@ static ld_status enqueue_step(ld_model* m, const int32_t* tokens, int32_t B, con
     HIPCHK(m, launch_mega(P, g, m->thr_mega, m->smem_mega, s0));
     return LD_OK;
   }
+  if (m->mode == LD_MODE_GRAPH && P.S.inject == 0) {
+    // the whole-kernel-wait step captured once per argument set (on the
+    // library's own stream) and replayed on the caller's stream
+    P.S.wait = 1;
+    P.S.x_cap = m->xcap_wait;
+    ld_model::StepGraph* hit = nullptr;
+    for (auto& g : m->graphs)
+      if (g.B == B && g.variant == P.S.gu_variant && g.tokens == tokens && g.pos == pos &&
+          g.logits == logits && g.next == next)
+        hit = &g;
+    if (!hit) {
+      if (m->graphs.size() >= kMaxGraphs) {
+        (void)hipGraphExecDestroy(m->graphs.front().exec);
+        (void)hipGraphDestroy(m->graphs.front().graph);
+        m->graphs.erase(m->graphs.begin());
+      }
+      ld_model::StepGraph g{B, P.S.gu_variant, tokens, pos, logits, next, nullptr, nullptr};
+      HIPCHK(m, hipStreamBeginCapture(m->s_cap, hipStreamCaptureModeThreadLocal));
+      const hipError_t e = enqueue_wait_kernels(m, P, m->s_cap);
+      const hipError_t e2 = hipStreamEndCapture(m->s_cap, &g.graph);
+      HIPCHK(m, e);
+      HIPCHK(m, e2);
+      const hipError_t e3 = hipGraphInstantiate(&g.exec, g.graph, nullptr, nullptr, 0);
+      if (e3 != hipSuccess) {
+        (void)hipGraphDestroy(g.graph);
+        HIPCHK(m, e3);
+      }
+      m->graphs.push_back(g);
+      hit = &m->graphs.back();
+    }
+    HIPCHK(m, hipGraphLaunch(hit->exec, s0));
+    return LD_OK;
+  }
+  // whole-kernel wait (also graph mode with a watchdog test target pending)
   const bool flags = (m->mode == LD_MODE_FLAGS);
   if (flags && !m->flags_ok)
     return fail(m, LD_EINVAL, "tile-flag mode cannot keep two stage kernels of this shape on a CU");
@@ -624,7 +694,9 @@ extern "C" void ld_free(ld_model* m) {
   (void)hipDeviceSynchronize();
   if (m->own_w && m->warena) (void)hipFree(m->warena);
   if (m->own_k && m->karena) (void)hipFree(m->karena);
+  drop_graphs(m);
   if (m->s1) (void)hipStreamDestroy(m->s1);
+  if (m->s_cap) (void)hipStreamDestroy(m->s_cap);
   if (m->ev_fork) (void)hipEventDestroy(m->ev_fork);
   if (m->ev_join) (void)hipEventDestroy(m->ev_join);
   delete m;

@@ -11,8 +11,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libld.so")
 
 LD_OK, LD_EINVAL, LD_ENOMEM, LD_EHIP, LD_ETIMEOUT, LD_ESTATE, LD_EDEVICE = 0, -1, -2, -3, -4, -5, -6
-LD_MODE_WAIT, LD_MODE_FLAGS, LD_MODE_MEGA = 0, 1, 2
-MODES = {"wait": LD_MODE_WAIT, "flags": LD_MODE_FLAGS, "mega": LD_MODE_MEGA}
+LD_MODE_WAIT, LD_MODE_FLAGS, LD_MODE_MEGA, LD_MODE_GRAPH = 0, 1, 2, 3
+MODES = {"wait": LD_MODE_WAIT, "flags": LD_MODE_FLAGS, "mega": LD_MODE_MEGA, "graph": LD_MODE_GRAPH}
 LD_SWIGLU_COL, LD_SWIGLU_ROW = 0, 1
 (LD_W_EMBED, LD_W_ATTN_NORM, LD_W_Q, LD_W_K, LD_W_V, LD_W_O, LD_W_MLP_NORM, LD_W_GATE, LD_W_UP,
  LD_W_DOWN, LD_W_FINAL_NORM, LD_W_LM_HEAD) = range(12)

@@ -55,12 +55,17 @@ class GpuRunner:
         self.dev = torch.device("cuda:0")
         self.logits = torch.empty((max_batch, vocab), dtype=torch.float32, device=self.dev)
         self.next = torch.empty(max_batch, dtype=torch.int32, device=self.dev)
+        # fixed input buffers, updated in place: graph mode replays its
+        # captured step as long as the addresses stay the same
+        self.tok = torch.empty(max_batch, dtype=torch.int32, device=self.dev)
+        self.pos = torch.empty(max_batch, dtype=torch.int32, device=self.dev)
 
     def step(self, tokens, positions):
         torch = self.torch
         B = len(tokens)
-        t = torch.tensor(list(tokens), dtype=torch.int32, device=self.dev)
-        p = torch.tensor(list(positions), dtype=torch.int32, device=self.dev)
+        t, p = self.tok[:B], self.pos[:B]
+        t.copy_(torch.tensor(list(tokens), dtype=torch.int32))
+        p.copy_(torch.tensor(list(positions), dtype=torch.int32))
         lg = self.logits[:B]
         nx = self.next[:B]
         self.m.step(t, p, lg, nx)

@@ -13,7 +13,7 @@ from synth import workloads as W
 
 pytestmark = pytest.mark.gpu
 
-MODES = ("wait", "flags", "mega")
+MODES = ("wait", "flags", "mega", "graph")
 
 
 @pytest.fixture(scope="module")
@@ -118,6 +118,40 @@ def test_modes_bitwise_equal_and_rerun(ld, tiny_ref):
     for mode in MODES[1:]:
         for a, b in zip(outs["wait"], outs[mode]):
             assert np.array_equal(a, b), f"{mode} differs from wait"
+    m.free()
+
+
+def test_graph_replays_match_eager(ld, tiny_ref):
+    # Graph mode replays the captured whole-kernel-wait step: every replay,
+    # with eager work of the program (input updates, another torch kernel)
+    # and a synchronisation between replays, must equal the eager step bit
+    # for bit.  Two token buffers are ping-ponged, so two argument sets are
+    # captured and each is replayed several times.
+    import torch
+    shape = W.TINY
+    m = gpu_model(ld, shape, 1, 256, [128])
+    dev = torch.device("cuda:0")
+    tok = [torch.zeros(1, dtype=torch.int32, device=dev) for _ in range(2)]
+    pos = torch.zeros(1, dtype=torch.int32, device=dev)
+    lg = torch.empty((1, shape["vocab"]), dtype=torch.float32, device=dev)
+    nx = torch.empty(1, dtype=torch.int32, device=dev)
+    outs = {}
+    for mode in ("wait", "graph"):
+        m.fill_kv(W.SEED_KV, 1.0, [128])
+        m.set_mode(mode)
+        seq = []
+        for s, (t, p, _, _) in enumerate(tiny_ref[:8]):
+            tok[s & 1].fill_(int(t))
+            pos.fill_(int(p))
+            scratch = torch.ones(4096, device=dev) * float(s)  # eager work between replays
+            m.step(tok[s & 1], pos, lg, nx)
+            torch.cuda.synchronize()
+            assert float(scratch[0]) == float(s)
+            assert m.device_error() == 0
+            seq.append((lg.cpu().numpy().copy(), int(nx.cpu()[0])))
+        outs[mode] = seq
+    for s, ((a, na), (b, nb)) in enumerate(zip(outs["wait"], outs["graph"])):
+        assert np.array_equal(a, b) and na == nb, f"graph replay {s} differs from the eager step"
     m.free()
 
 
@@ -268,7 +302,7 @@ def test_wide_shapes_two_layers(ld, orc, name, w_std):
     # half the LDS, so two stage kernels cannot share a CU): that refusal is
     # checked instead.
     shape = dict(W.SHAPES[name], n_layers=2)
-    modes = MODES if name != "llama70b" else ("wait", "mega")
+    modes = MODES if name != "llama70b" else ("wait", "mega", "graph")
     print(f"{name} x2 layers: oracle weights", flush=True)
     om = orc.model(shape, seed=W.SEED_WEIGHTS, w_std=w_std)
     okv = orc.kv(shape, 1, 1040, seed=W.SEED_KV, kv_std=1.0, prefill=[1024])
@@ -325,7 +359,7 @@ def test_full_depth_properties(ld, name, w_std, batches):
     print(f"{name}: GPU model ({Bmax} sequences)", flush=True)
     m = gpu_model(ld, shape, Bmax, 1040, [1024] * Bmax, w_std=w_std)
     run = GpuRunner(m, shape["vocab"], Bmax)
-    modes = MODES if name != "llama70b" else ("wait", "mega")
+    modes = MODES if name != "llama70b" else ("wait", "mega", "graph")
     for B in batches:
         toks = W.first_tokens(B, shape["vocab"])
         outs = {}
