@@ -186,6 +186,9 @@ def main():
                     help="also run the batch sweep (1, 4, 16, 64; KV ~U[256,1024]; every mode)")
     ap.add_argument("--shape", default="llama1b", choices=["llama1b", "llama8b", "llama70b"],
                     help="decoder shape (the 8B and 70B shapes skip the CPU baseline)")
+    ap.add_argument("--mlp-ablation", action="store_true",
+                    help="also time the whole-kernel-wait step with the fused SwiGLU stage "
+                         "against its two- and four-kernel unfused forms (batch < 16)")
     ap.add_argument("--prefill", type=int, default=None,
                     help="KV prefill per sequence (default 512 for llama1b, else 1024)")
     args = ap.parse_args()
@@ -266,6 +269,16 @@ def main():
         print(f"# mode={mode} batch={B} ms/step={ms:.4f} tok/s={B * 1000.0 / ms:.1f}",
               file=sys.stderr, flush=True)
     ms = results[args.mode]
+    ablation = None
+    if args.mlp_ablation:
+        ablation = {}
+        for variant in ("fused", "two", "four"):
+            m.set_mlp_variant(variant)
+            run("wait", warmup, False)
+            ablation[variant] = run("wait", steps, True)
+            print(f"# mlp={variant} mode=wait batch={B} ms/step={ablation[variant]:.4f}",
+                  file=sys.stderr, flush=True)
+        m.set_mlp_variant("fused")
     m.free()
     del m
     torch.cuda.synchronize()
@@ -313,6 +326,8 @@ def main():
     }
     if sweep is not None:
         out["batch_sweep_tokens_per_s"] = sweep
+    if ablation is not None:
+        out["mlp_ablation_wait_ms_per_step"] = ablation
     print(json.dumps(out), flush=True)
 
 

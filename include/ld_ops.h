@@ -52,6 +52,19 @@ ld_status ld_read_kv(ld_model* m, int32_t layer, int32_t seq, int32_t kv_head, i
 ld_status ld_set_swiglu_variant(ld_model* m, int32_t batch, int32_t variant);
 int32_t ld_get_swiglu_variant(const ld_model* m, int32_t batch);
 
+/* Unfused-MLP ablation (Deep Kernel Fusion for Transformers, "Key points",
+ * "Fusion scope": the fused first MLP stage never writes the projections
+ * out).  LD_MLP_FUSED (the default) runs the fused SwiGLU stage;
+ * LD_MLP_TWO_KERNELS one GEMV writing the gate and up projections, then a
+ * silu-product kernel; LD_MLP_FOUR_KERNELS the gate GEMV, the up GEMV, silu
+ * in place and the product.  All three give bitwise-equal results.  The
+ * unfused forms apply to the whole-kernel-wait mode only (the other modes
+ * always run the fused stage) and to batches below 16 (the VALU engine): a
+ * step outside that returns LD_EINVAL.  Returns LD_EINVAL for an unknown
+ * variant. */
+enum { LD_MLP_FUSED = 0, LD_MLP_TWO_KERNELS = 1, LD_MLP_FOUR_KERNELS = 2 };
+ld_status ld_set_mlp_variant(ld_model* m, int32_t variant);
+
 /* Spin limit of every device-side readiness wait (default 2 s). */
 ld_status ld_set_watchdog(ld_model* m, double seconds);
 

@@ -51,6 +51,7 @@ struct ld_model {
   uint32_t tot_qkv = 0, tot_attn = 0, tot_o = 0, tot_gu = 0, tot_d = 0;
   int gu_variant[65];
   bool gu_tuned[65];
+  int mlp_variant = LD_MLP_FUSED;  // unfused-MLP ablation (whole-kernel-wait mode)
   // launch geometry per mode: grid, threads per workgroup, LDS bytes, LDS for staged inputs
   int grid_wait = 0, grid_flags = 0, grid_mega[65] = {0};  // grid_mega indexed by nb
   int thr_wait = 512, thr_flags = 512, thr_mega = 512;
@@ -172,8 +173,8 @@ extern "C" size_t ld_weights_bytes(const ld_config* cfg) {
 
 // KV + workspace arena layout (byte offsets).
 struct KLayout {
-  size_t kc, vc, xa, xb, qkv, ao, part, hbuf, lm_val, lm_idx, rope, ctr, lm_ctr, split_ctr, err,
-      tune_ctr, total;
+  size_t kc, vc, xa, xb, qkv, ao, part, hbuf, gbuf, ubuf, lm_val, lm_idx, rope, ctr, lm_ctr,
+      split_ctr, err, tune_ctr, total;
   int split_len, max_splits, max_wg;
 };
 
@@ -236,6 +237,8 @@ static KLayout klayout(const ld_config* c, int maxB, int max_seq) {
   K.ao = take((size_t)maxB * qd * 4);
   K.part = take((size_t)maxB * c->n_q_heads * K.max_splits * (d + 2) * 4);
   K.hbuf = take((size_t)maxB * I * 4);
+  K.gbuf = take((size_t)maxB * I * 4);
+  K.ubuf = take((size_t)maxB * I * 4);
   K.lm_val = take((size_t)K.max_wg * maxB * 4);
   K.lm_idx = take((size_t)K.max_wg * maxB * 4);
   K.rope = take((size_t)max_seq * (d / 2) * 2 * 4);
@@ -396,6 +399,7 @@ static ld_status compute_grids(ld_model* m) {
       const size_t sm = (st == 0) ? m->smem_mega : std::max(m->smem_wait, m->smem_flags);
       HIPCHK(m, set_max_dynamic_smem(st, nb, sm));
     }
+    if (nb < kMfmaMinBatch) HIPCHK(m, set_max_dynamic_smem(kSMlpProj, nb, m->smem_wait));
     int occ = 0;
     HIPCHK(m, occupancy(0, nb, m->thr_mega, m->smem_mega, &occ));
     if (occ < 1) return fail(m, LD_EINVAL, "persistent kernel does not fit on a CU");
@@ -441,6 +445,8 @@ extern "C" ld_status ld_alloc_kv(ld_model* m, void* dev_buf, size_t bytes, int32
   K.ao = reinterpret_cast<float*>(base + KL.ao);
   K.part = reinterpret_cast<float*>(base + KL.part);
   K.hbuf = reinterpret_cast<float*>(base + KL.hbuf);
+  K.gbuf = reinterpret_cast<float*>(base + KL.gbuf);
+  K.ubuf = reinterpret_cast<float*>(base + KL.ubuf);
   K.lm_val = reinterpret_cast<float*>(base + KL.lm_val);
   K.lm_idx = reinterpret_cast<int*>(base + KL.lm_idx);
   K.rope = reinterpret_cast<const float*>(base + KL.rope);
@@ -634,11 +640,27 @@ static ld_status enqueue_step(ld_model* m, const int32_t* tokens, int32_t B, con
     ++k;
     return launch_stage(stage, P, l, g, thr, smem, s);
   };
+  // the first MLP stage: fused, or an unfused form of the ablation
+  const int mlp = flags ? LD_MLP_FUSED : m->mlp_variant;
+  if (mlp != LD_MLP_FUSED && B >= kMfmaMinBatch)
+    return fail(m, LD_EINVAL, "the unfused-MLP forms run on the VALU engine only (batch < 16)");
+  auto launch_mlp = [&](int l) -> hipError_t {
+    if (mlp == LD_MLP_FUSED) return launch(kSGu, l);
+    hipError_t e;
+    if (mlp == LD_MLP_TWO_KERNELS) {
+      if ((e = launch_mlp_proj(kMlpBoth, P, l, g, thr, smem, s0)) != hipSuccess) return e;
+      return launch_mlp_elem(kMlpSiluMul, P, s0);
+    }
+    if ((e = launch_mlp_proj(kMlpGate, P, l, g, thr, smem, s0)) != hipSuccess) return e;
+    if ((e = launch_mlp_proj(kMlpUp, P, l, g, thr, smem, s0)) != hipSuccess) return e;
+    if ((e = launch_mlp_elem(kMlpSilu, P, s0)) != hipSuccess) return e;
+    return launch_mlp_elem(kMlpMul, P, s0);
+  };
   for (int l = 0; l < L; ++l) {
     HIPCHK(m, launch(kSQkv, l));
     HIPCHK(m, launch(kSAttn, l));
     HIPCHK(m, launch(kSO, l));
-    HIPCHK(m, launch(kSGu, l));
+    HIPCHK(m, launch_mlp(l));
     HIPCHK(m, launch(kSD, l));
   }
   HIPCHK(m, launch(kSLm, 0));
@@ -700,6 +722,14 @@ extern "C" void ld_free(ld_model* m) {
   if (m->ev_fork) (void)hipEventDestroy(m->ev_fork);
   if (m->ev_join) (void)hipEventDestroy(m->ev_join);
   delete m;
+}
+
+extern "C" ld_status ld_set_mlp_variant(ld_model* m, int32_t variant) {
+  if (!m) return fail(nullptr, LD_EINVAL, "null model");
+  if (variant != LD_MLP_FUSED && variant != LD_MLP_TWO_KERNELS && variant != LD_MLP_FOUR_KERNELS)
+    return fail(m, LD_EINVAL, "unknown MLP variant");
+  m->mlp_variant = variant;
+  return LD_OK;
 }
 
 // ------------------------------------------------------------- tuning

@@ -60,6 +60,20 @@ __global__ __launch_bounds__(kMaxThreads, kStageWavesPerSimd) void k_lm(Params P
   stage_lm<NB>(P, blockIdx.x, gridDim.x, smem);
 }
 
+// unfused-MLP ablation: the projection GEMVs and the elementwise kernels
+template <int NB>
+__global__ __launch_bounds__(kMaxThreads, kStageWavesPerSimd) void k_mlp_proj(Params P, int l,
+                                                                             int which) {
+  extern __shared__ __align__(16) char smem[];
+  stage_mlp_proj<NB>(P, l, which, blockIdx.x, gridDim.x, smem);
+}
+
+__global__ void k_mlp_elem(Params P, int op, int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+    mlp_elementwise(P, op, i);
+}
+
 // The persistent kernel reads its argument block for every stage straight
 // from the kernel-argument segment (invariant constant memory), so the
 // compiler reloads fields with scalar loads where a stage uses them.  (Kept in
@@ -148,6 +162,9 @@ static const void* stage_fn(int stage) {
     case kSGu: return reinterpret_cast<const void*>(&k_gu<NB>);
     case kSD: return reinterpret_cast<const void*>(&k_d<NB>);
     case kSLm: return reinterpret_cast<const void*>(&k_lm<NB>);
+    case kSMlpProj:  // VALU engine only
+      if constexpr (NB < kMfmaMinBatch) return reinterpret_cast<const void*>(&k_mlp_proj<NB>);
+      return nullptr;
     default: return nullptr;
   }
 }
@@ -174,7 +191,7 @@ int nb_for_batch(int B) {
 hipError_t launch_stage(int stage, const Params& P, int l, int grid, int threads, size_t smem,
                         hipStream_t s) {
   const void* fn = kernel_ptr(stage, nb_for_batch(P.S.B));
-  if (!fn || stage == 0) return hipErrorInvalidValue;
+  if (!fn || stage == 0 || stage == kSMlpProj) return hipErrorInvalidValue;
   Params p = P;
   void* args[] = {&p, &l};
   return hipLaunchKernel(fn, dim3(grid), dim3(threads), args, smem, s);
@@ -191,6 +208,23 @@ hipError_t launch_mega(const Params& P, int grid, int threads, size_t smem, hipS
   Params p = P;
   void* args[] = {&p};
   return hipLaunchKernel(fn, dim3(grid), dim3(threads), args, smem, s);
+}
+
+hipError_t launch_mlp_proj(int which, const Params& P, int l, int grid, int threads, size_t smem,
+                           hipStream_t s) {
+  const void* fn = kernel_ptr(kSMlpProj, nb_for_batch(P.S.B));
+  if (!fn) return hipErrorInvalidValue;
+  Params p = P;
+  void* args[] = {&p, &l, &which};
+  return hipLaunchKernel(fn, dim3(grid), dim3(threads), args, smem, s);
+}
+
+hipError_t launch_mlp_elem(int op, const Params& P, hipStream_t s) {
+  const int64_t n = (int64_t)P.S.B * P.D.I;
+  const int64_t blocks = (n + 255) / 256;
+  const int grid = (int)(blocks < 4096 ? blocks : 4096);
+  hipLaunchKernelGGL(k_mlp_elem, dim3(grid), dim3(256), 0, s, P, op, n);
+  return hipGetLastError();
 }
 
 hipError_t occupancy(int stage, int nb, int threads, size_t smem, int* blocks_per_cu) {

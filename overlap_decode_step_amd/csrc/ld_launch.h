@@ -13,6 +13,11 @@ int nb_for_batch(int B);
 hipError_t launch_stage(int stage, const Params& P, int layer, int grid, int threads, size_t smem,
                         hipStream_t s);
 hipError_t launch_mega(const Params& P, int grid, int threads, size_t smem, hipStream_t s);
+// unfused-MLP ablation (VALU engine, batch < 16): projection GEMV `which`
+// (gate, up or both) and elementwise op (silu, mul, silu-mul)
+hipError_t launch_mlp_proj(int which, const Params& P, int layer, int grid, int threads,
+                           size_t smem, hipStream_t s);
+hipError_t launch_mlp_elem(int op, const Params& P, hipStream_t s);
 hipError_t occupancy(int stage, int nb, int threads, size_t smem, int* blocks_per_cu);
 hipError_t set_max_dynamic_smem(int stage, int nb, size_t smem);
 size_t scratch_bytes();

@@ -31,7 +31,6 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kMfmaMinBatch = 16;  // batches from here on take this engine
 constexpr int kMfmaTileMats = 2;   // 16-row tiles x matrices a wave accumulates at once
 // K steps of weight fragments in flight per wave: the persistent kernel has
 // 256 VGPRs per wave, the stage kernels 128

@@ -15,16 +15,25 @@ constexpr int kLeaves = 16;
 constexpr int kLeafStride = 32;  // uint32 slots between leaves (128 bytes)
 constexpr int kCtrWords = (kLeaves + 1) * kLeafStride;
 
-// Stage ids (watchdog error codes and schedule bookkeeping).
-enum : int { kSQkv = 1, kSAttn = 2, kSO = 3, kSGu = 4, kSD = 5, kSLm = 6 };
+// Stage ids (watchdog error codes and schedule bookkeeping).  kSMlpProj is
+// the projection kernel of the unfused-MLP ablation (kernel lookup only).
+enum : int { kSQkv = 1, kSAttn = 2, kSO = 3, kSGu = 4, kSD = 5, kSLm = 6, kSMlpProj = 7 };
 
 // Device error word codes (low byte; a timeout carries the stage id << 8).
 constexpr int kErrToken = 1;
 constexpr int kErrPos = 2;
 constexpr int kErrTimeout = 3;
 
+// Batches from here on take the MFMA engine; smaller ones the VALU engine.
+constexpr int kMfmaMinBatch = 16;
+
 // SwiGLU tiling variants (chosen offline per batch size).
 enum : int { kGuCol = 0, kGuRow = 1 };
+
+// Unfused-MLP ablation: projection kernels (gate rows, up rows, or both into
+// separate outputs) and elementwise ops (silu in place, product, silu-product).
+enum : int { kMlpGate = 0, kMlpUp = 1, kMlpBoth = 2 };
+enum : int { kMlpSilu = 0, kMlpMul = 1, kMlpSiluMul = 2 };
 
 struct Dims {
   int L, H, nq, nkv, d, I, V, group;
@@ -59,6 +68,8 @@ struct Work {
   float* ao;      // attention output [maxB][qd]
   float* part;    // attention split partials [maxB][nq][max_splits][d + 2]
   float* hbuf;    // SwiGLU output [maxB][I]
+  float* gbuf;    // unfused-MLP ablation: gate projections [maxB][I]
+  float* ubuf;    // unfused-MLP ablation: up projections [maxB][I]
   float* lm_val;  // argmax partials [max_wg][maxB]
   int* lm_idx;
   const float* rope;  // [max_seq][d/2][2] (cos, sin)

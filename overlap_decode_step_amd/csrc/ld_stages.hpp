@@ -707,6 +707,82 @@ __device__ __forceinline__ void stage_gu(const Params& P, int l, int wg, int nwg
   trace_ev(P, l, kSGu, 3, wg);
 }
 
+// ------------------------------------------ unfused-MLP ablation (VALU)
+//
+// The fused SwiGLU stage measured against two unfused forms of the same
+// first MLP stage (the fused form, Deep Kernel Fusion for Transformers, "Key
+// points" / "Fusion scope", never writes the projections out):
+//  - two kernels: one GEMV over the gate and up rows writing both
+//    projections (kMlpBoth), then silu(g) * u;
+//  - four kernels: the gate GEMV (kMlpGate), the up GEMV (kMlpUp), silu(g)
+//    in place, then the product.
+// Every form adds the same numbers in the same order as the fused stage (the
+// same staged input and norm factor, the same chunk order and reductions per
+// row, the same activation formula), so all three give bitwise-equal
+// results.  Whole-kernel-wait launches only: they wait on nothing and signal
+// nothing.  (The kMlp* codes are in ld_params.hpp.)
+
+template <int NB>
+__device__ __forceinline__ void stage_mlp_proj(const Params& P, int l, int which, int wg, int nwg,
+                                               char* smem) {
+  const Dims& D = P.D;
+  const int lane = lane_id();
+  const int I = D.I, K = D.H, B = P.S.B;
+  const XSrc src{P.K.xb, K, nullptr, nullptr, 0};
+  const uint16_t* base = layer_w(P, l, 0);
+  const uint32_t bytes = (uint32_t)(P.W.layer_stride * 2);
+  const uint16_t* gain = layer_w(P, l, P.W.o_mlp_norm);
+  const int bw = batch_tile(P, K, NB);
+  auto nowait = [] {};
+  if (which == kMlpBoth) {
+    constexpr int NP = kPairsGu, NR = 2 * kPairsGu;
+    const GuRows rows = gu_rows(P, l);
+    const GuStream ws(rows, gu_tiles(P), K, base, bytes, wg, nwg);
+    auto epi = [&](int t, int b0, int nb, float (&acc)[NR][NB], Scratch& sc) {
+#pragma unroll
+      for (int r = 0; r < NP; ++r)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          const int row = t * NP + r;
+          if (b < nb && row < I && lane == ((r * NB + b) & (kWave - 1))) {
+            st_coh(P.K.gbuf + (int64_t)(b0 + b) * I + row, acc[r][b] * sc.rs[b]);
+            st_coh(P.K.ubuf + (int64_t)(b0 + b) * I + row, acc[NP + r][b] * sc.rs[b]);
+          }
+        }
+    };
+    GuBlock ring[kPfGu];
+    gemv_run<NR, kUcGu, NB, kPfGu>(ws, ring, false, src, gain, true, D.eps, B, bw, nowait, epi, smem);
+  } else {
+    const uint16_t* Wm = which == kMlpGate ? layer_w(P, l, P.W.o_wg) : layer_w(P, l, P.W.o_wu);
+    float* out = which == kMlpGate ? P.K.gbuf : P.K.ubuf;
+    auto rowfn = [&](int t, const uint16_t* (&rows)[1]) {
+      rows[0] = t < I ? Wm + (int64_t)t * K : nullptr;
+    };
+    auto epi = [&](int t, int b0, int nb, float (&acc)[1][NB], Scratch& sc) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+        if (b < nb && t < I && lane == (b & (kWave - 1)))
+          st_coh(out + (int64_t)(b0 + b) * I + t, acc[0][b] * sc.rs[b]);
+    };
+    gemv_stage<1, kUcGu, NB, kPfGu>(rowfn, I, K, base, bytes, src, gain, true, D.eps, B, bw, nowait,
+                                    epi, wg, nwg, smem);
+  }
+}
+
+// The elementwise kernels of the unfused forms over [B][I]: silu(g) in place
+// (kMlpSilu), h = g * u (kMlpMul), or h = silu(g) * u (kMlpSiluMul).
+__device__ __forceinline__ void mlp_elementwise(const Params& P, int op, int64_t i) {
+  float* g = P.K.gbuf;
+  const float a = ld_coh(g + i);
+  if (op == kMlpSilu) {
+    st_coh(g + i, a / (1.0f + expf(-a)));
+  } else {
+    const float u = ld_coh(P.K.ubuf + i);
+    const float s = op == kMlpSiluMul ? a / (1.0f + expf(-a)) : a;
+    st_coh(P.K.hbuf + i, s * u);
+  }
+}
+
 // ---------------------------------------------------------- Down-proj
 
 template <int NB, int MR = kMfmaRingSmall>

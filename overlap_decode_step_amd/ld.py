@@ -14,6 +14,8 @@ LD_OK, LD_EINVAL, LD_ENOMEM, LD_EHIP, LD_ETIMEOUT, LD_ESTATE, LD_EDEVICE = 0, -1
 LD_MODE_WAIT, LD_MODE_FLAGS, LD_MODE_MEGA, LD_MODE_GRAPH = 0, 1, 2, 3
 MODES = {"wait": LD_MODE_WAIT, "flags": LD_MODE_FLAGS, "mega": LD_MODE_MEGA, "graph": LD_MODE_GRAPH}
 LD_SWIGLU_COL, LD_SWIGLU_ROW = 0, 1
+LD_MLP_FUSED, LD_MLP_TWO_KERNELS, LD_MLP_FOUR_KERNELS = 0, 1, 2
+MLP_VARIANTS = {"fused": LD_MLP_FUSED, "two": LD_MLP_TWO_KERNELS, "four": LD_MLP_FOUR_KERNELS}
 (LD_W_EMBED, LD_W_ATTN_NORM, LD_W_Q, LD_W_K, LD_W_V, LD_W_O, LD_W_MLP_NORM, LD_W_GATE, LD_W_UP,
  LD_W_DOWN, LD_W_FINAL_NORM, LD_W_LM_HEAD) = range(12)
 
@@ -58,6 +60,7 @@ def _load():
         "ld_write_weight": (S, [P, I32, I32, P]),
         "ld_read_kv": (S, [P, I32, I32, I32, I32, I32, P, P]),
         "ld_set_swiglu_variant": (S, [P, I32, I32]),
+        "ld_set_mlp_variant": (S, [P, I32]),
         "ld_get_swiglu_variant": (I32, [P, I32]),
         "ld_set_watchdog": (S, [P, D]),
         "ld_debug_inject_stall": (S, [P]),
@@ -164,6 +167,10 @@ def ld_set_swiglu_variant(m, batch, variant):
     return _check(LIB.ld_set_swiglu_variant(m, batch, variant), m)
 
 
+def ld_set_mlp_variant(m, variant):
+    return _check(LIB.ld_set_mlp_variant(m, MLP_VARIANTS.get(variant, variant)), m)
+
+
 def ld_get_swiglu_variant(m, batch):
     return int(LIB.ld_get_swiglu_variant(m, batch))
 
@@ -224,6 +231,9 @@ class Model:
 
     def set_mode(self, mode):
         ld_set_mode(self.h, mode)
+
+    def set_mlp_variant(self, variant):
+        ld_set_mlp_variant(self.h, variant)
 
     def step(self, tokens, positions, logits, next_tokens=None):
         """tokens/positions: cuda int32 [B]; logits: cuda float32 [B, vocab]."""

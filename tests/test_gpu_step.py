@@ -385,6 +385,45 @@ def test_full_depth_properties(ld, name, w_std, batches):
     m.free()
 
 
+# --------------------------------------------- unfused-MLP ablation
+
+@pytest.mark.parametrize("name,B", [("tiny", 1), ("tiny", 3), ("llama1b", 1)])
+def test_mlp_ablation_bitwise(ld, name, B):
+    # The fused SwiGLU stage and its two- and four-kernel unfused forms add
+    # the same numbers in the same order: whole-kernel-wait steps agree bit
+    # for bit.  Other modes keep the fused stage whatever the setting, and
+    # the unfused forms refuse the MFMA engine's batch sizes.
+    shape = W.SHAPES[name]
+    steps = 3 if name == "tiny" else 1
+    prefill = [128] * B if name == "tiny" else [512] * B
+    m = gpu_model(ld, shape, 16, 700, prefill + [128] * (16 - B))
+    run = GpuRunner(m, shape["vocab"], 16)
+    toks = W.first_tokens(B, shape["vocab"])
+    outs = {}
+    for mode, variant in (("wait", "fused"), ("wait", "two"), ("wait", "four"), ("mega", "four")):
+        m.fill_kv(W.SEED_KV, 1.0, prefill + [128] * (16 - B))
+        m.set_mode(mode)
+        m.set_mlp_variant(variant)
+        t = list(toks)
+        seq = []
+        for s in range(steps):
+            lg, nx = run.step(t, [p + s for p in prefill])
+            seq.append(lg)
+            t = list(nx)
+        outs[(mode, variant)] = seq
+    ref = outs[("wait", "fused")]
+    for key in (("wait", "two"), ("wait", "four"), ("mega", "four")):
+        for s, (a, b) in enumerate(zip(ref, outs[key])):
+            assert np.array_equal(a, b), f"{name} B={B} {key} step {s} differs from the fused stage"
+    m.set_mode("wait")
+    m.set_mlp_variant("two")
+    with pytest.raises(ld.LdError) as ei:
+        run.step(W.first_tokens(16, shape["vocab"]), [128] * 16)
+    assert ei.value.status == ld.LD_EINVAL
+    m.set_mlp_variant("fused")
+    m.free()
+
+
 # ------------------------------------------------------ errors and faults
 
 def test_host_argument_errors(ld):
