@@ -15,8 +15,9 @@
  * a fused Up/Gate/SiLU/product stage and a separate Down projection ("Deep
  * Kernel Fusion for Transformers", Key points, "Fusion scope").
  *
- * Execution modes (all share the same stage code and give bitwise-equal
- * results):
+ * Execution modes (all share the same stage code; below batch 16 they give
+ * bitwise-equal results, from 16 on the MFMA engine's split of each tile's
+ * K steps over waves depends on the mode's grid, so they agree to rounding):
  *   LD_MODE_WAIT  - one kernel per stage on one stream; each kernel starts
  *                   when the previous one has finished (the conventional
  *                   whole-kernel wait of the MegaOps summary, "In plain
