@@ -170,6 +170,58 @@ def copy_calibration():
     print(json.dumps({"copy_bytes": n, "copies": 3}), flush=True)
 
 
+def multi_token_bench(shape_name, B, M, steps, warmup, modes):
+    """Several tokens per sequence per step (ld_decode_step_tokens): B
+    sequences x M consecutive tokens (teacher forced: seeded tokens), KV
+    prefill 512 (1024 for the 8B and 70B shapes), positions advancing by M
+    per step.  Returns {mode: ms per step}; tokens/s = B * M / step time."""
+    import torch
+    from overlap_decode_step_amd import ld
+    from synth import workloads as W
+    shape = W.SHAPES[shape_name]
+    w_std = W.WORKLOADS["llama70b"]["w_std"] if shape_name == "llama70b" else 0.02
+    prefill = 512 if shape_name == "llama1b" else 1024
+    rows = B * M
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    m = ld.Model(shape, seed=W.SEED_WEIGHTS, w_std=w_std)
+    m.alloc_kv(rows, prefill + (steps + warmup) * M + 8)
+    logits = torch.empty((rows, shape["vocab"]), dtype=torch.float32, device=dev)
+    nxt = torch.empty(rows, dtype=torch.int32, device=dev)
+    toks = torch.tensor(W.first_tokens(rows, shape["vocab"]), dtype=torch.int32, device=dev)
+    pos_all = [torch.tensor([prefill + i * M + j for b in range(B) for j in range(M)],
+                            dtype=torch.int32, device=dev) for i in range(max(steps, warmup))]
+    pbuf = torch.empty_like(pos_all[0])
+    stream = torch.cuda.current_stream()
+    out = {}
+    for mode in modes:
+        try:
+            m.set_mode(mode)
+        except ld.LdError as e:
+            print(f"# tokens_per_seq={M} mode={mode} refused: {e}", file=sys.stderr, flush=True)
+            continue
+        ms = None
+        for n, timed in ((warmup, False), (steps, True)):
+            m.fill_kv(W.SEED_KV, 1.0, [prefill] * B + [1] * (rows - B))
+            torch.cuda.synchronize()
+            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ev0.record(stream)
+            for i in range(n):
+                pbuf.copy_(pos_all[i])
+                m.step_tokens(toks, M, pbuf, logits, nxt)
+            ev1.record(stream)
+            torch.cuda.synchronize()
+            if m.device_error() != 0:
+                raise RuntimeError(f"device error with {M} tokens per sequence, mode {mode}")
+            if timed:
+                ms = ev0.elapsed_time(ev1) / n
+        out[mode] = ms
+        print(f"# tokens_per_seq={M} sequences={B} mode={mode} ms/step={ms:.4f} "
+              f"tok/s={rows * 1000.0 / ms:.1f}", file=sys.stderr, flush=True)
+    m.free()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -186,6 +238,9 @@ def main():
                     help="also run the batch sweep (1, 4, 16, 64; KV ~U[256,1024]; every mode)")
     ap.add_argument("--shape", default="llama1b", choices=["llama1b", "llama8b", "llama70b"],
                     help="decoder shape (the 8B and 70B shapes skip the CPU baseline)")
+    ap.add_argument("--tokens-per-seq", type=int, default=1,
+                    help="several consecutive tokens per sequence per step (a prefill chunk): "
+                         "times ld_decode_step_tokens in every mode instead of the decode step")
     ap.add_argument("--mlp-ablation", action="store_true",
                     help="also time the whole-kernel-wait step with the fused SwiGLU stage "
                          "against its two- and four-kernel unfused forms (batch < 16)")
@@ -197,6 +252,20 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.tokens_per_seq > 1:
+        M, B = args.tokens_per_seq, args.batch
+        res = multi_token_bench(args.shape, B, M, args.steps, args.warmup,
+                                ["wait", "flags", "mega", "graph"])
+        best = min(v for v in res.values() if v is not None)
+        print(json.dumps({
+            "metric": f"prefill-chunk tokens/s, {args.shape} shape, {B} sequences x {M} tokens",
+            "value": B * M * 1000.0 / best, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": best, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": f"{args.shape}-shape, {B} sequences x {M} consecutive tokens "
+                                   f"per step (teacher forced)", "tokens_per_seq": M, "batch": B},
+            "modes_ms_per_step": res}), flush=True)
         return
 
     import torch

@@ -138,6 +138,28 @@ ld_status ld_decode_step(ld_model* m, const int32_t* tokens, int32_t batch,
                          const int32_t* positions, float* logits, int32_t* next_tokens,
                          void* stream);
 
+/* Several consecutive tokens per sequence in one step (a prefill chunk, or
+ * the verification of drafted tokens): the prompt-processing setting of the
+ * MegaOps summary's prefill comparisons ("A multi-GPU check"), here on one
+ * GPU, with every GEMV a GEMM over batch * tokens_per_seq rows.  Row
+ * r = b * tokens_per_seq + j is token
+ * j of sequence b (KV cache slot b):
+ *   tokens      dev int32 [batch * tokens_per_seq] (in)
+ *   positions   dev int32 [batch * tokens_per_seq]: positions[r] =
+ *               positions[b * tokens_per_seq] + j, each < max_seq (a device
+ *               error otherwise, like a bad position)
+ *   logits      dev fp32 [batch * tokens_per_seq, vocab] (out)
+ *   next_tokens dev int32 [batch * tokens_per_seq] or NULL (out)
+ * Token j attends to positions 0 .. positions[r] of its sequence, that is
+ * the cache plus this step's tokens 0 .. j; all of the step's K and V rows
+ * are appended.  The result equals tokens_per_seq single-token steps in
+ * order (teacher forced).  batch * tokens_per_seq must be in
+ * [1, max_batch] and tokens_per_seq >= 1 (LD_EINVAL otherwise); 16 rows and
+ * more run on the MFMA engine.  tokens_per_seq = 1 is ld_decode_step. */
+ld_status ld_decode_step_tokens(ld_model* m, const int32_t* tokens, int32_t tokens_per_seq,
+                                int32_t batch, const int32_t* positions, float* logits,
+                                int32_t* next_tokens, void* stream);
+
 /* Offline choice of the SwiGLU tiling ("Deep Kernel Fusion for Transformers",
  * Summary: a profiler benchmarks the tiling variants on the target before
  * inference and keeps the fastest; Key points: no runtime dispatch cost).

@@ -38,7 +38,7 @@ struct ld_model {
   hipEvent_t ev_fork = nullptr, ev_join = nullptr;
   // graph mode: captured whole-kernel-wait steps, keyed by their arguments
   struct StepGraph {
-    int B, variant;
+    int B, M, variant;
     const void *tokens, *pos;
     void *logits, *next;
     hipGraph_t graph;
@@ -524,6 +524,7 @@ static Params make_params(ld_model* m) {
   P.D = m->D;
   P.W = m->W;
   P.K = m->K;
+  P.S.M = 1;
   return P;
 }
 
@@ -552,14 +553,16 @@ static hipError_t enqueue_wait_kernels(ld_model* m, const Params& P, hipStream_t
 }
 
 // Enqueue one step in the current mode.
-static ld_status enqueue_step(ld_model* m, const int32_t* tokens, int32_t B, const int32_t* pos,
-                              float* logits, int32_t* next, hipStream_t s0) {
+// B rows: M consecutive tokens of each of B / M sequences.
+static ld_status enqueue_step(ld_model* m, const int32_t* tokens, int32_t B, int32_t M,
+                              const int32_t* pos, float* logits, int32_t* next, hipStream_t s0) {
   Params P = make_params(m);
   P.S.tokens = tokens;
   P.S.pos = pos;
   P.S.logits = logits;
   P.S.next = next;
   P.S.B = B;
+  P.S.M = M;
   P.S.T = step_split_len(m->D.split_len, B);
   P.S.gu_variant = m->gu_variant[B];
   P.S.inject = m->inject_next;
@@ -593,8 +596,8 @@ static ld_status enqueue_step(ld_model* m, const int32_t* tokens, int32_t B, con
     P.S.x_cap = m->xcap_wait;
     ld_model::StepGraph* hit = nullptr;
     for (auto& g : m->graphs)
-      if (g.B == B && g.variant == P.S.gu_variant && g.tokens == tokens && g.pos == pos &&
-          g.logits == logits && g.next == next)
+      if (g.B == B && g.M == M && g.variant == P.S.gu_variant && g.tokens == tokens &&
+          g.pos == pos && g.logits == logits && g.next == next)
         hit = &g;
     if (!hit) {
       if (m->graphs.size() >= kMaxGraphs) {
@@ -602,7 +605,7 @@ static ld_status enqueue_step(ld_model* m, const int32_t* tokens, int32_t B, con
         (void)hipGraphDestroy(m->graphs.front().graph);
         m->graphs.erase(m->graphs.begin());
       }
-      ld_model::StepGraph g{B, P.S.gu_variant, tokens, pos, logits, next, nullptr, nullptr};
+      ld_model::StepGraph g{B, M, P.S.gu_variant, tokens, pos, logits, next, nullptr, nullptr};
       HIPCHK(m, hipStreamBeginCapture(m->s_cap, hipStreamCaptureModeThreadLocal));
       const hipError_t e = enqueue_wait_kernels(m, P, m->s_cap);
       const hipError_t e2 = hipStreamEndCapture(m->s_cap, &g.graph);
@@ -681,8 +684,25 @@ extern "C" ld_status ld_decode_step(ld_model* m, const int32_t* tokens, int32_t 
   if (((uintptr_t)tokens & 3) || ((uintptr_t)positions & 3) || ((uintptr_t)logits & 3) ||
       ((uintptr_t)next_tokens & 3))
     return fail(m, LD_EINVAL, "unaligned pointer");
-  return enqueue_step(m, tokens, batch, positions, logits, next_tokens,
+  return enqueue_step(m, tokens, batch, 1, positions, logits, next_tokens,
                       static_cast<hipStream_t>(stream));
+}
+
+extern "C" ld_status ld_decode_step_tokens(ld_model* m, const int32_t* tokens,
+                                           int32_t tokens_per_seq, int32_t batch,
+                                           const int32_t* positions, float* logits,
+                                           int32_t* next_tokens, void* stream) {
+  if (!m) return fail(nullptr, LD_EINVAL, "null model");
+  if (!m->kv_ready) return fail(m, LD_ESTATE, "ld_alloc_kv first");
+  if (tokens_per_seq < 1) return fail(m, LD_EINVAL, "tokens_per_seq must be >= 1");
+  if (batch < 1 || (int64_t)batch * tokens_per_seq > m->D.max_batch)
+    return fail(m, LD_EINVAL, "batch * tokens_per_seq outside [1, max_batch]");
+  if (!tokens || !positions || !logits) return fail(m, LD_EINVAL, "null tokens, positions or logits");
+  if (((uintptr_t)tokens & 3) || ((uintptr_t)positions & 3) || ((uintptr_t)logits & 3) ||
+      ((uintptr_t)next_tokens & 3))
+    return fail(m, LD_EINVAL, "unaligned pointer");
+  return enqueue_step(m, tokens, batch * tokens_per_seq, tokens_per_seq, positions, logits,
+                      next_tokens, static_cast<hipStream_t>(stream));
 }
 
 extern "C" ld_status ld_device_error(ld_model* m) {

@@ -95,6 +95,8 @@ struct Step {
   uint32_t inject;  // debug: added to one wait target to force a watchdog timeout
   uint32_t x_cap;   // bytes of LDS for staged input vectors
   int T;            // attention split length of this step (<= Dims::split_len)
+  int M;            // tokens per sequence: rows b*M .. b*M + M - 1 are sequence b's
+                    // consecutive positions (KV cache slot b); 1 for a decode step
 };
 
 struct Params {

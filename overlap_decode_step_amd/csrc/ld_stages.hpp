@@ -95,6 +95,9 @@ __device__ __forceinline__ void stage_qkv(const Params& P, int l, int wg, int nw
     const int t = P.S.tokens[tid()], p = P.S.pos[tid()];
     if ((unsigned)t >= (unsigned)D.V) raise_error(P.K.err, kErrToken);
     if ((unsigned)p >= (unsigned)D.max_seq) raise_error(P.K.err, kErrPos);
+    // a sequence's tokens take consecutive positions
+    const int j = tid() % P.S.M;
+    if (j > 0 && p != P.S.pos[tid() - j] + j) raise_error(P.K.err, kErrPos);
   }
   trace_ev(P, l, kSQkv, 0, wg);
   auto wait = [&]() {
@@ -171,8 +174,10 @@ __host__ __device__ constexpr size_t attn_smem_bytes(int group, int d, int T, in
          + (size_t)group * 2 * 4;                                  /* (max, sum) per head */
 }
 
+// Row b of the step (token j = b % M of sequence slot = b / M, at position
+// p = p0 + j, where p0 is the sequence's first position of this step).
 struct AttnItem {
-  int b, kvh, s, ns, p;
+  int b, kvh, s, ns, p, slot, p0;
 };
 
 constexpr int kCombBatch = 16;  // splits combined from registers in one round of loads
@@ -181,10 +186,15 @@ constexpr int kCombBatch = 16;  // splits combined from registers in one round o
 __device__ __forceinline__ bool attn_item_at(const Params& P, const Scratch& sc, int T, int it,
                                              AttnItem& a) {
   int base = 0;
+  const int M = P.S.M;
   for (int b = 0; b < P.S.B; ++b) {
-    const int p = sc.pos[b], ns = (p + T) / T, cnt = P.D.nkv * ns;
+    const int slot = b / M, p0 = sc.pos[slot * M];
+    const int p = min(p0 + (b - slot * M), P.D.max_seq - 1);
+    const int ns = (p + T) / T, cnt = P.D.nkv * ns;
     if (it < base + cnt) {
       a.b = b;
+      a.slot = slot;
+      a.p0 = p0;
       a.p = p;
       a.ns = ns;
       a.kvh = (it - base) / ns;
@@ -234,11 +244,11 @@ __device__ __forceinline__ void attn_copy_tiles(const Params& P, int l, const At
   const AttnLds s = attn_lds(D, smem);
   const int len = a.p + 1;
   const int n0 = (a.s * len) / a.ns, n1 = ((a.s + 1) * len) / a.ns;
-  const int ncached = (n1 == len) ? n1 - n0 - 1 : n1 - n0;
+  const int ncached = max(0, min(n1, a.p0) - n0);  // rows before this step's tokens
   const int bytes = ncached * D.d * 2;
   const int nw = nwaves(), w0 = (skip_wave0 && nw > 1) ? 1 : 0, w = wave_id(), lane = lane_id();
   if (w < w0 || bytes <= 0) return;
-  const int64_t off = attn_cache_off(P, l, a.b, a.kvh) + (int64_t)n0 * D.d;
+  const int64_t off = attn_cache_off(P, l, a.slot, a.kvh) + (int64_t)n0 * D.d;
   const char* ksrc = reinterpret_cast<const char*>(P.K.kc + off);
   const char* vsrc = reinterpret_cast<const char*>(P.K.vc + off);
   const int chunks = (bytes + 1023) >> 10;
@@ -265,15 +275,21 @@ __device__ __forceinline__ void attn_item(const Params& P, int l, const AttnItem
   const int len = p + 1;
   const int n0 = (a.s * len) / nsplit, n1 = ((a.s + 1) * len) / nsplit;
   const int n = n1 - n0;
-  const bool has_new = (n1 == len);
+  // positions [q_lo, n1) of the split belong to this step's tokens of the
+  // sequence: their k and v come from the QKV outputs of rows
+  // slot * M + (q - p0), not from the cache, and the sequence's last token
+  // appends them to the cache (each position is appended once)
+  const int M = P.S.M;
+  const int q_lo = max(n0, a.p0), nnew = max(0, n1 - q_lo);
+  const bool appends = (b - a.slot * M) == M - 1;
   const float* qkv = P.K.qkv + (int64_t)b * D.qkv_rows;
   const float* rope = P.K.rope + (int64_t)p * half * 2;
-  const int64_t cache_off = attn_cache_off(P, l, b, kvh);
+  const int64_t cache_off = attn_cache_off(P, l, a.slot, kvh);
   uint16_t* kc = P.K.kc + cache_off;
   uint16_t* vc = P.K.vc + cache_off;
 
   // ---- q heads of this group (one (head, pair) per thread: group * half <=
-  // 512) and, in the split holding p, the new k and v
+  // 512) and the split's new k and v rows
   trace_ev(P, l, 6, 0, blockIdx.x);
   const bool qthread = tid < group * half;
   const int qg = tid >> (ld - 1), qi = tid & (half - 1);
@@ -285,33 +301,33 @@ __device__ __forceinline__ void attn_item(const Params& P, int l, const AttnItem
     cq = rope[2 * qi];
     sq = rope[2 * qi + 1];
   }
-  float k0 = 0.f, k1 = 0.f, v0 = 0.f, v1 = 0.f;
-  const bool newrow = has_new && tid < half;
-  if (newrow) {
-    const float* kh = qkv + D.qd + (int64_t)kvh * d;
-    const float* vh = kh + D.kvd;
-    k0 = ld_coh(kh + tid);
-    k1 = ld_coh(kh + tid + half);
-    v0 = ld_coh(vh + tid);
-    v1 = ld_coh(vh + tid + half);
-  }
   if (qthread) {  // rotate q (rotate-half pairs) into LDS
     s.qs[qg * d + qi] = q0 * cq - q1 * sq;
     s.qs[qg * d + qi + half] = q0 * sq + q1 * cq;
   }
-  if (newrow) {
-    // rotate the new key, round k and v to bf16, append them to the cache at p
-    // (thread tid < half holds pair tid, whose cos/sin it loaded as a q thread)
-    const uint16_t ka = f2bf(k0 * cq - k1 * sq), kb = f2bf(k0 * sq + k1 * cq);
+  // new row e (position q = q_lo + e), pair i: rotate the key at q, round k
+  // and v to bf16, place them in the tiles (and append them to the cache)
+  for (int e = tid / half; e < nnew; e += nth / half) {
+    const int i = tid & (half - 1), q = q_lo + e;
+    const float* kh = P.K.qkv + (int64_t)(a.slot * M + (q - a.p0)) * D.qkv_rows + D.qd +
+                      (int64_t)kvh * d;
+    const float* vh = kh + D.kvd;
+    const float* rq = P.K.rope + (int64_t)q * half * 2;
+    const float k0 = ld_coh(kh + i), k1 = ld_coh(kh + i + half);
+    const float v0 = ld_coh(vh + i), v1 = ld_coh(vh + i + half);
+    const float c = rq[2 * i], sn = rq[2 * i + 1];
+    const uint16_t ka = f2bf(k0 * c - k1 * sn), kb = f2bf(k0 * sn + k1 * c);
     const uint16_t va = f2bf(v0), vb = f2bf(v1);
-    kc[(int64_t)p * d + tid] = ka;
-    kc[(int64_t)p * d + tid + half] = kb;
-    vc[(int64_t)p * d + tid] = va;
-    vc[(int64_t)p * d + tid + half] = vb;
-    s.Ks[(n - 1) * d + tid] = ka;
-    s.Ks[(n - 1) * d + tid + half] = kb;
-    s.Vs[(n - 1) * d + tid] = va;
-    s.Vs[(n - 1) * d + tid + half] = vb;
+    if (appends) {
+      kc[(int64_t)q * d + i] = ka;
+      kc[(int64_t)q * d + i + half] = kb;
+      vc[(int64_t)q * d + i] = va;
+      vc[(int64_t)q * d + i + half] = vb;
+    }
+    s.Ks[(q - n0) * d + i] = ka;
+    s.Ks[(q - n0) * d + i + half] = kb;
+    s.Vs[(q - n0) * d + i] = va;
+    s.Vs[(q - n0) * d + i + half] = vb;
   }
   wave_drain();  // direct-to-LDS copies have landed
   __syncthreads();

@@ -50,6 +50,7 @@ def _load():
         "ld_fill_kv": (S, [P, U64, F, P, P]),
         "ld_set_mode": (S, [P, S]),
         "ld_decode_step": (S, [P, P, I32, P, P, P, P]),
+        "ld_decode_step_tokens": (S, [P, P, I32, I32, P, P, P, P]),
         "ld_tune": (S, [P, P, I32, ctypes.c_char_p]),
         "ld_load_tuning": (S, [P, ctypes.c_char_p]),
         "ld_device_error": (S, [P]),
@@ -120,6 +121,12 @@ def ld_set_mode(m, mode):
 
 def ld_decode_step(m, tokens, batch, positions, logits, next_tokens, stream=0):
     return _check(LIB.ld_decode_step(m, tokens, batch, positions, logits, next_tokens, stream), m)
+
+
+def ld_decode_step_tokens(m, tokens, tokens_per_seq, batch, positions, logits, next_tokens,
+                          stream=0):
+    return _check(LIB.ld_decode_step_tokens(m, tokens, tokens_per_seq, batch, positions, logits,
+                                            next_tokens, stream), m)
 
 
 def ld_tune(m, batches, table_path=None):
@@ -240,6 +247,15 @@ class Model:
         B = int(tokens.numel())
         ld_decode_step(self.h, tokens.data_ptr(), B, positions.data_ptr(), logits.data_ptr(),
                        next_tokens.data_ptr() if next_tokens is not None else None, self.stream())
+
+    def step_tokens(self, tokens, tokens_per_seq, positions, logits, next_tokens=None):
+        """tokens/positions: cuda int32 [B * M] (row b * M + j: token j of
+        sequence b); logits: cuda float32 [B * M, vocab]."""
+        rows = int(tokens.numel())
+        ld_decode_step_tokens(self.h, tokens.data_ptr(), tokens_per_seq, rows // tokens_per_seq,
+                              positions.data_ptr(), logits.data_ptr(),
+                              next_tokens.data_ptr() if next_tokens is not None else None,
+                              self.stream())
 
     def device_error(self):
         return ld_device_error(self.h)

@@ -385,6 +385,90 @@ def test_full_depth_properties(ld, name, w_std, batches):
     m.free()
 
 
+# ----------------------------------------- several tokens per sequence
+
+MULTI_CASES = [("tiny", [128, 40], 4, 0.02), ("ragged", [1100], 5, 0.05), ("llama1b", [512], 16, 0.02)]
+_multi_refs = {}  # oracle references per case, shared by the modes
+
+
+def _multi_token_refs(orc, name, shape, prefill, M, w_std, toks, maxs):
+    """The oracle's teacher-forced decode of each sequence's M tokens, then of
+    one more token (the greedy next of token M - 1) at position p0 + M."""
+    if name not in _multi_refs:
+        om = orc.model(shape, seed=W.SEED_WEIGHTS, w_std=w_std)
+        rows, extra = [], []
+        for b, p0 in enumerate(prefill):
+            okv = orc.kv(shape, 1, maxs, seed=W.SEED_KV, kv_std=1.0, prefill=[p0], seq0=b)
+            for j in range(M):
+                rows.append(orc.decode_one(om, okv, 0, toks[b * M + j], p0 + j))
+            nxt = int(rows[-1][1])
+            extra.append((nxt,) + tuple(orc.decode_one(om, okv, 0, nxt, p0 + M)))
+        _multi_refs[name] = (rows, extra)
+    return _multi_refs[name]
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("name,prefill,M,w_std", MULTI_CASES, ids=[c[0] for c in MULTI_CASES])
+def test_multi_token_step(ld, orc, name, prefill, M, w_std, mode):
+    # M consecutive tokens per sequence in one step (token j attends to the
+    # cache plus the step's tokens 0..j) equal M single-token steps in order:
+    # every row against the oracle's teacher-forced decode, then one more
+    # single-token step that reads the K/V rows the multi-token step appended.
+    # The tiny case has 8 rows (VALU engine), the ragged one splits up to 1105
+    # positions three ways (group 3), Llama-1B has 16 rows (MFMA engine).
+    import torch
+    shape = RAGGED if name == "ragged" else W.SHAPES[name]
+    B = len(prefill)
+    rows = B * M
+    maxs = max(prefill) + M + 8
+    toks = W.first_tokens(rows, shape["vocab"])
+    refs, extra = _multi_token_refs(orc, name, shape, prefill, M, w_std, toks, maxs)
+    m = gpu_model(ld, shape, rows, maxs, prefill + [1] * (rows - B), w_std=w_std)
+    m.set_mode(mode)
+    dev = torch.device("cuda:0")
+    pos = [prefill[b] + j for b in range(B) for j in range(M)]
+    t = torch.tensor(toks, dtype=torch.int32, device=dev)
+    p = torch.tensor(pos, dtype=torch.int32, device=dev)
+    lg = torch.empty((rows, shape["vocab"]), dtype=torch.float32, device=dev)
+    nx = torch.empty(rows, dtype=torch.int32, device=dev)
+    m.step_tokens(t, M, p, lg, nx)
+    torch.cuda.synchronize()
+    assert m.device_error() == 0
+    lg_h, nx_h = lg.cpu().numpy(), nx.cpu().numpy()
+    for b in range(B):
+        for j in range(M):
+            r = b * M + j
+            ref, rn = refs[r]
+            err, rel, _ = check_row(lg_h[r], ref, nx_h[r], rn, f"{name} mode={mode} seq={b} token={j}")
+        print(f"{name} M={M} mode={mode} seq={b} last-token max_abs={err:.2e} rel={rel:.2e}", flush=True)
+    # one more token per sequence (the oracle's greedy next), attending to the
+    # rows the multi-token step appended
+    run = GpuRunner(m, shape["vocab"], rows)
+    nxt = [extra[b][0] for b in range(B)]
+    lg2, nx2 = run.step(nxt, [prefill[b] + M for b in range(B)])
+    for b in range(B):
+        _, ref, rn = extra[b]
+        check_row(lg2[b], ref, nx2[b], rn, f"{name} mode={mode} seq={b} after the chunk")
+    m.free()
+
+
+def test_multi_token_positions_must_be_consecutive(ld):
+    import torch
+    shape = W.TINY
+    m = gpu_model(ld, shape, 4, 64, [10, 10, 10, 10])
+    dev = torch.device("cuda:0")
+    lg = torch.empty((4, shape["vocab"]), dtype=torch.float32, device=dev)
+    t = torch.tensor([3, 4, 5, 6], dtype=torch.int32, device=dev)
+    m.step_tokens(t, 4, torch.tensor([10, 11, 13, 14], dtype=torch.int32, device=dev), lg)
+    assert m.device_error() == ld.LD_EDEVICE
+    m.step_tokens(t, 4, torch.tensor([10, 11, 12, 13], dtype=torch.int32, device=dev), lg)
+    assert m.device_error() == ld.LD_OK
+    with pytest.raises(ld.LdError) as ei:
+        m.step_tokens(torch.zeros(5 * 1, dtype=torch.int32, device=dev), 5, torch.zeros(5, dtype=torch.int32, device=dev), lg)
+    assert ei.value.status == ld.LD_EINVAL  # 5 rows > max_batch 4
+    m.free()
+
+
 # --------------------------------------------- unfused-MLP ablation
 
 @pytest.mark.parametrize("name,B", [("tiny", 1), ("tiny", 3), ("llama1b", 1)])
