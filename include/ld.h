@@ -155,7 +155,9 @@ ld_status ld_decode_step(ld_model* m, const int32_t* tokens, int32_t batch,
  * are appended.  The result equals tokens_per_seq single-token steps in
  * order (teacher forced).  batch * tokens_per_seq must be in
  * [1, max_batch] and tokens_per_seq >= 1 (LD_EINVAL otherwise); 16 rows and
- * more run on the MFMA engine.  tokens_per_seq = 1 is ld_decode_step. */
+ * more run on the MFMA engine.  tokens_per_seq = 1 is ld_decode_step.  The
+ * persistent kernel is built for decode steps only: tokens_per_seq > 1 in
+ * LD_MODE_MEGA returns LD_EINVAL. */
 ld_status ld_decode_step_tokens(ld_model* m, const int32_t* tokens, int32_t tokens_per_seq,
                                 int32_t batch, const int32_t* positions, float* logits,
                                 int32_t* next_tokens, void* stream);

@@ -695,6 +695,8 @@ extern "C" ld_status ld_decode_step_tokens(ld_model* m, const int32_t* tokens,
   if (!m) return fail(nullptr, LD_EINVAL, "null model");
   if (!m->kv_ready) return fail(m, LD_ESTATE, "ld_alloc_kv first");
   if (tokens_per_seq < 1) return fail(m, LD_EINVAL, "tokens_per_seq must be >= 1");
+  if (tokens_per_seq > 1 && m->mode == LD_MODE_MEGA)
+    return fail(m, LD_EINVAL, "several tokens per sequence need the wait, tile-flag or graph mode");
   if (batch < 1 || (int64_t)batch * tokens_per_seq > m->D.max_batch)
     return fail(m, LD_EINVAL, "batch * tokens_per_seq outside [1, max_batch]");
   if (!tokens || !positions || !logits) return fail(m, LD_EINVAL, "null tokens, positions or logits");

@@ -32,7 +32,7 @@ __global__ __launch_bounds__(kMaxThreads, kStageWavesPerSimd) void k_qkv(Params 
 __global__ __launch_bounds__(kMaxThreads, kStageWavesPerSimd) void k_attn(Params P, int l) {
   extern __shared__ __align__(16) char smem[];
   scratch_init(smem);
-  stage_attn(P, l, blockIdx.x, gridDim.x, smem, [] {});
+  stage_attn<true>(P, l, blockIdx.x, gridDim.x, smem, [] {});
 }
 
 template <int NB>
@@ -106,7 +106,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_mega(Params P0) {
     int gnl = 0;
     {
       const Params P = fresh_params();
-      stage_attn(P, l, wg, nwg, smem, [&] {
+      stage_attn<false>(P, l, wg, nwg, smem, [&] {
         if constexpr (NB < kMfmaMinBatch) {
           gnl = gu_prefetch<NB>(P, l, wg, nwg, gring, smem);
           gpre = true;

@@ -183,10 +183,14 @@ struct AttnItem {
 constexpr int kCombBatch = 16;  // splits combined from registers in one round of loads
 
 // Item `it` of the step (sequence-major, then kv head, then split).
+// MULTI: the step may hold several tokens per sequence (P.S.M > 1); the
+// persistent kernel is built without it (decode steps only), which keeps its
+// scalar registers from spilling.
+template <bool MULTI>
 __device__ __forceinline__ bool attn_item_at(const Params& P, const Scratch& sc, int T, int it,
                                              AttnItem& a) {
   int base = 0;
-  const int M = P.S.M;
+  const int M = MULTI ? P.S.M : 1;
   for (int b = 0; b < P.S.B; ++b) {
     const int slot = b / M, p0 = sc.pos[slot * M];
     const int p = min(p0 + (b - slot * M), P.D.max_seq - 1);
@@ -263,6 +267,7 @@ __device__ __forceinline__ void attn_copy_tiles(const Params& P, int l, const At
   }
 }
 
+template <bool MULTI>
 __device__ __forceinline__ void attn_item(const Params& P, int l, const AttnItem& a, char* smem) {
   // head_dim is a power of two (checked on the host): index math uses shifts
   const Dims& D = P.D;
@@ -279,7 +284,7 @@ __device__ __forceinline__ void attn_item(const Params& P, int l, const AttnItem
   // sequence: their k and v come from the QKV outputs of rows
   // slot * M + (q - p0), not from the cache, and the sequence's last token
   // appends them to the cache (each position is appended once)
-  const int M = P.S.M;
+  const int M = MULTI ? P.S.M : 1;
   const int q_lo = max(n0, a.p0), nnew = max(0, n1 - q_lo);
   const bool appends = (b - a.slot * M) == M - 1;
   const float* qkv = P.K.qkv + (int64_t)b * D.qkv_rows;
@@ -293,31 +298,26 @@ __device__ __forceinline__ void attn_item(const Params& P, int l, const AttnItem
   trace_ev(P, l, 6, 0, blockIdx.x);
   const bool qthread = tid < group * half;
   const int qg = tid >> (ld - 1), qi = tid & (half - 1);
-  float q0 = 0.f, q1 = 0.f, cq = 0.f, sq = 0.f;
-  if (qthread) {
-    const float* qh = qkv + (int64_t)(kvh * group + qg) * d;
-    q0 = ld_coh(qh + qi);
-    q1 = ld_coh(qh + qi + half);
-    cq = rope[2 * qi];
-    sq = rope[2 * qi + 1];
-  }
-  if (qthread) {  // rotate q (rotate-half pairs) into LDS
-    s.qs[qg * d + qi] = q0 * cq - q1 * sq;
-    s.qs[qg * d + qi + half] = q0 * sq + q1 * cq;
-  }
-  // new row e (position q = q_lo + e), pair i: rotate the key at q, round k
-  // and v to bf16, place them in the tiles (and append them to the cache)
-  for (int e = tid / half; e < nnew; e += nth / half) {
-    const int i = tid & (half - 1), q = q_lo + e;
+  // new row e (position q = q_lo + e), pair i: its k, v and the cos/sin of q
+  const int rstep = nth / half, i = tid & (half - 1);
+  struct NewRow {
+    float k0, k1, v0, v1, c, sn;
+  };
+  auto load_row = [&](int e) {
+    const int q = q_lo + e;
     const float* kh = P.K.qkv + (int64_t)(a.slot * M + (q - a.p0)) * D.qkv_rows + D.qd +
                       (int64_t)kvh * d;
     const float* vh = kh + D.kvd;
     const float* rq = P.K.rope + (int64_t)q * half * 2;
-    const float k0 = ld_coh(kh + i), k1 = ld_coh(kh + i + half);
-    const float v0 = ld_coh(vh + i), v1 = ld_coh(vh + i + half);
-    const float c = rq[2 * i], sn = rq[2 * i + 1];
-    const uint16_t ka = f2bf(k0 * c - k1 * sn), kb = f2bf(k0 * sn + k1 * c);
-    const uint16_t va = f2bf(v0), vb = f2bf(v1);
+    return NewRow{ld_coh(kh + i), ld_coh(kh + i + half), ld_coh(vh + i), ld_coh(vh + i + half),
+                  rq[2 * i], rq[2 * i + 1]};
+  };
+  // rotate the key at q, round k and v to bf16, place them in the tiles (and
+  // append them to the cache)
+  auto store_row = [&](int e, const NewRow& w) {
+    const int q = q_lo + e;
+    const uint16_t ka = f2bf(w.k0 * w.c - w.k1 * w.sn), kb = f2bf(w.k0 * w.sn + w.k1 * w.c);
+    const uint16_t va = f2bf(w.v0), vb = f2bf(w.v1);
     if (appends) {
       kc[(int64_t)q * d + i] = ka;
       kc[(int64_t)q * d + i + half] = kb;
@@ -328,6 +328,42 @@ __device__ __forceinline__ void attn_item(const Params& P, int l, const AttnItem
     s.Ks[(q - n0) * d + i + half] = kb;
     s.Vs[(q - n0) * d + i] = va;
     s.Vs[(q - n0) * d + i + half] = vb;
+  };
+  // the q loads and the (first pass of) new rows share one round trip
+  float q0 = 0.f, q1 = 0.f, cq = 0.f, sq = 0.f;
+  if (qthread) {
+    const float* qh = qkv + (int64_t)(kvh * group + qg) * d;
+    q0 = ld_coh(qh + qi);
+    q1 = ld_coh(qh + qi + half);
+    cq = rope[2 * qi];
+    sq = rope[2 * qi + 1];
+  }
+  auto rotate_q = [&] {  // rotate q (rotate-half pairs) into LDS
+    if (qthread) {
+      s.qs[qg * d + qi] = q0 * cq - q1 * sq;
+      s.qs[qg * d + qi + half] = q0 * sq + q1 * cq;
+    }
+  };
+  if (!MULTI || M == 1) {
+    // a decode step: at most one new row, position p, in the last split;
+    // thread tid < half holds pair tid, whose cos/sin it loaded as a q thread
+    const bool newrow = (n1 == len) && tid < half;
+    NewRow w0{};
+    if (newrow) {
+      const float* kh = qkv + D.qd + (int64_t)kvh * d;
+      const float* vh = kh + D.kvd;
+      w0 = NewRow{ld_coh(kh + tid), ld_coh(kh + tid + half), ld_coh(vh + tid),
+                  ld_coh(vh + tid + half), cq, sq};
+    }
+    rotate_q();
+    if (newrow) store_row(p - q_lo, w0);
+  } else if constexpr (MULTI) {
+    const int e0 = tid / half;
+    NewRow w0{};
+    if (e0 < nnew) w0 = load_row(e0);
+    rotate_q();
+    if (e0 < nnew) store_row(e0, w0);
+    for (int e = e0 + rstep; e < nnew; e += rstep) store_row(e, load_row(e));
   }
   wave_drain();  // direct-to-LDS copies have landed
   __syncthreads();
@@ -494,7 +530,7 @@ __device__ __forceinline__ void attn_item(const Params& P, int l, const AttnItem
 // `idle_hook()` runs in a workgroup that has no attention item, once the
 // stage's input is ready (the persistent kernel issues the SwiGLU stage's
 // first weight loads there, while the memory system is otherwise quiet).
-template <class Hook>
+template <bool MULTI, class Hook>
 __device__ __forceinline__ void stage_attn(const Params& P, int l, int wg, int nwg, char* smem,
                            const Hook& idle_hook) {
   const Dims& D = P.D;
@@ -507,7 +543,7 @@ __device__ __forceinline__ void stage_attn(const Params& P, int l, int wg, int n
   }
   const int T = P.S.T;
   AttnItem a;
-  const bool any = attn_item_at(P, sc, T, wg, a);
+  const bool any = attn_item_at<MULTI>(P, sc, T, wg, a);
   // the first item's cached rows are copied while this stage's input is
   // still being produced
   if (any) attn_copy_tiles(P, l, a, smem, !P.S.wait);
@@ -516,10 +552,10 @@ __device__ __forceinline__ void stage_attn(const Params& P, int l, int wg, int n
   if (!any) idle_hook();
   if (any) {
     for (int it = wg;;) {
-      attn_item(P, l, a, smem);
+      attn_item<MULTI>(P, l, a, smem);
       __syncthreads();  // LDS is reused by the next item
       it += nwg;
-      if (!attn_item_at(P, sc, T, it, a)) break;
+      if (!attn_item_at<MULTI>(P, sc, T, it, a)) break;
       attn_copy_tiles(P, l, a, smem, false);
     }
   }

@@ -415,7 +415,8 @@ def test_multi_token_step(ld, orc, name, prefill, M, w_std, mode):
     # every row against the oracle's teacher-forced decode, then one more
     # single-token step that reads the K/V rows the multi-token step appended.
     # The tiny case has 8 rows (VALU engine), the ragged one splits up to 1105
-    # positions three ways (group 3), Llama-1B has 16 rows (MFMA engine).
+    # positions three ways (group 3), Llama-1B has 16 rows (MFMA engine).  The
+    # persistent kernel is built for decode steps only and refuses them.
     import torch
     shape = RAGGED if name == "ragged" else W.SHAPES[name]
     B = len(prefill)
@@ -431,6 +432,12 @@ def test_multi_token_step(ld, orc, name, prefill, M, w_std, mode):
     p = torch.tensor(pos, dtype=torch.int32, device=dev)
     lg = torch.empty((rows, shape["vocab"]), dtype=torch.float32, device=dev)
     nx = torch.empty(rows, dtype=torch.int32, device=dev)
+    if mode == "mega":  # the persistent kernel is built for decode steps only
+        with pytest.raises(ld.LdError) as ei:
+            m.step_tokens(t, M, p, lg, nx)
+        assert ei.value.status == ld.LD_EINVAL
+        m.free()
+        return
     m.step_tokens(t, M, p, lg, nx)
     torch.cuda.synchronize()
     assert m.device_error() == 0
@@ -456,6 +463,7 @@ def test_multi_token_positions_must_be_consecutive(ld):
     import torch
     shape = W.TINY
     m = gpu_model(ld, shape, 4, 64, [10, 10, 10, 10])
+    m.set_mode("wait")
     dev = torch.device("cuda:0")
     lg = torch.empty((4, shape["vocab"]), dtype=torch.float32, device=dev)
     t = torch.tensor([3, 4, 5, 6], dtype=torch.int32, device=dev)
