@@ -267,11 +267,15 @@ __device__ __forceinline__ void attn_copy_tiles(const Params& P, int l, const At
   }
 }
 
-template <bool MULTI>
+// G, DH: the GQA group and head_dim when known at compile time (0: read from
+// the dimensions); the arithmetic is the same either way, the known-shape
+// forms only fold the index math (slice bounds, lane groups) into constants.
+template <bool MULTI, int G = 0, int DH = 0>
 __device__ __forceinline__ void attn_item(const Params& P, int l, const AttnItem& a, char* smem) {
   // head_dim is a power of two (checked on the host): index math uses shifts
   const Dims& D = P.D;
-  const int d = D.d, half = d / 2, group = D.group, w8 = d / 8, T = D.split_len;
+  const int d = DH > 0 ? DH : D.d, half = d / 2, group = G > 0 ? G : D.group, w8 = d / 8;
+  const int T = D.split_len;
   const int ld = 31 - __builtin_clz(d), lw8 = ld - 3;
   const int tid = ld::tid(), nth = blockDim.x, lane = lane_id(), wave = wave_id();
   Scratch& sc = *reinterpret_cast<Scratch*>(smem);
@@ -550,9 +554,17 @@ __device__ __forceinline__ void stage_attn(const Params& P, int l, int wg, int n
   if (!P.S.wait) wg_wait(sync_of(P), stage_ctr(P, l, kCQkv), P.S.t_qkv + P.S.inject, kSAttn);
   trace_ev(P, l, kSAttn, 1, wg);
   if (!any) idle_hook();
+  // the shapes of the Llama-1B, 8B and 70B configurations run with their
+  // index math folded; any other shape takes the general form
+  auto run_item = [&](const AttnItem& a) {
+    if (D.group == 4 && D.d == 64) return attn_item<MULTI, 4, 64>(P, l, a, smem);
+    if (D.group == 4 && D.d == 128) return attn_item<MULTI, 4, 128>(P, l, a, smem);
+    if (D.group == 8 && D.d == 128) return attn_item<MULTI, 8, 128>(P, l, a, smem);
+    attn_item<MULTI>(P, l, a, smem);
+  };
   if (any) {
     for (int it = wg;;) {
-      attn_item<MULTI>(P, l, a, smem);
+      run_item(a);
       __syncthreads();  // LDS is reused by the next item
       it += nwg;
       if (!attn_item_at<MULTI>(P, sc, T, it, a)) break;
