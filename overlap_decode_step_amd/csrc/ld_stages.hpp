@@ -531,6 +531,11 @@ __device__ __forceinline__ void attn_item(const Params& P, int l, const AttnItem
   signal_if(P, stage_ctr(P, l, kCAttn), b * D.nkv + kvh);
 }
 
+template <int G, int DH>
+struct AttnShape {
+  static constexpr int g = G, dh = DH;
+};
+
 // `idle_hook()` runs in a workgroup that has no attention item, once the
 // stage's input is ready (the persistent kernel issues the SwiGLU stage's
 // first weight loads there, while the memory system is otherwise quiet).
@@ -554,22 +559,28 @@ __device__ __forceinline__ void stage_attn(const Params& P, int l, int wg, int n
   if (!P.S.wait) wg_wait(sync_of(P), stage_ctr(P, l, kCQkv), P.S.t_qkv + P.S.inject, kSAttn);
   trace_ev(P, l, kSAttn, 1, wg);
   if (!any) idle_hook();
-  // the shapes of the Llama-1B, 8B and 70B configurations run with their
-  // index math folded; any other shape takes the general form
-  auto run_item = [&](const AttnItem& a) {
-    if (D.group == 4 && D.d == 64) return attn_item<MULTI, 4, 64>(P, l, a, smem);
-    if (D.group == 4 && D.d == 128) return attn_item<MULTI, 4, 128>(P, l, a, smem);
-    if (D.group == 8 && D.d == 128) return attn_item<MULTI, 8, 128>(P, l, a, smem);
-    attn_item<MULTI>(P, l, a, smem);
-  };
-  if (any) {
+  // the item loop of one shape (the dispatch stays outside the loop, so each
+  // loop's hoisted index math is computed on its own path only)
+  auto items = [&](auto shape) {
     for (int it = wg;;) {
-      run_item(a);
+      attn_item<MULTI, decltype(shape)::g, decltype(shape)::dh>(P, l, a, smem);
       __syncthreads();  // LDS is reused by the next item
       it += nwg;
       if (!attn_item_at<MULTI>(P, sc, T, it, a)) break;
       attn_copy_tiles(P, l, a, smem, false);
     }
+  };
+  // the shapes of the Llama-1B, 8B and 70B configurations run with their
+  // index math folded; any other shape takes the general form
+  if (any) {
+    if (D.group == 4 && D.d == 64)
+      items(AttnShape<4, 64>{});
+    else if (D.group == 4 && D.d == 128)
+      items(AttnShape<4, 128>{});
+    else if (D.group == 8 && D.d == 128)
+      items(AttnShape<8, 128>{});
+    else
+      items(AttnShape<0, 0>{});
   }
   (void)D;
   trace_ev(P, l, kSAttn, 3, wg);
