@@ -603,16 +603,40 @@ __device__ __forceinline__ void stage_o(const Params& P, int l, int wg, int nwg,
     }
   };
   trace_ev(P, l, kSO, 0, wg);
-  auto wait = [&]() {
-    if (!P.S.wait) wg_wait(sync_of(P), stage_ctr(P, l, kCAttn), P.S.t_attn, kSO);
-    trace_ev(P, l, kSO, 1, wg);
-  };
   const XSrc src{P.K.ao, K, nullptr, nullptr, 0};
   // residual input: the layer input (the embedding row for layer 0)
   const float* xa = P.K.xa;
   const uint16_t* emb = P.W.embed;
   const int* tok = P.S.tokens;
   float* xb = P.K.xb;
+  auto residual = [&](int bb, int row) -> float {
+    if (l == 0) {
+      int tk = tok[bb];
+      tk = ((unsigned)tk < (unsigned)D.V) ? tk : 0;
+      return bf16f(emb[(int64_t)tk * D.H + row]);
+    }
+    return ld_coh(xa + (int64_t)bb * D.H + row);
+  };
+  // VALU engine: the residuals of this wave's first task are loaded before
+  // the readiness wait (the layer input is complete once this layer's QKV
+  // stage has run), so the epilogue does not wait for them
+  const int t0 = wg * nwaves() + wave_id();
+  float pre[NR][NB];
+  auto wait = [&]() {
+    if constexpr (NB < kMfmaMinBatch) {
+#pragma unroll
+      for (int r = 0; r < NR; ++r)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          const int row = t0 * NR + r;
+          pre[r][b] = (b < B && row < rows_total && lane == ((r * NB + b) & (kWave - 1)))
+                          ? residual(b, row)
+                          : 0.f;
+        }
+    }
+    if (!P.S.wait) wg_wait(sync_of(P), stage_ctr(P, l, kCAttn), P.S.t_attn, kSO);
+    trace_ev(P, l, kSO, 1, wg);
+  };
   auto epi = [&](int t, int b0, int nb, float (&acc)[NR][NB], Scratch&) {
 #pragma unroll
     for (int r = 0; r < NR; ++r)
@@ -621,14 +645,7 @@ __device__ __forceinline__ void stage_o(const Params& P, int l, int wg, int nwg,
         const int row = t * NR + r;
         if (b < nb && row < rows_total && lane == ((r * NB + b) & (kWave - 1))) {
           const int bb = b0 + b;
-          float res;
-          if (l == 0) {
-            int tk = tok[bb];
-            tk = ((unsigned)tk < (unsigned)D.V) ? tk : 0;
-            res = bf16f(emb[(int64_t)tk * D.H + row]);
-          } else {
-            res = ld_coh(xa + (int64_t)bb * D.H + row);
-          }
+          const float res = (t == t0 && b0 == 0) ? pre[r][b] : residual(bb, row);
           st_coh(xb + (int64_t)bb * D.H + row, res + acc[r][b]);
         }
       }
@@ -875,13 +892,29 @@ __device__ __forceinline__ void stage_d(const Params& P, int l, int wg, int nwg,
     }
   };
   trace_ev(P, l, kSD, 0, wg);
-  auto wait = [&]() {
-    if (!P.S.wait) wg_wait(sync_of(P), stage_ctr(P, l, kCGu), P.S.t_gu, kSD);
-    trace_ev(P, l, kSD, 1, wg);
-  };
   const XSrc src{P.K.hbuf, K, nullptr, nullptr, 0};
   const float* xb = P.K.xb;
   float* xa = P.K.xa;
+  // VALU engine: the residuals of this wave's first task (the O stage's
+  // output, complete before the SwiGLU stage this one waits for) are loaded
+  // before the readiness wait
+  const int t0 = wg * nwaves() + wave_id();
+  float pre[NR][NB];
+  auto wait = [&]() {
+    if constexpr (NB < kMfmaMinBatch) {
+#pragma unroll
+      for (int r = 0; r < NR; ++r)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          const int row = t0 * NR + r;
+          pre[r][b] = (b < B && row < rows_total && lane == ((r * NB + b) & (kWave - 1)))
+                          ? ld_coh(xb + (int64_t)b * D.H + row)
+                          : 0.f;
+        }
+    }
+    if (!P.S.wait) wg_wait(sync_of(P), stage_ctr(P, l, kCGu), P.S.t_gu, kSD);
+    trace_ev(P, l, kSD, 1, wg);
+  };
   auto epi = [&](int t, int b0, int nb, float (&acc)[NR][NB], Scratch&) {
 #pragma unroll
     for (int r = 0; r < NR; ++r)
@@ -890,7 +923,8 @@ __device__ __forceinline__ void stage_d(const Params& P, int l, int wg, int nwg,
         const int row = t * NR + r;
         if (b < nb && row < rows_total && lane == ((r * NB + b) & (kWave - 1))) {
           const int64_t o = (int64_t)(b0 + b) * D.H + row;
-          st_coh(xa + o, ld_coh(xb + o) + acc[r][b]);
+          const float res = (t == t0 && b0 == 0) ? pre[r][b] : ld_coh(xb + o);
+          st_coh(xa + o, res + acc[r][b]);
         }
       }
   };
