@@ -106,14 +106,17 @@ __device__ __forceinline__ void stage_qkv(const Params& P, int l, int wg, int nw
   };
   const XSrc src{l == 0 ? nullptr : P.K.xa, K, P.W.embed, P.S.tokens, D.V};
   float* out = P.K.qkv;
+  static_assert(NR * NB <= kWave, "one task's results take one lane each");
+  HeldStores<(NB > 1)> held;
   auto epi = [&](int t, int b0, int nb, float (&acc)[NR][NB], Scratch& sc) {
+    const int base = held.reserve(NR * NB);
 #pragma unroll
     for (int r = 0; r < NR; ++r)
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
         const int row = t * NR + r;
-        if (b < nb && row < rows_total && lane == ((r * NB + b) & (kWave - 1)))
-          st_coh(out + (int64_t)(b0 + b) * rows_total + row, acc[r][b] * sc.rs[b]);
+        if (b < nb && row < rows_total && lane == base + r * NB + b)
+          held.hold(out + (int64_t)(b0 + b) * rows_total + row, acc[r][b] * sc.rs[b]);
       }
   };
   const uint32_t wbytes = (uint32_t)((int64_t)rows_total * K * 2);
@@ -130,6 +133,7 @@ __device__ __forceinline__ void stage_qkv(const Params& P, int l, int wg, int nw
     gemv_stage<NR, UC, NB, kPfQkv>(rowfn, (rows_total + NR - 1) / NR, K, Wm, wbytes, src,
                                    layer_w(P, l, P.W.o_attn_norm), true, D.eps, B,
                                    batch_tile(P, K, NB), wait, epi, wg, nwg, smem);
+    held.flush();
   }
   trace_ev(P, l, kSQkv, 2, wg);
   signal_if(P, stage_ctr(P, l, kCQkv), wg);
@@ -637,16 +641,18 @@ __device__ __forceinline__ void stage_o(const Params& P, int l, int wg, int nwg,
     if (!P.S.wait) wg_wait(sync_of(P), stage_ctr(P, l, kCAttn), P.S.t_attn, kSO);
     trace_ev(P, l, kSO, 1, wg);
   };
+  HeldStores<(NB > 1)> held;
   auto epi = [&](int t, int b0, int nb, float (&acc)[NR][NB], Scratch&) {
+    const int base = held.reserve(NR * NB);
 #pragma unroll
     for (int r = 0; r < NR; ++r)
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
         const int row = t * NR + r;
-        if (b < nb && row < rows_total && lane == ((r * NB + b) & (kWave - 1))) {
+        if (b < nb && row < rows_total && lane == base + r * NB + b) {
           const int bb = b0 + b;
           const float res = (t == t0 && b0 == 0) ? pre[r][b] : residual(bb, row);
-          st_coh(xb + (int64_t)bb * D.H + row, res + acc[r][b]);
+          held.hold(xb + (int64_t)bb * D.H + row, res + acc[r][b]);
         }
       }
   };
@@ -671,6 +677,7 @@ __device__ __forceinline__ void stage_o(const Params& P, int l, int wg, int nwg,
   } else {
     gemv_stage<NR, UC, NB, kPfO>(rowfn, (rows_total + NR - 1) / NR, K, Wm, wbytes, src, nullptr,
                                  false, D.eps, B, batch_tile(P, K, NB), wait, epi, wg, nwg, smem);
+    held.flush();
   }
   trace_ev(P, l, kSO, 2, wg);
   signal_if(P, stage_ctr(P, l, kCO), wg);
@@ -760,15 +767,17 @@ __device__ __forceinline__ void stage_gu(const Params& P, int l, int wg, int nwg
   };
   const XSrc src{P.K.xb, K, nullptr, nullptr, 0};
   float* h = P.K.hbuf;
+  HeldStores<(NB > 1)> held;
   auto epi = [&](int t, int b0, int nb, float (&acc)[NR][NB], Scratch& sc) {
+    const int base = held.reserve(NP * NB);
 #pragma unroll
     for (int r = 0; r < NP; ++r)
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
         const int row = t * NP + r;
-        if (b < nb && row < I && lane == ((r * NB + b) & (kWave - 1))) {
+        if (b < nb && row < I && lane == base + r * NB + b) {
           const float a = acc[r][b] * sc.rs[b], u = acc[NP + r][b] * sc.rs[b];
-          st_coh(h + (int64_t)(b0 + b) * I + row, a / (1.0f + expf(-a)) * u);
+          held.hold(h + (int64_t)(b0 + b) * I + row, a / (1.0f + expf(-a)) * u);
         }
       }
   };
@@ -793,6 +802,7 @@ __device__ __forceinline__ void stage_gu(const Params& P, int l, int wg, int nwg
                                    D.eps, B, bw, wait, epi, smem,
                                    lds_blocks > 0 ? gu_lds_base(P, smem, lds_blocks) : nullptr,
                                    lds_blocks);
+    held.flush();
   }
   trace_ev(P, l, kSGu, 2, wg);
   signal_if(P, stage_ctr(P, l, kCGu), wg);
@@ -830,34 +840,42 @@ __device__ __forceinline__ void stage_mlp_proj(const Params& P, int l, int which
     constexpr int NP = kPairsGu, NR = 2 * kPairsGu;
     const GuRows rows = gu_rows(P, l);
     const GuStream ws(rows, gu_tiles(P), K, base, bytes, wg, nwg);
+    HeldStores<(NB > 1)> held_g, held_u;  // the stores wait for the end of the stream, as in the fused stage
     auto epi = [&](int t, int b0, int nb, float (&acc)[NR][NB], Scratch& sc) {
+      const int base = held_g.reserve(NP * NB);
+      held_u.reserve(NP * NB);
 #pragma unroll
       for (int r = 0; r < NP; ++r)
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
           const int row = t * NP + r;
-          if (b < nb && row < I && lane == ((r * NB + b) & (kWave - 1))) {
-            st_coh(P.K.gbuf + (int64_t)(b0 + b) * I + row, acc[r][b] * sc.rs[b]);
-            st_coh(P.K.ubuf + (int64_t)(b0 + b) * I + row, acc[NP + r][b] * sc.rs[b]);
+          if (b < nb && row < I && lane == base + r * NB + b) {
+            held_g.hold(P.K.gbuf + (int64_t)(b0 + b) * I + row, acc[r][b] * sc.rs[b]);
+            held_u.hold(P.K.ubuf + (int64_t)(b0 + b) * I + row, acc[NP + r][b] * sc.rs[b]);
           }
         }
     };
     GuBlock ring[kPfGu];
     gemv_run<NR, kUcGu, NB, kPfGu>(ws, ring, false, src, gain, true, D.eps, B, bw, nowait, epi, smem);
+    held_g.flush();
+    held_u.flush();
   } else {
     const uint16_t* Wm = which == kMlpGate ? layer_w(P, l, P.W.o_wg) : layer_w(P, l, P.W.o_wu);
     float* out = which == kMlpGate ? P.K.gbuf : P.K.ubuf;
     auto rowfn = [&](int t, const uint16_t* (&rows)[1]) {
       rows[0] = t < I ? Wm + (int64_t)t * K : nullptr;
     };
+    HeldStores<(NB > 1)> held;
     auto epi = [&](int t, int b0, int nb, float (&acc)[1][NB], Scratch& sc) {
+      const int base = held.reserve(NB);
 #pragma unroll
       for (int b = 0; b < NB; ++b)
-        if (b < nb && t < I && lane == (b & (kWave - 1)))
-          st_coh(out + (int64_t)(b0 + b) * I + t, acc[0][b] * sc.rs[b]);
+        if (b < nb && t < I && lane == base + b)
+          held.hold(out + (int64_t)(b0 + b) * I + t, acc[0][b] * sc.rs[b]);
     };
     gemv_stage<1, kUcGu, NB, kPfGu>(rowfn, I, K, base, bytes, src, gain, true, D.eps, B, bw, nowait,
                                     epi, wg, nwg, smem);
+    held.flush();
   }
 }
 
@@ -915,16 +933,18 @@ __device__ __forceinline__ void stage_d(const Params& P, int l, int wg, int nwg,
     if (!P.S.wait) wg_wait(sync_of(P), stage_ctr(P, l, kCGu), P.S.t_gu, kSD);
     trace_ev(P, l, kSD, 1, wg);
   };
+  HeldStores<(NB > 1)> held;
   auto epi = [&](int t, int b0, int nb, float (&acc)[NR][NB], Scratch&) {
+    const int base = held.reserve(NR * NB);
 #pragma unroll
     for (int r = 0; r < NR; ++r)
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
         const int row = t * NR + r;
-        if (b < nb && row < rows_total && lane == ((r * NB + b) & (kWave - 1))) {
+        if (b < nb && row < rows_total && lane == base + r * NB + b) {
           const int64_t o = (int64_t)(b0 + b) * D.H + row;
           const float res = (t == t0 && b0 == 0) ? pre[r][b] : ld_coh(xb + o);
-          st_coh(xa + o, res + acc[r][b]);
+          held.hold(xa + o, res + acc[r][b]);
         }
       }
   };
@@ -942,6 +962,7 @@ __device__ __forceinline__ void stage_d(const Params& P, int l, int wg, int nwg,
   } else {
     gemv_stage<NR, UC, NB, kPfD>(rowfn, (rows_total + NR - 1) / NR, K, Wm, wbytes, src, nullptr,
                                  false, D.eps, B, batch_tile(P, K, NB), wait, epi, wg, nwg, smem);
+    held.flush();
   }
   trace_ev(P, l, kSD, 2, wg);
   signal_if(P, stage_ctr(P, l, kCD), wg);
