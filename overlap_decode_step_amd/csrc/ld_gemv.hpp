@@ -40,6 +40,10 @@ struct XSrc {
   const uint16_t* emb;  // [V][ldx] bf16 when x == nullptr
   const int* tokens;    // [B]
   int V;
+  // MFMA engine only: x holds each value as its split-bf16 pair (the
+  // producer wrote split_pair(v)), staged as copied, with no conversion pass;
+  // only for inputs without an RMSNorm gain or norm
+  bool pairs = false;
 
   __device__ __forceinline__ void raw8(int b, int k, float* o) const {
     if (x) {

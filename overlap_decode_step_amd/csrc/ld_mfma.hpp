@@ -31,6 +31,16 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
+// x as the packed pair (bf16(x) | bf16(x - bf16(x)) << 16), both halves
+// rounded to nearest even by the hardware conversion: the form in which the
+// engine stages its inputs.  Producers feeding an MFMA stage directly write
+// this form, so the stage copies it without a conversion pass.
+__device__ __forceinline__ uint32_t split_pair(float x) {
+  const float hi = (float)(__bf16)x;
+  const bf16x2 hl = {(__bf16)x, (__bf16)(x - hi)};
+  return __builtin_bit_cast(uint32_t, hl);
+}
+
 constexpr int kMfmaTileMats = 2;   // 16-row tiles x matrices a wave accumulates at once
 // K steps of weight fragments in flight per wave: the persistent kernel has
 // 256 VGPRs per wave, the stage kernels 128
@@ -169,6 +179,17 @@ __device__ __forceinline__ void mfma_stage(const MatRows& mr, int ntile, int K, 
       }
       wave_drain();
       __syncthreads();
+      if (src.pairs) {
+        // already split-bf16 pairs: only the columns of the last 32-wide K
+        // step past K (if K is not a multiple of 32) must read as zeros
+        const int kpad = min(KC, ((kn + 31) / 32) * 32);
+        for (int i = t; i < nb * (kpad - kn); i += nth) {
+          const int b = i / (kpad - kn), k = kn + (i - b * (kpad - kn));
+          xw[(size_t)b * ldx + k] = 0u;
+        }
+        if (kpad > kn) __syncthreads();
+        return;
+      }
     }
     // thread t takes 8-column group j = t % gpr of the rows h, h + tpc, ...
     // (h = t / gpr, tpc = threads per column group), so it loads its gain
@@ -215,12 +236,7 @@ __device__ __forceinline__ void mfma_stage(const MatRows& mr, int ntile, int K, 
       }
       uint32_t pr[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float x = v[i] * g8[i];
-        const float hi = (float)(__bf16)x;
-        const bf16x2 hl = {(__bf16)x, (__bf16)(x - hi)};
-        pr[i] = __builtin_bit_cast(uint32_t, hl);
-      }
+      for (int i = 0; i < 8; ++i) pr[i] = split_pair(v[i] * g8[i]);
       *reinterpret_cast<u32x4*>(w) = u32x4{pr[0], pr[1], pr[2], pr[3]};
       *reinterpret_cast<u32x4*>(w + 4) = u32x4{pr[4], pr[5], pr[6], pr[7]};
     }

@@ -178,6 +178,13 @@ __host__ __device__ constexpr size_t attn_smem_bytes(int group, int d, int T, in
          + (size_t)group * 2 * 4;                                  /* (max, sum) per head */
 }
 
+// Attention output for the O stage: fp32 for the VALU engine, split-bf16
+// pairs when the step runs on the MFMA engine (16 rows and more), which then
+// stages them without a conversion pass.
+__device__ __forceinline__ void st_ao(const Params& P, float* p, float v) {
+  st_coh(p, P.S.B >= kMfmaMinBatch ? __uint_as_float(split_pair(v)) : v);
+}
+
 // Row b of the step (token j = b % M of sequence slot = b / M, at position
 // p = p0 + j, where p0 is the sequence's first position of this step).
 struct AttnItem {
@@ -469,7 +476,7 @@ __device__ __forceinline__ void attn_item(const Params& P, int l, const AttnItem
 #pragma unroll 4
     for (int sl = 0; sl < parts; ++sl) o += s.op[sl * gd + r];
     if (nsplit == 1) {
-      st_coh(out + r, o / s.ml[2 * g + 1]);
+      st_ao(P, out + r, o / s.ml[2 * g + 1]);
     } else {
       float* pp = P.K.part + (((int64_t)b * D.nq + kvh * group + g) * D.max_splits + a.s) * (d + 2);
       st_coh(pp + 2 + i, o);
@@ -529,7 +536,7 @@ __device__ __forceinline__ void attn_item(const Params& P, int l, const AttnItem
         L = fmaf(ld_coh(q + s0 * (d + 2) + 1), f, L);
         O = fmaf(ld_coh(q + s0 * (d + 2) + 2 + i), f, O);
       }
-      st_coh(out + r, O / L);
+      st_ao(P, out + r, O / L);
     }
   }
   signal_if(P, stage_ctr(P, l, kCAttn), b * D.nkv + kvh);
@@ -671,8 +678,9 @@ __device__ __forceinline__ void stage_o(const Params& P, int l, int wg, int nwg,
       }
       st_coh(xb + (int64_t)b * D.H + row, res + v[0]);
     };
+    const XSrc srcp{src.x, src.ldx, nullptr, nullptr, 0, true};  // split-bf16 pairs
     mfma_stage<kMfmaNbt<NB>, 1, MR>(MatRows{Wm, {Wm, Wm}, rows_total, K}, (rows_total + 15) / 16, K, Wm,
-                           wbytes, src, nullptr, false, D.eps, B, P.S.x_cap, wait, epe,
+                           wbytes, srcp, nullptr, false, D.eps, B, P.S.x_cap, wait, epe,
                            [](int, int) {}, wg, nwg, smem);
   } else {
     gemv_stage<NR, UC, NB, kPfO>(rowfn, (rows_total + NR - 1) / NR, K, Wm, wbytes, src, nullptr,
@@ -791,7 +799,8 @@ __device__ __forceinline__ void stage_gu(const Params& P, int l, int wg, int nwg
       const int row = tile * 16 + r;
       if (row >= I) return;
       const float a = v[0] * sc.rs[bl], u = v[1] * sc.rs[bl];
-      st_coh(h + (int64_t)b * I + row, a / (1.0f + expf(-a)) * u);
+      // the Down stage (MFMA engine too) stages h as split-bf16 pairs
+      st_coh(h + (int64_t)b * I + row, __uint_as_float(split_pair(a / (1.0f + expf(-a)) * u)));
     };
     mfma_stage<kMfmaNbt<NB>, 2, MR>(MatRows{layer_w(P, l, 0), {rows.Wg, rows.Wu}, I, K}, (I + 15) / 16, K,
                            layer_w(P, l, 0), (uint32_t)(P.W.layer_stride * 2), src,
@@ -956,8 +965,9 @@ __device__ __forceinline__ void stage_d(const Params& P, int l, int wg, int nwg,
       const int64_t o = (int64_t)b * D.H + row;
       st_coh(xa + o, ld_coh(xb + o) + v[0]);
     };
+    const XSrc srcp{src.x, src.ldx, nullptr, nullptr, 0, true};  // split-bf16 pairs
     mfma_stage<kMfmaNbt<NB>, 1, MR>(MatRows{Wm, {Wm, Wm}, rows_total, K}, (rows_total + 15) / 16, K, Wm,
-                           wbytes, src, nullptr, false, D.eps, B, P.S.x_cap, wait, epe,
+                           wbytes, srcp, nullptr, false, D.eps, B, P.S.x_cap, wait, epe,
                            [](int, int) {}, wg, nwg, smem);
   } else {
     gemv_stage<NR, UC, NB, kPfD>(rowfn, (rows_total + NR - 1) / NR, K, Wm, wbytes, src, nullptr,
