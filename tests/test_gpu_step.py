@@ -336,6 +336,24 @@ def test_wide_shapes_two_layers(ld, orc, name, w_std):
         for b, (lg_ref, nref) in refs.items():
             err, rel, _ = check_row(lg[b], lg_ref, nx[b], nref, f"{name} B={B} mode={mode} seq={b}")
             print(f"{name} x2 B={B} mode={mode} seq={b} max_abs={err:.2e} rel={rel:.2e}", flush=True)
+    # batch 8: the VALU engine's 8-row kernels, whose results are held in
+    # lane slots until a wave's stream ends; at the 70B width a SwiGLU wave has
+    # 14 tasks of 8 results, more than the 64 slots, so the held stores are
+    # also written mid-stream
+    B8 = 8
+    toks8 = W.first_tokens(B8, shape["vocab"])
+    refs8 = {}
+    for b in (0, B8 - 1):
+        okv_b = orc.kv(shape, 1, 1040, seed=W.SEED_KV, kv_std=1.0, prefill=[1024], seq0=b)
+        refs8[b] = orc.decode_one(om, okv_b, 0, toks8[b], 1024)
+    run8 = GpuRunner(m, shape["vocab"], B8)
+    for mode in ("wait", "mega"):
+        m.fill_kv(W.SEED_KV, 1.0, [1024] * B)
+        m.set_mode(mode)
+        lg, nx = run8.step(toks8, [1024] * B8)
+        for b, (lg_ref, nref) in refs8.items():
+            err, rel, _ = check_row(lg[b], lg_ref, nx[b], nref, f"{name} B={B8} mode={mode} seq={b}")
+            print(f"{name} x2 B={B8} mode={mode} seq={b} max_abs={err:.2e} rel={rel:.2e}", flush=True)
     m.free()
 
 
