@@ -58,6 +58,10 @@ struct ld_model {
   size_t smem_wait = 0, smem_flags = 0, smem_mega = 0;
   uint32_t xcap_wait = 0, xcap_flags = 0, xcap_mega = 0;
   bool flags_ok = true;
+  // attention split capacity of the whole-kernel-wait, graph and persistent
+  // modes (a full CU's LDS), used from 16 rows; the tile-flag mode and every
+  // step below 16 rows use D.split_len (half a CU's LDS)
+  int split_len_full = 0;
   uint64_t watchdog_ticks = 0;
   double wall_khz = 100000.0;
   uint32_t inject_next = 0;
@@ -384,7 +388,7 @@ static ld_status compute_grids(ld_model* m) {
   const uint32_t xcap_full = (uint32_t)((kLdsPerCu - scratch - best) / 256 * 256);
   if (kmax > xcap_full) return fail(m, LD_EINVAL, "input rows longer than the LDS staging area");
   m->xcap_wait = m->xcap_mega = xcap_full;
-  const size_t attn_full = attn_smem(D.group, D.d, D.split_len, D.max_splits);
+  const size_t attn_full = attn_smem(D.group, D.d, m->split_len_full, D.max_splits);
   m->smem_wait = m->smem_mega = scratch + std::max<size_t>(xcap_full + best, attn_full);
   if (m->smem_mega > kLdsPerCu) return fail(m, LD_EINVAL, "stage tiles do not fit in LDS");
   // tile-flag mode: two consecutive stage kernels share each CU, so each
@@ -460,6 +464,10 @@ extern "C" ld_status ld_alloc_kv(ld_model* m, void* dev_buf, size_t bytes, int32
   m->D.max_batch = max_batch;
   m->D.max_seq = max_seq;
   m->D.split_len = KL.split_len;
+  m->split_len_full = KL.split_len;
+  while (m->split_len_full + 32 <= 512 &&
+         scratch_bytes() + attn_smem(m->D.group, m->D.d, m->split_len_full + 32, KL.max_splits) <= kLdsPerCu)
+    m->split_len_full += 32;
   m->D.max_splits = KL.max_splits;
 
   // zero everything except the caches, then counters and error word
@@ -563,7 +571,11 @@ static ld_status enqueue_step(ld_model* m, const int32_t* tokens, int32_t B, int
   P.S.next = next;
   P.S.B = B;
   P.S.M = M;
-  P.S.T = step_split_len(m->D.split_len, B);
+  // split length: from 16 rows the modes with a full CU's LDS take longer
+  // splits (fewer items and partial results); below 16 rows every mode uses
+  // the same splits, so they add the same numbers in the same order
+  if (m->mode != LD_MODE_FLAGS) P.D.split_len = m->split_len_full;
+  P.S.T = step_split_len(B >= kMfmaMinBatch ? P.D.split_len : m->D.split_len, B);
   P.S.gu_variant = m->gu_variant[B];
   P.S.inject = m->inject_next;
   m->inject_next = 0;
