@@ -55,10 +55,11 @@ constexpr int kMfmaMinChunk = 512; // smallest K chunk (a wave's 64 lanes stage 
 constexpr int kSc1 = 16;           // cache policy: agent-coherent (sc1)
 
 // Batch tiles of 16 a wave accumulates at once for a kernel built for NB
-// batch rows: at most 2 (32 rows) within 128 VGPRs; larger batches take
-// several batch passes.
-template <int NB>
-constexpr int kMfmaNbt = NB / 16 < 2 ? NB / 16 : 2;
+// batch rows and a weight ring of MR steps: at most 2 (32 rows) within the
+// stage kernels' 128 VGPRs, 4 (64 rows) in the persistent kernel's 256;
+// larger batches take several batch passes, each streaming the weights again.
+template <int NB, int MR>
+constexpr int kMfmaNbt = MR == kMfmaRingBig ? (NB / 16 < 4 ? NB / 16 : 4) : (NB / 16 < 2 ? NB / 16 : 2);
 
 // LDS bytes per staged batch row: hi and lo bf16 halves of a chunk of `kc`
 // columns (plus padding), and the row's per-wave sums of squares (at most 16

@@ -126,7 +126,7 @@ __device__ __forceinline__ void stage_qkv(const Params& P, int l, int wg, int nw
       const int row = tile * 16 + r;
       if (row < rows_total) st_coh(out + (int64_t)b * rows_total + row, v[0] * sc.rs[bl]);
     };
-    mfma_stage<kMfmaNbt<NB>, 1, MR>(MatRows{Wm, {Wm, Wm}, rows_total, K}, (rows_total + 15) / 16, K, Wm,
+    mfma_stage<kMfmaNbt<NB, MR>, 1, MR>(MatRows{Wm, {Wm, Wm}, rows_total, K}, (rows_total + 15) / 16, K, Wm,
                            wbytes, src, layer_w(P, l, P.W.o_attn_norm), true, D.eps, B, P.S.x_cap,
                            wait, epe, [](int, int) {}, wg, nwg, smem);
   } else {
@@ -679,7 +679,7 @@ __device__ __forceinline__ void stage_o(const Params& P, int l, int wg, int nwg,
       st_coh(xb + (int64_t)b * D.H + row, res + v[0]);
     };
     const XSrc srcp{src.x, src.ldx, nullptr, nullptr, 0, true};  // split-bf16 pairs
-    mfma_stage<kMfmaNbt<NB>, 1, MR>(MatRows{Wm, {Wm, Wm}, rows_total, K}, (rows_total + 15) / 16, K, Wm,
+    mfma_stage<kMfmaNbt<NB, MR>, 1, MR>(MatRows{Wm, {Wm, Wm}, rows_total, K}, (rows_total + 15) / 16, K, Wm,
                            wbytes, srcp, nullptr, false, D.eps, B, P.S.x_cap, wait, epe,
                            [](int, int) {}, wg, nwg, smem);
   } else {
@@ -802,7 +802,7 @@ __device__ __forceinline__ void stage_gu(const Params& P, int l, int wg, int nwg
       // the Down stage (MFMA engine too) stages h as split-bf16 pairs
       st_coh(h + (int64_t)b * I + row, __uint_as_float(split_pair(a / (1.0f + expf(-a)) * u)));
     };
-    mfma_stage<kMfmaNbt<NB>, 2, MR>(MatRows{layer_w(P, l, 0), {rows.Wg, rows.Wu}, I, K}, (I + 15) / 16, K,
+    mfma_stage<kMfmaNbt<NB, MR>, 2, MR>(MatRows{layer_w(P, l, 0), {rows.Wg, rows.Wu}, I, K}, (I + 15) / 16, K,
                            layer_w(P, l, 0), (uint32_t)(P.W.layer_stride * 2), src,
                            layer_w(P, l, P.W.o_mlp_norm), true, D.eps, B, P.S.x_cap, wait, epe,
                            [](int, int) {}, wg, nwg, smem);
@@ -966,7 +966,7 @@ __device__ __forceinline__ void stage_d(const Params& P, int l, int wg, int nwg,
       st_coh(xa + o, ld_coh(xb + o) + v[0]);
     };
     const XSrc srcp{src.x, src.ldx, nullptr, nullptr, 0, true};  // split-bf16 pairs
-    mfma_stage<kMfmaNbt<NB>, 1, MR>(MatRows{Wm, {Wm, Wm}, rows_total, K}, (rows_total + 15) / 16, K, Wm,
+    mfma_stage<kMfmaNbt<NB, MR>, 1, MR>(MatRows{Wm, {Wm, Wm}, rows_total, K}, (rows_total + 15) / 16, K, Wm,
                            wbytes, srcp, nullptr, false, D.eps, B, P.S.x_cap, wait, epe,
                            [](int, int) {}, wg, nwg, smem);
   } else {
@@ -1048,7 +1048,7 @@ __device__ __forceinline__ void stage_lm(const Params& P, int wg, int nwg, char*
   if constexpr (NB >= kMfmaMinBatch) {
     // logits, and each lane's running best per batch tile (the lane holds one
     // batch row of each tile); merged into the wave's slots per batch pass
-    constexpr int NBT = kMfmaNbt<NB>;
+    constexpr int NBT = kMfmaNbt<NB, MR>;
     float bv[NBT];
     int bi[NBT];
 #pragma unroll
