@@ -16,8 +16,10 @@
  * Kernel Fusion for Transformers", Key points, "Fusion scope").
  *
  * Execution modes (all share the same stage code; below batch 16 they give
- * bitwise-equal results, from 16 on the MFMA engine's split of each tile's
- * K steps over waves depends on the mode's grid, so they agree to rounding):
+ * bitwise-equal results.  From 16 on they agree to rounding: the MFMA
+ * engine's split of each tile's K steps over waves depends on the mode's
+ * grid, and the tile-flag mode splits attention into shorter KV ranges,
+ * since two of its stage kernels share a CU's LDS):
  *   LD_MODE_WAIT  - one kernel per stage on one stream; each kernel starts
  *                   when the previous one has finished (the conventional
  *                   whole-kernel wait of the MegaOps summary, "In plain
