@@ -402,6 +402,7 @@ static ld_status compute_grids(ld_model* m) {
     for (int st = 0; st <= kSLm; ++st) {
       const size_t sm = (st == 0) ? m->smem_mega : std::max(m->smem_wait, m->smem_flags);
       HIPCHK(m, set_max_dynamic_smem(st, nb, sm));
+      if (st > 0 && nb == 64) HIPCHK(m, set_max_dynamic_smem(st, nb, m->smem_wait, true));
     }
     if (nb < kMfmaMinBatch) HIPCHK(m, set_max_dynamic_smem(kSMlpProj, nb, m->smem_wait));
     int occ = 0;
@@ -410,7 +411,7 @@ static ld_status compute_grids(ld_model* m) {
     m->grid_mega[nb] = std::min(occ * m->n_cu, m->K.max_wg);
     for (int st = kSQkv; st <= kSLm; ++st) {
       int o1 = 0, o2 = 0;
-      HIPCHK(m, occupancy(st, nb, m->thr_wait, m->smem_wait, &o1));
+      HIPCHK(m, occupancy(st, nb, m->thr_wait, m->smem_wait, &o1, nb == 64));
       HIPCHK(m, occupancy(st, nb, m->thr_flags, m->smem_flags, &o2));
       if (o1 < 1) return fail(m, LD_EINVAL, "stage kernel does not fit on a CU");
       if (o2 < 2) m->flags_ok = false;  // two tile-flag kernels must fit side by side

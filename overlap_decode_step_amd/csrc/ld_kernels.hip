@@ -22,11 +22,21 @@ namespace ld {
 // two of them fit on a CU side by side in the tile-flag mode.
 constexpr int kMaxThreads = kBlockThreads;
 constexpr int kStageWavesPerSimd = 4;
+// At 64 rows the whole-kernel-wait and graph modes (one kernel on a CU at a
+// time) run stage kernels built for two waves per SIMD, so that the MFMA
+// engine takes the batch in one 64-row pass like the persistent kernel
+// (measured 5.63 -> 5.03 ms per step at batch 64; at batch 16 the deeper
+// weight ring of these builds was 9% slower, so 16 and 32 rows keep the
+// four-wave builds, as does the tile-flag mode).
+constexpr int kStageWavesFull = 2;
+constexpr int kFullNb = 64;
+template <int WPS>
+constexpr int kStageRing = WPS == kStageWavesFull ? kMfmaRingBig : kMfmaRingSmall;
 
-template <int NB>
-__global__ __launch_bounds__(kMaxThreads, kStageWavesPerSimd) void k_qkv(Params P, int l) {
+template <int NB, int WPS = kStageWavesPerSimd>
+__global__ __launch_bounds__(kMaxThreads, WPS) void k_qkv(Params P, int l) {
   extern __shared__ __align__(16) char smem[];
-  stage_qkv<NB>(P, l, blockIdx.x, gridDim.x, smem);
+  stage_qkv<NB, kStageRing<WPS>>(P, l, blockIdx.x, gridDim.x, smem);
 }
 
 __global__ __launch_bounds__(kMaxThreads, kStageWavesPerSimd) void k_attn(Params P, int l) {
@@ -35,29 +45,29 @@ __global__ __launch_bounds__(kMaxThreads, kStageWavesPerSimd) void k_attn(Params
   stage_attn<true>(P, l, blockIdx.x, gridDim.x, smem, [] {});
 }
 
-template <int NB>
-__global__ __launch_bounds__(kMaxThreads, kStageWavesPerSimd) void k_o(Params P, int l) {
+template <int NB, int WPS = kStageWavesPerSimd>
+__global__ __launch_bounds__(kMaxThreads, WPS) void k_o(Params P, int l) {
   extern __shared__ __align__(16) char smem[];
-  stage_o<NB>(P, l, blockIdx.x, gridDim.x, smem);
+  stage_o<NB, kStageRing<WPS>>(P, l, blockIdx.x, gridDim.x, smem);
 }
 
-template <int NB>
-__global__ __launch_bounds__(kMaxThreads, kStageWavesPerSimd) void k_gu(Params P, int l) {
+template <int NB, int WPS = kStageWavesPerSimd>
+__global__ __launch_bounds__(kMaxThreads, WPS) void k_gu(Params P, int l) {
   extern __shared__ __align__(16) char smem[];
   GuBlock ring[kPfGu];
-  stage_gu<NB>(P, l, blockIdx.x, gridDim.x, smem, ring, false);
+  stage_gu<NB, kStageRing<WPS>>(P, l, blockIdx.x, gridDim.x, smem, ring, false);
 }
 
-template <int NB>
-__global__ __launch_bounds__(kMaxThreads, kStageWavesPerSimd) void k_d(Params P, int l) {
+template <int NB, int WPS = kStageWavesPerSimd>
+__global__ __launch_bounds__(kMaxThreads, WPS) void k_d(Params P, int l) {
   extern __shared__ __align__(16) char smem[];
-  stage_d<NB>(P, l, blockIdx.x, gridDim.x, smem);
+  stage_d<NB, kStageRing<WPS>>(P, l, blockIdx.x, gridDim.x, smem);
 }
 
-template <int NB>
-__global__ __launch_bounds__(kMaxThreads, kStageWavesPerSimd) void k_lm(Params P, int l) {
+template <int NB, int WPS = kStageWavesPerSimd>
+__global__ __launch_bounds__(kMaxThreads, WPS) void k_lm(Params P, int l) {
   extern __shared__ __align__(16) char smem[];
-  stage_lm<NB>(P, blockIdx.x, gridDim.x, smem);
+  stage_lm<NB, kStageRing<WPS>>(P, blockIdx.x, gridDim.x, smem);
 }
 
 // unfused-MLP ablation: the projection GEMVs and the elementwise kernels
@@ -152,16 +162,16 @@ __global__ void k_gen_kv(uint16_t* kc, uint16_t* vc, const int* len, int n_kv, i
 
 // ------------------------------------------------------------ wrappers
 
-template <int NB>
+template <int NB, int WPS = kStageWavesPerSimd>
 static const void* stage_fn(int stage) {
   switch (stage) {
     case 0: return reinterpret_cast<const void*>(&k_mega<NB>);
-    case kSQkv: return reinterpret_cast<const void*>(&k_qkv<NB>);
+    case kSQkv: return reinterpret_cast<const void*>(&k_qkv<NB, WPS>);
     case kSAttn: return reinterpret_cast<const void*>(&k_attn);
-    case kSO: return reinterpret_cast<const void*>(&k_o<NB>);
-    case kSGu: return reinterpret_cast<const void*>(&k_gu<NB>);
-    case kSD: return reinterpret_cast<const void*>(&k_d<NB>);
-    case kSLm: return reinterpret_cast<const void*>(&k_lm<NB>);
+    case kSO: return reinterpret_cast<const void*>(&k_o<NB, WPS>);
+    case kSGu: return reinterpret_cast<const void*>(&k_gu<NB, WPS>);
+    case kSD: return reinterpret_cast<const void*>(&k_d<NB, WPS>);
+    case kSLm: return reinterpret_cast<const void*>(&k_lm<NB, WPS>);
     case kSMlpProj:  // VALU engine only
       if constexpr (NB < kMfmaMinBatch) return reinterpret_cast<const void*>(&k_mlp_proj<NB>);
       return nullptr;
@@ -169,7 +179,8 @@ static const void* stage_fn(int stage) {
   }
 }
 
-static const void* kernel_ptr(int stage, int nb) {
+static const void* kernel_ptr(int stage, int nb, bool full = false) {
+  if (full && nb == kFullNb && stage != kSMlpProj) return stage_fn<kFullNb, kStageWavesFull>(stage);
   switch (nb) {
     case 1: return stage_fn<1>(stage);
     case 2: return stage_fn<2>(stage);
@@ -190,7 +201,8 @@ int nb_for_batch(int B) {
 
 hipError_t launch_stage(int stage, const Params& P, int l, int grid, int threads, size_t smem,
                         hipStream_t s) {
-  const void* fn = kernel_ptr(stage, nb_for_batch(P.S.B));
+  // whole-kernel-wait launches (P.S.wait) take the full-register builds
+  const void* fn = kernel_ptr(stage, nb_for_batch(P.S.B), P.S.wait != 0);
   if (!fn || stage == 0 || stage == kSMlpProj) return hipErrorInvalidValue;
   Params p = P;
   void* args[] = {&p, &l};
@@ -227,14 +239,14 @@ hipError_t launch_mlp_elem(int op, const Params& P, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t occupancy(int stage, int nb, int threads, size_t smem, int* blocks_per_cu) {
-  const void* fn = kernel_ptr(stage, nb);
+hipError_t occupancy(int stage, int nb, int threads, size_t smem, int* blocks_per_cu, bool full) {
+  const void* fn = kernel_ptr(stage, nb, full);
   if (!fn) return hipErrorInvalidValue;
   return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, fn, threads, smem);
 }
 
-hipError_t set_max_dynamic_smem(int stage, int nb, size_t smem) {
-  const void* fn = kernel_ptr(stage, nb);
+hipError_t set_max_dynamic_smem(int stage, int nb, size_t smem, bool full) {
+  const void* fn = kernel_ptr(stage, nb, full);
   if (!fn) return hipErrorInvalidValue;
   return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
 }

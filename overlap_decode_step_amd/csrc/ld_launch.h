@@ -18,8 +18,10 @@ hipError_t launch_mega(const Params& P, int grid, int threads, size_t smem, hipS
 hipError_t launch_mlp_proj(int which, const Params& P, int layer, int grid, int threads,
                            size_t smem, hipStream_t s);
 hipError_t launch_mlp_elem(int op, const Params& P, hipStream_t s);
-hipError_t occupancy(int stage, int nb, int threads, size_t smem, int* blocks_per_cu);
-hipError_t set_max_dynamic_smem(int stage, int nb, size_t smem);
+// full: the whole-kernel-wait builds of the 64-row MFMA stage kernels
+hipError_t occupancy(int stage, int nb, int threads, size_t smem, int* blocks_per_cu,
+                     bool full = false);
+hipError_t set_max_dynamic_smem(int stage, int nb, size_t smem, bool full = false);
 size_t scratch_bytes();
 size_t attn_smem(int group, int d, int T, int max_splits);
 size_t best_bytes();
