@@ -178,7 +178,7 @@ extern "C" size_t ld_weights_bytes(const ld_config* cfg) {
 // KV + workspace arena layout (byte offsets).
 struct KLayout {
   size_t kc, vc, xa, xb, qkv, ao, part, hbuf, gbuf, ubuf, lm_val, lm_idx, rope, ctr, lm_ctr,
-      split_ctr, err, tune_ctr, total;
+      split_ctr, mctr, mpart, err, tune_ctr, total;
   int split_len, max_splits, max_wg;
 };
 
@@ -241,6 +241,7 @@ static KLayout klayout(const ld_config* c, int maxB, int max_seq) {
   K.ao = take((size_t)maxB * qd * 4);
   K.part = take((size_t)maxB * c->n_q_heads * K.max_splits * (d + 2) * 4);
   K.hbuf = take((size_t)maxB * I * 4);
+  K.mpart = take((size_t)kMaxKSplit * maxB * H * 4);
   K.gbuf = take((size_t)maxB * I * 4);
   K.ubuf = take((size_t)maxB * I * 4);
   K.lm_val = take((size_t)K.max_wg * maxB * 4);
@@ -250,6 +251,7 @@ static KLayout klayout(const ld_config* c, int maxB, int max_seq) {
   K.ctr = take((size_t)c->n_layers * kStageCtrs * kCtrWords * 4);
   K.lm_ctr = take((size_t)kCtrWords * 4);
   K.split_ctr = take((size_t)c->n_layers * maxB * c->n_kv_heads * 16 * 4);
+  K.mctr = take((size_t)2 * kMctrPasses * ((H + 15) / 16) * 4);
   K.err = take(256);
   // private counters of standalone tuning launches (one layer's worth)
   K.tune_ctr = take(((size_t)kStageCtrs * kCtrWords + kCtrWords + (size_t)maxB * c->n_kv_heads * 16) * 4);
@@ -458,6 +460,8 @@ extern "C" ld_status ld_alloc_kv(ld_model* m, void* dev_buf, size_t bytes, int32
   K.ctr = reinterpret_cast<uint32_t*>(base + KL.ctr);
   K.lm_ctr = reinterpret_cast<uint32_t*>(base + KL.lm_ctr);
   K.split_ctr = reinterpret_cast<uint32_t*>(base + KL.split_ctr);
+  K.mctr = reinterpret_cast<uint32_t*>(base + KL.mctr);
+  K.mpart = reinterpret_cast<float*>(base + KL.mpart);
   K.err = reinterpret_cast<int*>(base + KL.err);
   m->ctr_bytes = KL.err - KL.ctr;
   K.max_wg = KL.max_wg;

@@ -83,6 +83,39 @@ __host__ __device__ constexpr int mfma_chunk(int rows, int K, uint32_t cap) {
 }
 
 
+// Split K (64-row kernels).  Every workgroup of a stage stages the
+// batch rows it multiplies, B x K x 4 bytes, so at 64 rows a narrow matrix
+// (the O and Down projections) moves many times its own weight bytes as
+// staging traffic.  Such a stage splits K into S ranges: workgroup wg takes
+// range wg % S and deals the tiles among the nwg / S workgroups of its range,
+// so it stages only K / S columns.  Each range's partial tile goes to a
+// scratch buffer, part[((s * B + b) * nrows + row], and a per-(batch pass,
+// tile) counter elects the last arriving range, which adds the S partials in
+// range order and calls the epilogue with the sum.  (At 16 rows the extra
+// round trips cost more than the staging saved.)
+struct SplitK {
+  float* part;
+  uint32_t* ctr;
+  int S;
+};
+// Split K runs in the 64-row builds with 256 VGPRs (the persistent kernel,
+// and the whole-kernel-wait kernels at 64 rows); measured there: batch 64
+// 5.03 -> 4.53 ms (WAIT), 4.52 -> 4.14 ms (MEGA).  In the tile-flag mode's
+// 128-VGPR builds it spilled registers and was 2% slower.
+template <int NB, int MR>
+constexpr bool kSplitK = NB >= 64 && MR == kMfmaRingBig;
+
+// The largest power of two up to kMaxKSplit that divides the grid, leaves
+// every range at least kMfmaMinChunk columns and at most 8 tiles per
+// workgroup.
+__host__ __device__ constexpr int mfma_splits(int ntile, int K, int nwg) {
+  int S = 1;
+  while (2 * S <= kMaxKSplit && nwg % (2 * S) == 0 && K / (2 * S) >= kMfmaMinChunk &&
+         ntile * 2 * S <= 8 * nwg)
+    S *= 2;
+  return S;
+}
+
 // Rows of NT weight matrices in one buffer: tile t, matrix j, row r (0..15).
 struct MatRows {
   const uint16_t* base;
@@ -105,14 +138,23 @@ __device__ __forceinline__ void mfma_stage(const MatRows& mr, int ntile, int K, 
                                            uint32_t wbytes, const XSrc& src, const uint16_t* gain,
                                            bool norm, float eps, int B, uint32_t x_cap,
                                            const WaitFn& wait, Epe& epe, const PassEnd& pass_end,
-                                           int wg, int nwg, char* smem) {
+                                           int wg, int nwg, char* smem,
+                                           const SplitK& sk = SplitK{nullptr, nullptr, 1}) {
   constexpr int MT = kMfmaTileMats / NT;  // tiles per wave per tile pass
   Scratch& sc = *reinterpret_cast<Scratch*>(smem);
   char* xbase = smem + kScratchBytes;
   const int lane = lane_id(), wave = wave_id(), nw = nwaves(), t = tid(), nth = blockDim.x;
-  // ---- decomposition (uniform across the grid)
+  // ---- K range of this workgroup (split K: norm-free single-matrix stages)
+  const int S = sk.S, ks = wg % S;
+  const int Kfull = K;
+  const int Ks = S > 1 ? ((K + S - 1) / S + 31) / 32 * 32 : K;
+  const int ks0 = ks * Ks;
+  K = max(0, min(Kfull, ks0 + Ks) - ks0);  // columns of this range
+  wg /= S;
+  nwg /= S;
+  // ---- decomposition (uniform across the workgroups of a range)
   nwg = min(nwg, max(1, ntile / kMfmaMinTiles));
-  if (wg >= nwg) return;
+  if (wg >= nwg || K <= 0) return;
   const int tpw = (ntile + nwg - 1) / nwg;
   int WR = 1;
   while (WR < tpw && WR < nw) WR *= 2;
@@ -153,7 +195,7 @@ __device__ __forceinline__ void mfma_stage(const MatRows& mr, int ntile, int K, 
     for (int m = 0; m < MT; ++m)
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
-        const uint32_t off = (ok && roff[m][j] != kOob && k < K) ? roff[m][j] + 2u * k : kOob;
+        const uint32_t off = (ok && roff[m][j] != kOob && k < K) ? roff[m][j] + 2u * (ks0 + k) : kOob;
         f[m][j] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kNt);
       }
   };
@@ -174,7 +216,7 @@ __device__ __forceinline__ void mfma_stage(const MatRows& mr, int ntile, int K, 
         const int k = pc * 256 + lane * 4;
         char* dst = reinterpret_cast<char*>(xw + (size_t)b * ldx + pc * 256);
         if (k < kn)
-          __builtin_amdgcn_global_load_lds(src.x + (int64_t)(b0 + b) * src.ldx + kc0 + k,
+          __builtin_amdgcn_global_load_lds(src.x + (int64_t)(b0 + b) * src.ldx + ks0 + kc0 + k,
                                            (__attribute__((address_space(3))) void*)dst, 16, 0,
                                            kSc1);
       }
@@ -202,7 +244,7 @@ __device__ __forceinline__ void mfma_stage(const MatRows& mr, int ntile, int K, 
     const int kk = j * 8, k = kc0 + kk;
     float g8[8];
     if (gain && k < K) {
-      const u32x4 gw = *reinterpret_cast<const u32x4*>(gain + k);
+      const u32x4 gw = *reinterpret_cast<const u32x4*>(gain + ks0 + k);
       g8[0] = bf16lo(gw.x); g8[1] = bf16hi(gw.x); g8[2] = bf16lo(gw.y); g8[3] = bf16hi(gw.y);
       g8[4] = bf16lo(gw.z); g8[5] = bf16hi(gw.z); g8[6] = bf16lo(gw.w); g8[7] = bf16hi(gw.w);
     } else {
@@ -221,7 +263,7 @@ __device__ __forceinline__ void mfma_stage(const MatRows& mr, int ntile, int K, 
           v[4] = __uint_as_float(p1.x); v[5] = __uint_as_float(p1.y);
           v[6] = __uint_as_float(p1.z); v[7] = __uint_as_float(p1.w);
         } else {
-          src.raw8(b0 + b, k, v);
+          src.raw8(b0 + b, ks0 + k, v);
         }
       } else {
 #pragma unroll
@@ -323,7 +365,7 @@ __device__ __forceinline__ void mfma_stage(const MatRows& mr, int ntile, int K, 
       // ---- norms of this batch pass (first tile pass only)
       if (sums) {
         __syncthreads();
-        if (t < nb) sc.rs[t] = 1.0f / sqrtf(ssacc / (float)K + eps);
+        if (t < nb) sc.rs[t] = 1.0f / sqrtf(ssacc / (float)Kfull + eps);
       }
       // ---- add the WK partial tiles in fixed order, then the epilogue
       __syncthreads();  // LDS staging area is free
@@ -361,16 +403,67 @@ __device__ __forceinline__ void mfma_stage(const MatRows& mr, int ntile, int K, 
         for (int m = 0; m < MT; ++m) {
           if (m < tiles_here) {
             const int tile = wg + (wr + (m0 + m) * WR) * nwg;
+            bool split = false;
+            if constexpr (NT == 1) split = S > 1;
+            if (split) {
+              // this range's partial tile, then the last arriving range adds
+              // all S partials in range order
+#pragma unroll
+              for (int bt = 0; bt < NBT; ++bt) {
+                const int b = bt * 16 + (lane & 15);
+                if (bt * 16 < prow && b < nb) {
+#pragma unroll
+                  for (int i = 0; i < 4; ++i) {
+                    const int row = tile * 16 + (lane >> 4) * 4 + i;
+                    if (row < mr.nrows)
+                      st_coh(sk.part + ((int64_t)ks * B + b0 + b) * mr.nrows + row, acc[m][0][bt][i]);
+                  }
+                }
+              }
+              wave_drain();
+              uint32_t last = 0;
+              if (lane == 0) {
+                uint32_t* c = sk.ctr + (int64_t)bp * ntile + tile;
+                const uint32_t old = __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED,
+                                                            __HIP_MEMORY_SCOPE_AGENT);
+                last = old == (uint32_t)(S - 1);
+                if (last) __hip_atomic_store(c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              }
+              if (!__shfl(last, 0)) continue;
+            }
 #pragma unroll
             for (int bt = 0; bt < NBT; ++bt) {
               const int b = bt * 16 + (lane & 15);
               if (bt * 16 < prow && b < nb) {
+                if (split) {
+                  // every range's partials of the lane's 4 rows in one round
+                  // of loads, then added in range order
+                  float pv[4][kMaxKSplit];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                  float v[NT];
+                  for (int i = 0; i < 4; ++i) {
+                    const int row = tile * 16 + (lane >> 4) * 4 + i;
 #pragma unroll
-                  for (int j = 0; j < NT; ++j) v[j] = acc[m][j][bt][i];
-                  epe(tile, (lane >> 4) * 4 + i, b0 + b, b, bt, v);
+                    for (int q = 0; q < kMaxKSplit; ++q)
+                      pv[i][q] = (q < S && row < mr.nrows)
+                                     ? ld_coh(sk.part + ((int64_t)q * B + b0 + b) * mr.nrows + row)
+                                     : 0.f;
+                  }
+#pragma unroll
+                  for (int i = 0; i < 4; ++i) {
+                    float v[NT] = {pv[i][0]};
+#pragma unroll
+                    for (int q = 1; q < kMaxKSplit; ++q)
+                      if (q < S) v[0] += pv[i][q];
+                    epe(tile, (lane >> 4) * 4 + i, b0 + b, b, bt, v);
+                  }
+                } else {
+#pragma unroll
+                  for (int i = 0; i < 4; ++i) {
+                    float v[NT];
+#pragma unroll
+                    for (int j = 0; j < NT; ++j) v[j] = acc[m][j][bt][i];
+                    epe(tile, (lane >> 4) * 4 + i, b0 + b, b, bt, v);
+                  }
                 }
               }
             }

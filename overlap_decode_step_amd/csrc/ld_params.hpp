@@ -26,6 +26,11 @@ constexpr int kErrTimeout = 3;
 
 // Batches from here on take the MFMA engine; smaller ones the VALU engine.
 constexpr int kMfmaMinBatch = 16;
+// Split-K stages of the MFMA engine (64-row kernels): at most kMaxKSplit K
+// ranges, and one last-arriver counter per (batch pass of 16 rows, tile) and
+// stage.
+constexpr int kMaxKSplit = 4;
+constexpr int kMctrPasses = 4;  // batch passes at max_batch 64
 
 // SwiGLU tiling variants (chosen offline per batch size).
 enum : int { kGuCol = 0, kGuRow = 1 };
@@ -76,6 +81,8 @@ struct Work {
   uint32_t* ctr;        // stage counters [L][kStageCtrs][counter words]
   uint32_t* lm_ctr;     // LM-head last-arriver counter
   uint32_t* split_ctr;  // attention last-arriver counters [L][maxB][nkv][16]
+  uint32_t* mctr;       // split-K last-arriver counters: O, then Down, [kMctrPasses][tiles]
+  float* mpart;         // split-K partial tiles [kMaxKSplit][maxB][H]
   int* err;
   uint64_t* trace;  // optional stage timestamps (see trace_ev), nullptr = off
   uint64_t watchdog;

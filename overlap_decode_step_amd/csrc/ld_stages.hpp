@@ -679,9 +679,11 @@ __device__ __forceinline__ void stage_o(const Params& P, int l, int wg, int nwg,
       st_coh(xb + (int64_t)b * D.H + row, res + v[0]);
     };
     const XSrc srcp{src.x, src.ldx, nullptr, nullptr, 0, true};  // split-bf16 pairs
-    mfma_stage<kMfmaNbt<NB, MR>, 1, MR>(MatRows{Wm, {Wm, Wm}, rows_total, K}, (rows_total + 15) / 16, K, Wm,
+    const int ntile = (rows_total + 15) / 16;
+    const SplitK sk{P.K.mpart, P.K.mctr, kSplitK<NB, MR> ? mfma_splits(ntile, K, nwg) : 1};
+    mfma_stage<kMfmaNbt<NB, MR>, 1, MR>(MatRows{Wm, {Wm, Wm}, rows_total, K}, ntile, K, Wm,
                            wbytes, srcp, nullptr, false, D.eps, B, P.S.x_cap, wait, epe,
-                           [](int, int) {}, wg, nwg, smem);
+                           [](int, int) {}, wg, nwg, smem, sk);
   } else {
     gemv_stage<NR, UC, NB, kPfO>(rowfn, (rows_total + NR - 1) / NR, K, Wm, wbytes, src, nullptr,
                                  false, D.eps, B, batch_tile(P, K, NB), wait, epi, wg, nwg, smem);
@@ -966,9 +968,12 @@ __device__ __forceinline__ void stage_d(const Params& P, int l, int wg, int nwg,
       st_coh(xa + o, ld_coh(xb + o) + v[0]);
     };
     const XSrc srcp{src.x, src.ldx, nullptr, nullptr, 0, true};  // split-bf16 pairs
-    mfma_stage<kMfmaNbt<NB, MR>, 1, MR>(MatRows{Wm, {Wm, Wm}, rows_total, K}, (rows_total + 15) / 16, K, Wm,
+    const int ntile = (rows_total + 15) / 16;
+    const SplitK sk{P.K.mpart, P.K.mctr + kMctrPasses * ntile,
+                    kSplitK<NB, MR> ? mfma_splits(ntile, K, nwg) : 1};
+    mfma_stage<kMfmaNbt<NB, MR>, 1, MR>(MatRows{Wm, {Wm, Wm}, rows_total, K}, ntile, K, Wm,
                            wbytes, srcp, nullptr, false, D.eps, B, P.S.x_cap, wait, epe,
-                           [](int, int) {}, wg, nwg, smem);
+                           [](int, int) {}, wg, nwg, smem, sk);
   } else {
     gemv_stage<NR, UC, NB, kPfD>(rowfn, (rows_total + NR - 1) / NR, K, Wm, wbytes, src, nullptr,
                                  false, D.eps, B, batch_tile(P, K, NB), wait, epi, wg, nwg, smem);
