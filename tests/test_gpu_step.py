@@ -210,8 +210,10 @@ def test_ragged_shape_multi_split(ld, orc, mode):
     m.free()
 
 
-@pytest.mark.parametrize("B", [2, 5, 16])
+@pytest.mark.parametrize("B", [2, 5, 8, 16, 27, 45])
 def test_tiny_batches(ld, orc, B):
+    # every batch build: 2, 8 and 16 fill theirs; 5, 27 and 45 leave ragged
+    # batch tails in the 8-, 32- and 64-row builds
     shape = W.TINY
     prefill = W.kv_lengths(B, 1, 200)
     om = orc.model(shape, seed=W.SEED_WEIGHTS, w_std=0.02)
@@ -265,7 +267,7 @@ def test_llama1b_batch1_parity(ld, orc, llama1b):
     m.free()
 
 
-@pytest.mark.parametrize("B", [4, 16, 64])
+@pytest.mark.parametrize("B", [4, 16, 32, 64])
 def test_llama1b_batch_sweep_sampled(ld, orc, llama1b, B):
     # Short-context sweep: KV length ~U[256, 1024] per sequence; the oracle
     # checks sequences 0 and B-1 of one step in the tile-flag and persistent modes.
