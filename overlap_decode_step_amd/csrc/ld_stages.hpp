@@ -547,9 +547,9 @@ struct AttnShape {
   static constexpr int g = G, dh = DH;
 };
 
-// `idle_hook()` runs in a workgroup that has no attention item, once the
-// stage's input is ready (the persistent kernel issues the SwiGLU stage's
-// first weight loads there, while the memory system is otherwise quiet).
+// `idle_hook()` runs in a workgroup that has no attention item, without
+// waiting for the stage's input (the persistent kernel issues the SwiGLU
+// stage's first weight loads there).
 template <bool MULTI, class Hook>
 __device__ __forceinline__ void stage_attn(const Params& P, int l, int wg, int nwg, char* smem,
                            const Hook& idle_hook) {
@@ -565,11 +565,18 @@ __device__ __forceinline__ void stage_attn(const Params& P, int l, int wg, int n
   AttnItem a;
   const bool any = attn_item_at<MULTI>(P, sc, T, wg, a);
   // the first item's cached rows are copied while this stage's input is
-  // still being produced
-  if (any) attn_copy_tiles(P, l, a, smem, !P.S.wait);
-  if (!P.S.wait) wg_wait(sync_of(P), stage_ctr(P, l, kCQkv), P.S.t_qkv + P.S.inject, kSAttn);
+  // still being produced.  A workgroup without an item reads none of this
+  // stage's input, so it does not wait for it: its hook starts at once (the
+  // persistent kernel's SwiGLU weight loads then drain while the items
+  // compute, instead of during their combine), and the next stage's wait on
+  // this stage's counter orders it after the QKV stage as before.
+  if (any) {
+    attn_copy_tiles(P, l, a, smem, !P.S.wait);
+    if (!P.S.wait) wg_wait(sync_of(P), stage_ctr(P, l, kCQkv), P.S.t_qkv + P.S.inject, kSAttn);
+  } else {
+    idle_hook();
+  }
   trace_ev(P, l, kSAttn, 1, wg);
-  if (!any) idle_hook();
   // the item loop of one shape (the dispatch stays outside the loop, so each
   // loop's hoisted index math is computed on its own path only)
   auto items = [&](auto shape) {
