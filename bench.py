@@ -179,7 +179,7 @@ def multi_token_bench(shape_name, B, M, steps, warmup, modes):
     from overlap_decode_step_amd import ld
     from synth import workloads as W
     shape = W.SHAPES[shape_name]
-    w_std = W.WORKLOADS["llama70b"]["w_std"] if shape_name == "llama70b" else 0.02
+    w_std = W.WORKLOADS["llama70b"]["w_std"] if shape_name.startswith("llama70b") else 0.02
     prefill = 512 if shape_name == "llama1b" else 1024
     rows = B * M
     dev = torch.device("cuda:0")
@@ -236,8 +236,10 @@ def main():
                     help="only copy a 1 GiB buffer (counter calibration)")
     ap.add_argument("--sweep", action="store_true",
                     help="also run the batch sweep (1, 4, 16, 64; KV ~U[256,1024]; every mode)")
-    ap.add_argument("--shape", default="llama1b", choices=["llama1b", "llama8b", "llama70b"],
-                    help="decoder shape (the 8B and 70B shapes skip the CPU baseline)")
+    ap.add_argument("--shape", default="llama1b", choices=["llama1b", "llama8b", "llama70b", "llama70b_tp8"],
+                    help="decoder shape (the 8B and 70B shapes skip the CPU baseline; "
+                         "llama70b_tp8 is one GPU's 8-way tensor-parallel share of the 70B "
+                         "shape, without the exchanges)")
     ap.add_argument("--tokens-per-seq", type=int, default=1,
                     help="several consecutive tokens per sequence per step (a prefill chunk): "
                          "times ld_decode_step_tokens in every mode instead of the decode step")
@@ -275,7 +277,7 @@ def main():
     from synth import workloads as W
 
     shape = W.SHAPES[args.shape]
-    w_std = W.WORKLOADS["llama70b"]["w_std"] if args.shape == "llama70b" else 0.02
+    w_std = W.WORKLOADS["llama70b"]["w_std"] if args.shape.startswith("llama70b") else 0.02
     headline = args.shape == "llama1b"
     B = args.batch
     prefill = args.prefill if args.prefill is not None else (512 if headline else 1024)

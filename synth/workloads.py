@@ -106,8 +106,13 @@ LLAMA_1B = shape(16, 2048, 32, 8, 64, 8192, 128256, 1)
 LLAMA_8B = shape(32, 4096, 32, 8, 128, 14336, 128256, 0)
 # Llama-3.1-70B shape (about 141 GB of bf16 weights on one GPU).
 LLAMA_70B = shape(80, 8192, 64, 8, 128, 28672, 128256, 0)
+# One GPU's share of the Llama-70B shape under 8-way tensor parallelism:
+# 8 Q heads and 1 KV head of 128 (one whole GQA group), SwiGLU 3584 (an eighth
+# of 28672), a 16032-row vocabulary shard; the residual stream stays 8192 wide.
+LLAMA_70B_TP8 = shape(80, 8192, 8, 1, 128, 3584, 16032, 0)
 
-SHAPES = {"tiny": TINY, "llama1b": LLAMA_1B, "llama8b": LLAMA_8B, "llama70b": LLAMA_70B}
+SHAPES = {"tiny": TINY, "llama1b": LLAMA_1B, "llama8b": LLAMA_8B, "llama70b": LLAMA_70B,
+          "llama70b_tp8": LLAMA_70B_TP8}
 
 # Workloads: weights ~N(0, w_std) (norm gains 1.0), KV prefill ~N(0, 1).
 WORKLOADS = {
@@ -125,6 +130,10 @@ WORKLOADS = {
     # Llama-70B shape on one GPU: KV 1024 -> 16384, batch 1/4/16
     "llama70b": dict(shape="llama70b", w_std=0.01, kv_std=1.0, batches=[1, 4, 16],
                      prefill=1024, steps=4),
+    # the same at one GPU's 8-way tensor-parallel share (kernels at the shard's
+    # shapes; the exchanges between GPUs are not part of it)
+    "llama70b_tp8": dict(shape="llama70b_tp8", w_std=0.01, kv_std=1.0, batches=[1, 4, 16],
+                         prefill=1024, steps=4),
 }
 
 

@@ -293,10 +293,13 @@ def test_llama1b_batch_sweep_sampled(ld, orc, llama1b, B):
 # -------------------------------------- 8B and 70B widths, two layers
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("name,w_std", [("llama8b", 0.02), ("llama70b", 0.01)])
+@pytest.mark.parametrize("name,w_std", [("llama8b", 0.02), ("llama70b", 0.01),
+                                         ("llama70b_tp8", 0.01)])
 def test_wide_shapes_two_layers(ld, orc, name, w_std):
     # The Llama-8B and Llama-70B shapes at full width (hidden size, heads of
-    # 128, SwiGLU width, 128256-token vocabulary, untied LM head) with two
+    # 128, SwiGLU width, 128256-token vocabulary, untied LM head), and one
+    # GPU's 8-way tensor-parallel share of the 70B shape (8 Q heads and 1 KV
+    # head, SwiGLU 3584, a 16032-row vocabulary shard), with two
     # layers, so the oracle finishes in seconds; KV length 1024 as in those
     # workloads.  Batch 1 in every mode, then batch 16 (the MFMA engine) with
     # sequences 0 and 15 checked.  At the 70B width the tile-flag mode is
