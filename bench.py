@@ -26,6 +26,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix peak (no sparsity)
+MFMA_MIN_BATCH = 16  # from this many rows the projections run on the MFMA engine
 CSRC = os.path.join(ROOT, "overlap_decode_step_amd", "csrc")
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "k_mega_llama1b_b1_hbm_traffic.md")
 
@@ -41,6 +43,19 @@ def algorithmic_bytes(shape, batch, positions):
     kv_row = 2 * L * kvd * 2  # K and V, bf16, all layers, one position
     per_seq = [2 * H + kv_row * (p + 1) + kv_row + 4 * V for p in positions]
     return weights + sum(per_seq)
+
+
+def algorithmic_flops(shape, batch, positions):
+    """Floating-point operations of one decode step (a multiply-add counts
+    two): every projection row once per sequence (QKV, O, gate, up, Down, LM
+    head), then attention's q.K and p.V over positions 0..p of every query
+    head.  Returns (projections, attention); from 16 rows the projections run
+    on the MFMA engine and attention on the vector units."""
+    H, V, I, L = shape["hidden"], shape["vocab"], shape["intermediate"], shape["n_layers"]
+    qd, kvd = shape["n_q_heads"] * shape["head_dim"], shape["n_kv_heads"] * shape["head_dim"]
+    proj = 2 * batch * (L * (H * (qd + 2 * kvd) + qd * H + 3 * H * I) + V * H)
+    attn = sum(4 * L * qd * (p + 1) for p in positions)
+    return proj, attn
 
 
 def kernel_source_digest():
@@ -396,6 +411,16 @@ def main():
         "cpu_baseline": cpu,
         "modes_ms_per_step": results,
     }
+    if B >= MFMA_MIN_BATCH:
+        # MFMA utilisation of the projections: algorithmic FLOPs / (time x
+        # dense bf16 peak); the engine issues two MFMAs per product (the
+        # activations as split-bf16 hi and lo parts), hence issued = 2 x
+        proj = sum(algorithmic_flops(shape, B, [p] * B)[0] for p in positions) / steps
+        tf = proj / (ms * 1e-3) / 1e12
+        out["mfma"] = {"algorithmic_tflops": tf, "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
+                       "util": tf / MFMA_BF16_PEAK_TFLOPS,
+                       "issued_util": 2 * tf / MFMA_BF16_PEAK_TFLOPS,
+                       "flops_per_step": proj}
     if sweep is not None:
         out["batch_sweep_tokens_per_s"] = sweep
     if ablation is not None:
