@@ -123,7 +123,12 @@ constexpr int kRedThreads = 512;
 // Stage batch rows [b0, b0+nb) of the input into LDS: xs[b*K + k] =
 // x[b0+b][k] * gain[k] (gain may be null).  With `norm`, also
 // rs[b] = 1/sqrt(sum_k x^2 / K + eps) over the raw inputs.  nb <= NB.
-template <int NB>
+// A thread's column groups are j = tid, tid + kRedThreads, ...  With U > 1
+// (single-row inputs) it issues the loads of U groups before it uses any, so
+// a wide input costs one round trip per U groups rather than one per group;
+// the groups are added in the same order.  (A gain, if any, is read when a
+// group is used: the callers that group have none.)
+template <int NB, int U = 1>
 __device__ __forceinline__ void stage_x(const XSrc& src, int b0, int nb, int K,
                                         const uint16_t* gain, bool norm, float eps, float* xs,
                                         Scratch& sc) {
@@ -131,7 +136,33 @@ __device__ __forceinline__ void stage_x(const XSrc& src, int b0, int nb, int K,
 #pragma unroll
   for (int b = 0; b < NB; ++b) ss[b] = 0.f;
   const int n8 = K >> 3;
-  if (tid() < kRedThreads) {
+  if constexpr (U > 1) {
+    static_assert(NB == 1, "grouped staging holds one row's groups");
+    if (tid() < kRedThreads) {
+      for (int j0 = tid(); j0 < n8; j0 += U * kRedThreads) {
+        float v[U][8];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          if (j0 + u * kRedThreads < n8) src.raw8(b0, (j0 + u * kRedThreads) * 8, v[u]);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int j = j0 + u * kRedThreads;
+          if (j >= n8) break;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) ss[0] = fmaf(v[u][i], v[u][i], ss[0]);
+          if (gain) {
+            const u32x4 gw = *reinterpret_cast<const u32x4*>(gain + j * 8);
+            v[u][0] *= bf16lo(gw.x); v[u][1] *= bf16hi(gw.x); v[u][2] *= bf16lo(gw.y);
+            v[u][3] *= bf16hi(gw.y); v[u][4] *= bf16lo(gw.z); v[u][5] *= bf16hi(gw.z);
+            v[u][6] *= bf16lo(gw.w); v[u][7] *= bf16hi(gw.w);
+          }
+          float4* d = reinterpret_cast<float4*>(xs + j * 8);
+          d[0] = make_float4(v[u][0], v[u][1], v[u][2], v[u][3]);
+          d[1] = make_float4(v[u][4], v[u][5], v[u][6], v[u][7]);
+        }
+      }
+    }
+  } else if (tid() < kRedThreads) {
     for (int j = tid(); j < n8; j += kRedThreads) {
       float g[8];
       if (gain) {
@@ -346,7 +377,7 @@ __device__ __forceinline__ void gemv_prefetch(const WStream<NR, UC, RowFn>& ws,
 // batch tile streams the weights again (LDS blocks are used by a single batch
 // tile only).  Epi(tile, b0, nb, acc, scratch) consumes the reduced sums
 // (every lane of the calling wave holds every sum).
-template <int NR, int UC, int NB, int PF, class RowFn, class WaitFn, class Epi>
+template <int NR, int UC, int NB, int PF, int SU = 1, class RowFn, class WaitFn, class Epi>
 __device__ __forceinline__ void gemv_run(const WStream<NR, UC, RowFn>& ws,
                                          WBlock<NR, UC> (&ring)[PF], bool prefetched,
                                          const XSrc& src, const uint16_t* gain, bool norm, float eps,
@@ -367,7 +398,7 @@ __device__ __forceinline__ void gemv_run(const WStream<NR, UC, RowFn>& ws,
     const int b0 = bt * bw, nb = min(bw, B - b0);
     // (its input loads also wait for any earlier loads of this wave: the
     // copies to LDS have landed once this returns)
-    stage_x<NB>(src, b0, nb, K, gain, norm, eps, xs, sc);
+    stage_x<NB, SU>(src, b0, nb, K, gain, norm, eps, xs, sc);
     if (bt > 0 || (wave == 0 && !prefetched)) {
 #pragma unroll
       for (int j = 0; j < PF; ++j) ws.issue(ring[j], j, lane);
@@ -414,7 +445,7 @@ __device__ __forceinline__ void gemv_run(const WStream<NR, UC, RowFn>& ws,
 }
 
 // A whole GEMV stage with its own ring.
-template <int NR, int UC, int NB, int PF, class RowFn, class WaitFn, class Epi>
+template <int NR, int UC, int NB, int PF, int SU = 1, class RowFn, class WaitFn, class Epi>
 __device__ __forceinline__ void gemv_stage(const RowFn& rowfn, int ntile, int K,
                                            const uint16_t* wbase, uint32_t wbytes, const XSrc& src,
                                            const uint16_t* gain, bool norm, float eps, int B,
@@ -422,7 +453,7 @@ __device__ __forceinline__ void gemv_stage(const RowFn& rowfn, int ntile, int K,
                                            char* smem) {
   const WStream<NR, UC, RowFn> ws(rowfn, ntile, K, wbase, wbytes, wg, nwg);
   WBlock<NR, UC> ring[PF];
-  gemv_run<NR, UC, NB, PF>(ws, ring, false, src, gain, norm, eps, B, bw, wait, epi, smem);
+  gemv_run<NR, UC, NB, PF, SU>(ws, ring, false, src, gain, norm, eps, B, bw, wait, epi, smem);
 }
 
 }  // namespace ld

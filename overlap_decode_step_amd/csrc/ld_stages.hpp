@@ -32,6 +32,10 @@ constexpr int kNrQkv = 1, kUcQkv = 4, kPfQkv = 2;
 constexpr int kNrO = 1, kUcO = 4, kPfO = 2;
 constexpr int kPairsGu = 1, kUcGu = 4, kPfGu = 2;  // one (gate, up) row pair per task
 constexpr int kNrD = 1, kUcD = 8, kPfD = 2;
+// Down's input (the SwiGLU output, 8192 to 28672 columns) is staged with the
+// loads of 4 column groups per thread in flight at batch 1
+template <int NB>
+constexpr int kStageGroupsD = NB == 1 ? 4 : 1;
 constexpr int kNrLm = 2, kUcLm = 4, kPfLm = 2;
 
 __device__ __forceinline__ const uint16_t* layer_w(const Params& P, int l, int64_t off) {
@@ -982,8 +986,10 @@ __device__ __forceinline__ void stage_d(const Params& P, int l, int wg, int nwg,
                            wbytes, srcp, nullptr, false, D.eps, B, P.S.x_cap, wait, epe,
                            [](int, int) {}, wg, nwg, smem, sk);
   } else {
-    gemv_stage<NR, UC, NB, kPfD>(rowfn, (rows_total + NR - 1) / NR, K, Wm, wbytes, src, nullptr,
-                                 false, D.eps, B, batch_tile(P, K, NB), wait, epi, wg, nwg, smem);
+    gemv_stage<NR, UC, NB, kPfD, kStageGroupsD<NB>>(rowfn, (rows_total + NR - 1) / NR, K, Wm,
+                                                     wbytes, src, nullptr, false, D.eps, B,
+                                                     batch_tile(P, K, NB), wait, epi, wg, nwg,
+                                                     smem);
     held.flush();
   }
   trace_ev(P, l, kSD, 2, wg);
