@@ -415,3 +415,78 @@ def test_step_float_build_matches_double_build(orc, orc64):
         rel = np.linalg.norm(l32 - l64) / np.linalg.norm(l64)
         assert rel <= 1e-5, (step, rel)
         tok = int(n64[0])
+
+
+def _score_from_mass(o_marker, mass_rest, n_rest):
+    """Softmax score recovered from attention outputs: n_rest positions score 0
+    (K = 0) and carry V = e_1, so o_1 = n_rest / Z; a position whose V is e_0
+    has weight o_0 = e^s / Z, hence s = ln(o_0 * n_rest / o_1)."""
+    return math.log(float(o_marker) * n_rest / float(mass_rest))
+
+
+def test_step_rope_applied_to_q_and_k_at_the_position(orc):
+    # One layer.  q head 0 and kv head 0 share one weight row in channel 0 and
+    # every other Q/K/V row is zero, so before rotation q = k = c e_0: only the
+    # pair (0, d/2) is non-zero, and it turns by exactly p radians (frequency
+    # theta^0 = 1).  The cache holds K = 0 and V = e_1 at positions 0..p-1.
+    #  - step at p: the new key must score |q|^2 / sqrt(d) (a rotation keeps
+    #    the product of q and k at equal positions), and the stored key must
+    #    point at angle p;
+    #  - step at p + 1 with the same token (same c), reading the key stored at
+    #    p: that key must score cos(1) |q|^2 / sqrt(d), the new one |q|^2 / sqrt(d).
+    # A key left unrotated scores cos(p) |q|^2 / sqrt(d) (p = 20: 0.41), a q or
+    # k rotated at p +- 1 changes the angle of the stored key or the relative
+    # score, so each such slip fails one of the checks below.
+    shape = small_shape(n_layers=1)
+    d, H = shape["head_dim"], shape["hidden"]
+    m = orc.model(shape, seed=1, w_std=0.02)
+    for kind in (L.W_Q, L.W_K, L.W_V):
+        m.weight(kind, 0)[:] = 0
+    p, tok = 20, 7
+    # probe: the normalised layer input (independent of the Q/K/V weights)
+    probe = orc.trace(shape, 0, 0)
+    orc.decode_step(m, orc.kv(shape, 1, 64, seed=2, prefill=[p]), [tok], [p], trace=probe)
+    xn = probe["xn"].astype(np.float64)
+    j = int(np.argmax(np.abs(xn)))
+    row = np.zeros(H, dtype=np.float32)
+    row[j] = 4.0 / xn[j]  # c = row . xn close to 4, so |q|^2 / sqrt(d) is about 2
+    row = bf16_to_f32(np.array([orc.bf16_round(float(v)) for v in row], dtype=np.uint16))
+    m.weight(L.W_Q, 0)[0] = bf16_exact(row)
+    m.weight(L.W_K, 0)[0] = bf16_exact(row)
+    kv = orc.kv(shape, 1, 64, seed=2, prefill=[p])
+    one = orc.bf16_round(1.0)
+    for h in range(shape["n_kv_heads"]):
+        kv.k(0, 0, h)[:] = 0
+        kv.v(0, 0, h)[:] = 0
+        kv.v(0, 0, h)[:p, 1] = one
+    scale = 1 / math.sqrt(d)
+
+    tr = orc.trace(shape, 0, 0)
+    orc.decode_step(m, kv, [tok], [p], trace=tr)
+    q = tr["q"][:d].astype(np.float64)
+    assert np.count_nonzero(q) == 2 and q[0] != 0 and q[d // 2] != 0
+    q2 = float(q @ q)
+    # stored key: angle p (mod 2 pi), length |q| (to bf16 rounding)
+    kp = bf16_to_f32(kv.k(0, 0, 0)[p]).astype(np.float64)
+    assert np.count_nonzero(kp) == 2
+    ang = math.atan2(kp[d // 2], kp[0])
+    assert abs(math.remainder(ang - p, 2 * math.pi)) < 1e-2
+    assert abs(math.hypot(kp[0], kp[d // 2]) ** 2 / q2 - 1) < 1e-2
+    # the new key at the same position: |q|^2 / sqrt(d)
+    o = tr["o"][:d].astype(np.float64)
+    w_new = 1.0 - o[1]  # V at p is zero (Wv = 0): the rest of the mass is p's
+    s_same = math.log(w_new * p / o[1])
+    assert abs(s_same / (q2 * scale) - 1) < 1e-2, (s_same, q2 * scale)
+
+    # next step, same token: mark the row stored at p with V = e_0
+    kv.v(0, 0, 0)[p, :] = 0
+    kv.v(0, 0, 0)[p, 0] = one
+    tr2 = orc.trace(shape, 0, 0)
+    orc.decode_step(m, kv, [tok], [p + 1], trace=tr2)
+    o2 = tr2["o"][:d].astype(np.float64)
+    q2b = float(tr2["q"][:d].astype(np.float64) @ tr2["q"][:d].astype(np.float64))
+    assert abs(q2b / q2 - 1) < 1e-6  # same token, same |q|
+    s_prev = _score_from_mass(o2[0], o2[1], p)
+    s_new = math.log((1.0 - o2[0] - o2[1]) * p / o2[1])
+    assert abs(s_prev / (golden("cos_1") * q2 * scale) - 1) < 1e-2, (s_prev, q2 * scale)
+    assert abs(s_new / (q2 * scale) - 1) < 1e-2, (s_new, q2 * scale)
