@@ -89,6 +89,25 @@ def read_traffic(mode, batch):
         return None
 
 
+def host_cpu():
+    """The host the oracle ran on: CPU model, logical CPUs (nproc) and the CPUs
+    this process may run on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = None
+    return {"cpu_model": model, "nproc": os.cpu_count(), "usable_cpus": usable}
+
+
 def cpu_baseline(shape, prefill, steps):
     """The oracle (single-threaded C, fp32 over bf16 weights) decoding `steps`
     greedy steps of sequence 0 from position `prefill`; weights and KV are
@@ -104,6 +123,7 @@ def cpu_baseline(shape, prefill, steps):
         _, tok = orc.decode_one(om, okv, 0, tok, prefill + s)
     wall, cpu = time.perf_counter() - w0, time.process_time() - c0
     return {"value": steps / wall, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "host": host_cpu(),
             "sample": f"{steps} greedy steps of one sequence, positions {prefill}..{prefill + steps - 1}, "
                       f"same shape and seeds; {wall:.1f} s wall, {cpu:.1f} s CPU (one thread)"}
 

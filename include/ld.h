@@ -166,14 +166,22 @@ ld_status ld_decode_step_tokens(ld_model* m, const int32_t* tokens, int32_t toke
 
 /* Offline choice of the SwiGLU tiling ("Deep Kernel Fusion for Transformers",
  * Summary: a profiler benchmarks the tiling variants on the target before
- * inference and keeps the fastest; Key points: no runtime dispatch cost).
- * Times the row-major and column-major variants for each batch size in
- * batches[0..n) (each <= max_batch) and records the faster in the model's
- * table; writes the table as JSON to table_path unless NULL.  Synchronous;
- * needs ld_alloc_kv.  Overwrites workspace contents (not the KV cache). */
+ * inference and keeps the fastest; Key points, "Code and limitations": no
+ * dispatch cost at run time).  For each batch size in batches[0..n) (each
+ * <= max_batch) times whole decode steps in the model's current mode with the
+ * column-major and the row-major tiling, alternating, 5 rounds of 3 steps
+ * after 2 warm-up steps each, every sequence at position min(max_seq - 1,
+ * 1024); the row-major tiling is recorded for that (mode, batch) only if its
+ * median beats the column-major median by more than 1%.  Writes the mode's
+ * table (choices and both medians) as JSON to table_path unless NULL.
+ * Synchronous; needs ld_alloc_kv; allocates its own small step buffers.
+ * Overwrites the workspace and the KV cache row at that position of
+ * sequences 0..batch-1 (refill the cache afterwards if it matters).  A
+ * device error during the steps is returned as by ld_device_error. */
 ld_status ld_tune(ld_model* m, const int32_t* batches, int32_t n, const char* table_path);
 
-/* Load a table written by ld_tune (same shape required). */
+/* Load a table written by ld_tune (same shape required) into the mode it was
+ * tuned in (the current mode if the table names none). */
 ld_status ld_load_tuning(ld_model* m, const char* table_path);
 
 /* Synchronise the device, return LD_OK / LD_ETIMEOUT / LD_EDEVICE from the

@@ -48,7 +48,8 @@ ld_status ld_write_weight(ld_model* m, int32_t kind, int32_t layer, const uint16
 ld_status ld_read_kv(ld_model* m, int32_t layer, int32_t seq, int32_t kv_head, int32_t pos0,
                      int32_t npos, uint16_t* k_dst, uint16_t* v_dst);
 
-/* Force / query the SwiGLU tiling used for one batch size. */
+/* Force the SwiGLU tiling of one batch size in every mode / query the one the
+ * current mode uses. */
 ld_status ld_set_swiglu_variant(ld_model* m, int32_t batch, int32_t variant);
 int32_t ld_get_swiglu_variant(const ld_model* m, int32_t batch);
 
@@ -83,6 +84,21 @@ ld_status ld_debug_inject_stall(ld_model* m);
  * n_layers.  NULL turns it off.  bytes >= ld_trace_bytes(cfg). */
 size_t ld_trace_bytes(const ld_config* cfg);
 ld_status ld_set_trace(ld_model* m, void* dev_buf, size_t bytes);
+
+/* Work buffers of the last decode step, for inspection (synchronous).
+ * Copies rows [0, rows) of one fp32 buffer to host memory:
+ *   LD_ACT_X    - the residual stream after the last layer   [rows, hidden]
+ *   LD_ACT_QKV  - the last layer's q|k|v projections, before the rotary
+ *                 embedding (q rows, then k, then v)        [rows, (n_q + 2 n_kv) d]
+ *   LD_ACT_ATTN - the last layer's attention output         [rows, n_q d]
+ *   LD_ACT_H    - the last layer's SwiGLU output             [rows, intermediate]
+ * From 16 rows the attention and SwiGLU outputs hold each value as the MFMA
+ * engine's split-bf16 pair (bf16(v) in the low half, bf16(v - bf16(v)) in the
+ * high half of the 32-bit word), the form in which the next stage reads them.
+ * Returns LD_EINVAL for an unknown buffer or rows outside [1, max_batch],
+ * LD_ESTATE before ld_alloc_kv. */
+enum { LD_ACT_X = 0, LD_ACT_QKV = 1, LD_ACT_ATTN = 2, LD_ACT_H = 3 };
+ld_status ld_read_activation(ld_model* m, int32_t which, int32_t rows, float* host_dst);
 
 /* Launch geometry: out[0] CUs, out[1] grid of the whole-kernel-wait kernels,
  * out[2] grid of the tile-flag kernels, out[3] persistent grid at batch 1,

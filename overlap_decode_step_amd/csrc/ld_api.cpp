@@ -19,6 +19,8 @@
 
 using namespace ld;
 
+constexpr int kModes = 4;  // LD_MODE_WAIT .. LD_MODE_GRAPH
+
 struct ld_model {
   ld_config cfg{};
   Dims D{};
@@ -49,8 +51,12 @@ struct ld_model {
   // cumulative counter totals (what every layer's counter will read once all
   // enqueued steps have finished)
   uint32_t tot_qkv = 0, tot_attn = 0, tot_o = 0, tot_gu = 0, tot_d = 0;
-  int gu_variant[65];
-  bool gu_tuned[65];
+  // SwiGLU tiling per (mode, batch size), and whether ld_tune or a loaded
+  // table chose it; tile_ms[mode][b] = {column-major, row-major} median ms
+  // per step measured by ld_tune
+  int gu_variant[kModes][65];
+  bool gu_tuned[kModes][65];
+  float tile_ms[kModes][65][2];
   int mlp_variant = LD_MLP_FUSED;  // unfused-MLP ablation (whole-kernel-wait mode)
   // launch geometry per mode: grid, threads per workgroup, LDS bytes, LDS for staged inputs
   int grid_wait = 0, grid_flags = 0, grid_mega[65] = {0};  // grid_mega indexed by nb
@@ -277,10 +283,12 @@ static ld_status setup_launch(ld_model* m) {
   HIPCHK(m, hipStreamCreateWithFlags(&m->s_cap, hipStreamNonBlocking));
   HIPCHK(m, hipEventCreateWithFlags(&m->ev_fork, hipEventDisableTiming));
   HIPCHK(m, hipEventCreateWithFlags(&m->ev_join, hipEventDisableTiming));
-  for (int b = 0; b <= 64; ++b) {
-    m->gu_variant[b] = kGuCol;
-    m->gu_tuned[b] = false;
-  }
+  for (int md = 0; md < kModes; ++md)
+    for (int b = 0; b <= 64; ++b) {
+      m->gu_variant[md][b] = kGuCol;
+      m->gu_tuned[md][b] = false;
+      m->tile_ms[md][b][0] = m->tile_ms[md][b][1] = 0.f;
+    }
   return LD_OK;
 }
 
@@ -581,7 +589,7 @@ static ld_status enqueue_step(ld_model* m, const int32_t* tokens, int32_t B, int
   // the same splits, so they add the same numbers in the same order
   if (m->mode != LD_MODE_FLAGS) P.D.split_len = m->split_len_full;
   P.S.T = step_split_len(B >= kMfmaMinBatch ? P.D.split_len : m->D.split_len, B);
-  P.S.gu_variant = m->gu_variant[B];
+  P.S.gu_variant = m->gu_variant[m->mode][B];
   P.S.inject = m->inject_next;
   m->inject_next = 0;
   const int L = m->D.L;
@@ -773,54 +781,42 @@ extern "C" ld_status ld_set_mlp_variant(ld_model* m, int32_t variant) {
 
 // ------------------------------------------------------------- tuning
 
-// Time one standalone SwiGLU launch of layer 0 with the given variant.
-static ld_status time_gu(ld_model* m, int B, int variant, int reps, float* ms_out) {
-  Params P = make_params(m);
-  // private counters: never disturbs the decode totals (whole-kernel-wait
-  // launches of one stage do not signal anyway)
-  P.K.ctr = m->tune_ctr;
-  P.K.lm_ctr = m->tune_ctr + kStageCtrs * kCtrWords;
-  P.K.split_ctr = P.K.lm_ctr + kCtrWords;
-  P.S.B = B;
-  P.S.T = step_split_len(m->D.split_len, B);
-  P.S.wait = 1;
-  P.S.gu_variant = variant;
-  P.S.x_cap = m->xcap_wait;
-  hipStream_t s = nullptr;
-  hipEvent_t a, b;
-  HIPCHK(m, hipEventCreate(&a));
-  HIPCHK(m, hipEventCreate(&b));
-  for (int i = 0; i < 2; ++i)
-    HIPCHK(m, launch_stage(kSGu, P, 0, m->grid_wait, m->thr_wait, m->smem_wait, s));
-  HIPCHK(m, hipEventRecord(a, s));
-  for (int i = 0; i < reps; ++i)
-    HIPCHK(m, launch_stage(kSGu, P, 0, m->grid_wait, m->thr_wait, m->smem_wait, s));
-  HIPCHK(m, hipEventRecord(b, s));
-  HIPCHK(m, hipEventSynchronize(b));
-  float ms = 0.f;
-  HIPCHK(m, hipEventElapsedTime(&ms, a, b));
-  (void)hipEventDestroy(a);
-  (void)hipEventDestroy(b);
-  *ms_out = ms / reps;
-  return LD_OK;
+static const char* mode_name(int mode) {
+  return mode == LD_MODE_WAIT ? "wait" : mode == LD_MODE_FLAGS ? "flags" : mode == LD_MODE_MEGA ? "mega" : "graph";
 }
 
 static ld_status write_table(ld_model* m, const char* path) {
   FILE* f = fopen(path, "w");
   if (!f) return fail(m, LD_EINVAL, std::string("cannot write ") + path);
   const ld_config& c = m->cfg;
-  fprintf(f, "{\"shape\": [%d, %d, %d, %d, %d, %d, %d], \"swiglu\": {", c.n_layers, c.hidden,
-          c.n_q_heads, c.n_kv_heads, c.head_dim, c.intermediate, c.vocab);
+  const int md = m->mode;
+  fprintf(f, "{\"shape\": [%d, %d, %d, %d, %d, %d, %d], \"mode\": \"%s\", \"swiglu\": {", c.n_layers,
+          c.hidden, c.n_q_heads, c.n_kv_heads, c.head_dim, c.intermediate, c.vocab, mode_name(md));
   bool first = true;
   for (int b = 1; b <= 64; ++b)
-    if (m->gu_tuned[b]) {
-      fprintf(f, "%s\"%d\": \"%s\"", first ? "" : ", ", b, m->gu_variant[b] == kGuRow ? "row" : "col");
+    if (m->gu_tuned[md][b]) {
+      fprintf(f, "%s\"%d\": \"%s\"", first ? "" : ", ", b, m->gu_variant[md][b] == kGuRow ? "row" : "col");
       first = false;
     }
-  fprintf(f, "}}\n");
+  fprintf(f, "}, \"ms_per_step_col_row\": [");
+  first = true;
+  for (int b = 1; b <= 64; ++b)
+    if (m->gu_tuned[md][b] && m->tile_ms[md][b][0] > 0.f) {
+      fprintf(f, "%s[%d, %.5f, %.5f]", first ? "" : ", ", b, m->tile_ms[md][b][0], m->tile_ms[md][b][1]);
+      first = false;
+    }
+  fprintf(f, "]}\n");
   fclose(f);
   return LD_OK;
 }
+
+// The tuning pass: for each batch size, whole decode steps in the model's
+// current mode, the two tilings alternating in rounds (kTuneRounds rounds of
+// kTuneSteps steps each, after warm-up), median ms per step of each; the
+// row-major tiling is kept only if its median beats the column-major one by
+// more than kTuneMargin (run-to-run noise on one GPU is below that).
+constexpr int kTuneRounds = 5, kTuneSteps = 3;
+constexpr float kTuneMargin = 0.01f;
 
 extern "C" ld_status ld_tune(ld_model* m, const int32_t* batches, int32_t n, const char* table_path) {
   if (!m) return fail(nullptr, LD_EINVAL, "null model");
@@ -829,18 +825,65 @@ extern "C" ld_status ld_tune(ld_model* m, const int32_t* batches, int32_t n, con
   for (int i = 0; i < n; ++i)
     if (batches[i] < 1 || batches[i] > m->D.max_batch)
       return fail(m, LD_EINVAL, "tuning batch outside [1, max_batch]");
+  const int md = m->mode;
+  const int maxB = m->D.max_batch;
+  const int p = std::min(m->D.max_seq - 1, 1024);
   HIPCHK(m, hipDeviceSynchronize());
-  for (int i = 0; i < n; ++i) {
-    const int B = batches[i];
-    float t_col = 0.f, t_row = 0.f;
-    ld_status st = time_gu(m, B, kGuCol, 10, &t_col);
-    if (st != LD_OK) return st;
-    st = time_gu(m, B, kGuRow, 10, &t_row);
-    if (st != LD_OK) return st;
-    m->gu_variant[B] = (t_row < t_col) ? kGuRow : kGuCol;
-    m->gu_tuned[B] = true;
+  // the steps' inputs and outputs (tokens 0.., every sequence at position p)
+  int32_t* dtok = nullptr;
+  float* dlog = nullptr;
+  HIPCHK(m, hipMalloc(&dtok, (size_t)2 * maxB * sizeof(int32_t)));
+  hipError_t he = hipMalloc(&dlog, (size_t)maxB * m->D.V * sizeof(float));
+  std::vector<int32_t> host(2 * maxB);
+  for (int b = 0; b < maxB; ++b) {
+    host[b] = b % m->D.V;
+    host[maxB + b] = p;
   }
-  HIPCHK(m, hipDeviceSynchronize());
+  if (he == hipSuccess) he = hipMemcpy(dtok, host.data(), host.size() * sizeof(int32_t), hipMemcpyHostToDevice);
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (he == hipSuccess) he = hipEventCreate(&e0);
+  if (he == hipSuccess) he = hipEventCreate(&e1);
+  ld_status st = he == hipSuccess ? LD_OK : fail(m, LD_EHIP, std::string("tuning setup: ") + hipGetErrorString(he));
+  for (int i = 0; i < n && st == LD_OK; ++i) {
+    const int B = batches[i];
+    std::vector<float> t[2];
+    auto run = [&](int variant, int steps) -> ld_status {
+      m->gu_variant[md][B] = variant;
+      for (int s = 0; s < steps; ++s) {
+        const ld_status r = enqueue_step(m, dtok, B, 1, dtok + maxB, dlog, nullptr, nullptr);
+        if (r != LD_OK) return r;
+      }
+      return LD_OK;
+    };
+    for (int v = 0; v < 2 && st == LD_OK; ++v) st = run(v == 0 ? kGuCol : kGuRow, 2);
+    for (int r = 0; r < kTuneRounds && st == LD_OK; ++r)
+      for (int v = 0; v < 2 && st == LD_OK; ++v) {
+        he = hipEventRecord(e0, nullptr);
+        if (he == hipSuccess) st = run(v == 0 ? kGuCol : kGuRow, kTuneSteps);
+        if (st == LD_OK && he == hipSuccess) he = hipEventRecord(e1, nullptr);
+        if (he == hipSuccess && st == LD_OK) he = hipEventSynchronize(e1);
+        float ms = 0.f;
+        if (he == hipSuccess && st == LD_OK) he = hipEventElapsedTime(&ms, e0, e1);
+        if (he != hipSuccess && st == LD_OK) st = fail(m, LD_EHIP, std::string("tuning: ") + hipGetErrorString(he));
+        t[v].push_back(ms / kTuneSteps);
+      }
+    if (st != LD_OK) break;
+    for (auto& x : t) std::sort(x.begin(), x.end());
+    const float col = t[0][kTuneRounds / 2], row = t[1][kTuneRounds / 2];
+    m->gu_variant[md][B] = (row < col * (1.0f - kTuneMargin)) ? kGuRow : kGuCol;
+    m->gu_tuned[md][B] = true;
+    m->tile_ms[md][B][0] = col;
+    m->tile_ms[md][B][1] = row;
+  }
+  (void)hipDeviceSynchronize();
+  if (e0) (void)hipEventDestroy(e0);
+  if (e1) (void)hipEventDestroy(e1);
+  (void)hipFree(dtok);
+  (void)hipFree(dlog);
+  if (st != LD_OK) return st;
+  int w = 0;
+  HIPCHK(m, hipMemcpy(&w, m->K.err, sizeof(int), hipMemcpyDeviceToHost));
+  if (w != 0) return ld_device_error(m);
   if (table_path) return write_table(m, table_path);
   return LD_OK;
 }
@@ -865,6 +908,17 @@ extern "C" ld_status ld_load_tuning(ld_model* m, const char* table_path) {
   size_t p = txt.find('{', sw);
   const size_t end = txt.find('}', p);
   if (p == std::string::npos || end == std::string::npos) return fail(m, LD_EINVAL, "malformed tuning table");
+  int md = m->mode;
+  const size_t mk = txt.find("\"mode\"");
+  if (mk != std::string::npos) {
+    const size_t q = txt.find('"', txt.find(':', mk) + 1);
+    if (q == std::string::npos) return fail(m, LD_EINVAL, "malformed tuning table");
+    if (txt.compare(q + 1, 5, "wait\"") == 0) md = LD_MODE_WAIT;
+    else if (txt.compare(q + 1, 6, "flags\"") == 0) md = LD_MODE_FLAGS;
+    else if (txt.compare(q + 1, 5, "mega\"") == 0) md = LD_MODE_MEGA;
+    else if (txt.compare(q + 1, 6, "graph\"") == 0) md = LD_MODE_GRAPH;
+    else return fail(m, LD_EINVAL, "unknown mode in tuning table");
+  }
   int parsed[65];
   bool have[65] = {false};
   while (true) {
@@ -882,8 +936,8 @@ extern "C" ld_status ld_load_tuning(ld_model* m, const char* table_path) {
   }
   for (int b = 1; b <= 64; ++b)
     if (have[b]) {
-      m->gu_variant[b] = parsed[b];
-      m->gu_tuned[b] = true;
+      m->gu_variant[md][b] = parsed[b];
+      m->gu_tuned[md][b] = true;
     }
   return LD_OK;
 }
@@ -961,17 +1015,37 @@ extern "C" ld_status ld_read_kv(ld_model* m, int32_t layer, int32_t seq, int32_t
   return LD_OK;
 }
 
+extern "C" ld_status ld_read_activation(ld_model* m, int32_t which, int32_t rows,
+                                        float* host_dst) {
+  if (!m) return fail(nullptr, LD_EINVAL, "null model");
+  if (!m->kv_ready) return fail(m, LD_ESTATE, "ld_alloc_kv first");
+  if (!host_dst || rows < 1 || rows > m->D.max_batch) return fail(m, LD_EINVAL, "bad rows or buffer");
+  const Dims& D = m->D;
+  const float* src = nullptr;
+  size_t width = 0;
+  switch (which) {
+    case LD_ACT_X: src = m->K.xa; width = D.H; break;
+    case LD_ACT_QKV: src = m->K.qkv; width = D.qkv_rows; break;
+    case LD_ACT_ATTN: src = m->K.ao; width = D.qd; break;
+    case LD_ACT_H: src = m->K.hbuf; width = D.I; break;
+    default: return fail(m, LD_EINVAL, "unknown work buffer");
+  }
+  HIPCHK(m, hipDeviceSynchronize());
+  HIPCHK(m, hipMemcpy(host_dst, src, (size_t)rows * width * 4, hipMemcpyDeviceToHost));
+  return LD_OK;
+}
+
 extern "C" ld_status ld_set_swiglu_variant(ld_model* m, int32_t batch, int32_t variant) {
   if (!m) return fail(nullptr, LD_EINVAL, "null model");
   if (batch < 1 || batch > 64 || (variant != LD_SWIGLU_COL && variant != LD_SWIGLU_ROW))
     return fail(m, LD_EINVAL, "bad batch or variant");
-  m->gu_variant[batch] = variant == LD_SWIGLU_ROW ? kGuRow : kGuCol;
+  for (int md = 0; md < kModes; ++md) m->gu_variant[md][batch] = variant == LD_SWIGLU_ROW ? kGuRow : kGuCol;
   return LD_OK;
 }
 
 extern "C" int32_t ld_get_swiglu_variant(const ld_model* m, int32_t batch) {
   if (!m || batch < 1 || batch > 64) return -1;
-  return m->gu_variant[batch] == kGuRow ? LD_SWIGLU_ROW : LD_SWIGLU_COL;
+  return m->gu_variant[m->mode][batch] == kGuRow ? LD_SWIGLU_ROW : LD_SWIGLU_COL;
 }
 
 extern "C" ld_status ld_set_watchdog(ld_model* m, double seconds) {

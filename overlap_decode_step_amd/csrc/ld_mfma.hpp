@@ -139,7 +139,8 @@ __device__ __forceinline__ void mfma_stage(const MatRows& mr, int ntile, int K, 
                                            bool norm, float eps, int B, uint32_t x_cap,
                                            const WaitFn& wait, Epe& epe, const PassEnd& pass_end,
                                            int wg, int nwg, char* smem,
-                                           const SplitK& sk = SplitK{nullptr, nullptr, 1}) {
+                                           const SplitK& sk = SplitK{nullptr, nullptr, 1},
+                                           bool row_major = false) {
   constexpr int MT = kMfmaTileMats / NT;  // tiles per wave per tile pass
   Scratch& sc = *reinterpret_cast<Scratch*>(smem);
   char* xbase = smem + kScratchBytes;
@@ -162,9 +163,15 @@ __device__ __forceinline__ void mfma_stage(const MatRows& mr, int ntile, int K, 
   const int cnt = wg < ntile ? (ntile - 1 - wg) / nwg + 1 : 0;     // this workgroup's tiles
   const int mt = cnt > wr ? (cnt - 1 - wr) / WR + 1 : 0;            // this wave's tiles
   const int ntpass = ((tpw + WR - 1) / WR + MT - 1) / MT;            // tile passes
-  const int prow = min(mfma_pass_rows(B, x_cap), NBT * 16);         // batch rows per pass
+  // batch rows per pass: as many as the staging area and the accumulators
+  // allow (column-major: every batch row meets each weight fragment while it
+  // is in registers), or 16 (row-major: one batch tile stays staged while the
+  // whole weight stream passes, once per tile).  The K chunk is the
+  // column-major one in both, so both add the same numbers in the same order.
+  const int prow_col = min(mfma_pass_rows(B, x_cap), NBT * 16);
+  const int prow = row_major ? 16 : prow_col;
   const int nbpass = (B + prow - 1) / prow;
-  const int KC = mfma_chunk(prow, K, x_cap), ldx = KC + kMfmaPad;  // row stride (4-byte words)
+  const int KC = mfma_chunk(prow_col, K, x_cap), ldx = KC + kMfmaPad;  // row stride (4-byte words)
   const int nchunk = (K + KC - 1) / KC;
   const int cs = KC / 32;                 // 32-wide K steps per chunk
   const int spc = (cs + WK - 1) / WK;     // this wave's step slots per chunk (wave wk takes

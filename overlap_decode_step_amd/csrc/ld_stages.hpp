@@ -707,12 +707,17 @@ __device__ __forceinline__ void stage_o(const Params& P, int l, int wg, int nwg,
 
 // -------------------------------------------------------- fused SwiGLU
 
-// A task holds kPairsGu (gate, up) row pairs.  Column-major tiling (weight
-// reuse, the default): the whole batch tile is multiplied with each weight
-// tile while it is in registers.  Row-major tiling (activation reuse): the
-// batch is cut into tiles of at most two rows, each kept in LDS while every
-// weight tile streams past it.  At batch <= 2 both tilings issue the same
-// loads.
+// A task holds kPairsGu (gate, up) row pairs.  The two tilings of the fused
+// stage ("Deep Kernel Fusion for Transformers", Key points, "Fusion scope"):
+//  - column-major (weight reuse, the default): each weight tile, once in
+//    registers, is multiplied with every staged batch row, so the weights
+//    stream once per step;
+//  - row-major (activation reuse): one batch tile (a single row on the VALU
+//    engine, 16 rows on the MFMA engine) stays staged while the whole weight
+//    stream passes it, so the weights stream once per batch tile (the repeat
+//    passes read what the first left in the memory-side cache when it fits).
+// Both add the same numbers in the same order (bitwise-equal results); they
+// coincide at batch 1 and, on the MFMA engine, at 16 rows.
 // SwiGLU task t: gate rows and up rows t * kPairsGu .. + kPairsGu (gate and
 // up lie in one layer block, so one buffer covers both).
 struct GuRows {
@@ -802,7 +807,7 @@ __device__ __forceinline__ void stage_gu(const Params& P, int l, int wg, int nwg
         }
       }
   };
-  const int bw = (P.S.gu_variant == kGuRow) ? min(2, batch_tile(P, K, NB)) : batch_tile(P, K, NB);
+  const int bw = (P.S.gu_variant == kGuRow) ? 1 : batch_tile(P, K, NB);
   if constexpr (NB >= kMfmaMinBatch) {
     (void)ring;
     (void)prefetched;
@@ -818,7 +823,8 @@ __device__ __forceinline__ void stage_gu(const Params& P, int l, int wg, int nwg
     mfma_stage<kMfmaNbt<NB, MR>, 2, MR>(MatRows{layer_w(P, l, 0), {rows.Wg, rows.Wu}, I, K}, (I + 15) / 16, K,
                            layer_w(P, l, 0), (uint32_t)(P.W.layer_stride * 2), src,
                            layer_w(P, l, P.W.o_mlp_norm), true, D.eps, B, P.S.x_cap, wait, epe,
-                           [](int, int) {}, wg, nwg, smem);
+                           [](int, int) {}, wg, nwg, smem, SplitK{nullptr, nullptr, 1},
+                           P.S.gu_variant == kGuRow);
   } else {
     gemv_run<NR, kUcGu, NB, kPfGu>(ws, ring, prefetched, src, layer_w(P, l, P.W.o_mlp_norm), true,
                                    D.eps, B, bw, wait, epi, smem,

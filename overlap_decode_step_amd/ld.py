@@ -4,8 +4,10 @@ Argument marshalling only: every step of the decode path runs in the HIP
 kernels of libld.so.  PyTorch supplies device memory and streams.  Importing
 this module fails loudly when the library has not been built.
 """
+import atexit
 import ctypes
 import os
+import weakref
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libld.so")
@@ -14,6 +16,7 @@ LD_OK, LD_EINVAL, LD_ENOMEM, LD_EHIP, LD_ETIMEOUT, LD_ESTATE, LD_EDEVICE = 0, -1
 LD_MODE_WAIT, LD_MODE_FLAGS, LD_MODE_MEGA, LD_MODE_GRAPH = 0, 1, 2, 3
 MODES = {"wait": LD_MODE_WAIT, "flags": LD_MODE_FLAGS, "mega": LD_MODE_MEGA, "graph": LD_MODE_GRAPH}
 LD_SWIGLU_COL, LD_SWIGLU_ROW = 0, 1
+LD_ACT_X, LD_ACT_QKV, LD_ACT_ATTN, LD_ACT_H = 0, 1, 2, 3
 LD_MLP_FUSED, LD_MLP_TWO_KERNELS, LD_MLP_FOUR_KERNELS = 0, 1, 2
 MLP_VARIANTS = {"fused": LD_MLP_FUSED, "two": LD_MLP_TWO_KERNELS, "four": LD_MLP_FOUR_KERNELS}
 (LD_W_EMBED, LD_W_ATTN_NORM, LD_W_Q, LD_W_K, LD_W_V, LD_W_O, LD_W_MLP_NORM, LD_W_GATE, LD_W_UP,
@@ -66,6 +69,7 @@ def _load():
         "ld_set_watchdog": (S, [P, D]),
         "ld_debug_inject_stall": (S, [P]),
         "ld_launch_info": (S, [P, P, I32]),
+        "ld_read_activation": (S, [P, I32, I32, P]),
         "ld_trace_bytes": (ctypes.c_size_t, [CP]),
         "ld_set_trace": (S, [P, P, ctypes.c_size_t]),
     }
@@ -198,6 +202,10 @@ def ld_set_trace(m, dev_buf, nbytes):
     return _check(LIB.ld_set_trace(m, dev_buf, nbytes), m)
 
 
+def ld_read_activation(m, which, rows, host_ptr):
+    return _check(LIB.ld_read_activation(m, which, rows, host_ptr), m)
+
+
 def ld_launch_info(m):
     out = (ctypes.c_int32 * 6)()
     _check(LIB.ld_launch_info(m, out, 6), m)
@@ -206,6 +214,21 @@ def ld_launch_info(m):
 
 
 # ---- convenience owner of the device buffers (torch for memory and streams)
+
+# Models still alive when the interpreter exits are freed by an exit hook,
+# before Python tears its modules down.  Left to garbage collection during
+# that teardown, ld_free (a device synchronisation, stream, event and graph
+# destruction) could run after the HIP runtime, or a profiler attached to
+# it, had already shut down.  The hook is registered when the first model
+# is made, after torch has registered its own, so it runs before them (exit
+# hooks run last-in, first-out).
+_LIVE = weakref.WeakSet()
+_HOOKED = []
+
+
+def _free_live_models():
+    for m in list(_LIVE):
+        m.free()
 
 class Model:
     """A model whose weight and KV arenas are torch uint8 buffers on cuda:0."""
@@ -220,6 +243,10 @@ class Model:
             raise LdError(LD_EINVAL, "unsupported shape")
         self.wbuf = torch.empty(n, dtype=torch.uint8, device=device)
         self.h = ld_init_weights(shape, self.wbuf.data_ptr(), n, seed, w_std, self.stream())
+        if not _HOOKED:
+            atexit.register(_free_live_models)
+            _HOOKED.append(True)
+        _LIVE.add(self)
         self.kbuf = None
         self.max_batch = self.max_seq = 0
 
@@ -280,6 +307,16 @@ class Model:
         v = np.empty((npos, d), dtype=np.uint16)
         ld_read_kv(self.h, layer, seq, kv_head, pos0, npos, k.ctypes.data, v.ctypes.data)
         return k, v
+
+    def read_activation(self, which, rows):
+        import numpy as np
+        s = self.shape
+        qd, kvd = s["n_q_heads"] * s["head_dim"], s["n_kv_heads"] * s["head_dim"]
+        width = {LD_ACT_X: s["hidden"], LD_ACT_QKV: qd + 2 * kvd, LD_ACT_ATTN: qd,
+                 LD_ACT_H: s["intermediate"]}[which]
+        out = np.empty((rows, width), dtype=np.float32)
+        ld_read_activation(self.h, which, rows, out.ctypes.data)
+        return out
 
     def free(self):
         if getattr(self, "h", None):

@@ -210,10 +210,11 @@ def test_ragged_shape_multi_split(ld, orc, mode):
     m.free()
 
 
-@pytest.mark.parametrize("B", [2, 5, 8, 16, 27, 45])
+@pytest.mark.parametrize("B", [2, 5, 8, 12, 15, 16, 27, 45])
 def test_tiny_batches(ld, orc, B):
     # every batch build: 2, 8 and 16 fill theirs; 5, 27 and 45 leave ragged
-    # batch tails in the 8-, 32- and 64-row builds
+    # batch tails in the 8-, 32- and 64-row builds; 12 and 15 take the 8-row
+    # VALU build in two batch passes (the second one ragged)
     shape = W.TINY
     prefill = W.kv_lengths(B, 1, 200)
     om = orc.model(shape, seed=W.SEED_WEIGHTS, w_std=0.02)
@@ -292,73 +293,97 @@ def test_llama1b_batch_sweep_sampled(ld, orc, llama1b, B):
 
 # -------------------------------------- 8B and 70B widths, two layers
 
+_wide_oracles = {}
+
+
+def _wide_oracle(orc, name, w_std):
+    """The oracle's two-layer model of a wide shape (shared by its tests)."""
+    if name not in _wide_oracles:
+        _wide_oracles.clear()  # the 70B width's two layers take about 8 GB of host memory
+        shape = dict(W.SHAPES[name], n_layers=2)
+        print(f"{name} x2 layers: oracle weights", flush=True)
+        _wide_oracles[name] = orc.model(shape, seed=W.SEED_WEIGHTS, w_std=w_std)
+    return _wide_oracles[name]
+
+
+def _check_sampled(ld, orc, m, om, shape, B, prefill, modes, seqs, tag, max_seq):
+    """One step of B sequences (seeded first tokens) at positions `prefill`
+    in each mode; sequences `seqs` checked against the oracle's decode."""
+    toks = W.first_tokens(B, shape["vocab"])
+    refs = {}
+    for b in seqs:
+        okv = orc.kv(shape, 1, max_seq, seed=W.SEED_KV, kv_std=1.0, prefill=[prefill[b]], seq0=b)
+        refs[b] = orc.decode_one(om, okv, 0, toks[b], prefill[b])
+    run = GpuRunner(m, shape["vocab"], B)
+    fill = list(prefill) + [1] * (m.max_batch - B)
+    for mode in modes:
+        m.fill_kv(W.SEED_KV, 1.0, fill)
+        m.set_mode(mode)
+        lg, nx = run.step(toks, prefill)
+        for b, (lg_ref, nref) in refs.items():
+            err, rel, _ = check_row(lg[b], lg_ref, nx[b], nref, f"{tag} B={B} mode={mode} seq={b}")
+            print(f"{tag} B={B} mode={mode} seq={b} max_abs={err:.2e} rel={rel:.2e}", flush=True)
+
+
+WIDE_CASES = [
+    # (shape, weight std, batch sizes): batch 1 is checked in every mode, the
+    # others with the first and last sequence of the batch
+    ("llama1b", 0.02, (64,)),
+    ("llama8b", 0.02, (1, 2, 8, 16, 64)),
+    ("llama70b", 0.01, (1, 4, 8, 16)),
+    ("llama70b_tp8", 0.01, (1, 8, 16)),
+]
+
+
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("name,w_std", [("llama8b", 0.02), ("llama70b", 0.01),
-                                         ("llama70b_tp8", 0.01)])
-def test_wide_shapes_two_layers(ld, orc, name, w_std):
+@pytest.mark.parametrize("name,w_std,batches", WIDE_CASES, ids=[c[0] for c in WIDE_CASES])
+def test_wide_shapes_two_layers(ld, orc, name, w_std, batches):
     # The Llama-8B and Llama-70B shapes at full width (hidden size, heads of
-    # 128, SwiGLU width, 128256-token vocabulary, untied LM head), and one
-    # GPU's 8-way tensor-parallel share of the 70B shape (8 Q heads and 1 KV
-    # head, SwiGLU 3584, a 16032-row vocabulary shard), with two
-    # layers, so the oracle finishes in seconds; KV length 1024 as in those
-    # workloads.  Batch 1 in every mode, then batch 16 (the MFMA engine) with
-    # sequences 0 and 15 checked.  At the 70B width the tile-flag mode is
-    # refused (the Down stage's staged input row, 28672 fp32, does not fit in
-    # half the LDS, so two stage kernels cannot share a CU): that refusal is
-    # checked instead.
+    # 128, SwiGLU width, 128256-token vocabulary, untied LM head), one GPU's
+    # 8-way tensor-parallel share of the 70B shape (8 Q heads and 1 KV head,
+    # SwiGLU 3584, a 16032-row vocabulary shard) and the Llama-1B shape at 64
+    # rows, each with two layers so the oracle finishes in seconds; KV length
+    # 1024.  Every mode at every batch size: the VALU engine's 1-, 2-, 4- and
+    # 8-row builds (at the 70B width an 8-row SwiGLU wave holds 14 tasks of 8
+    # results, more than its 64 store slots, so held stores are also written
+    # mid-stream) and the MFMA engine's 16-row builds and 64-row builds (the
+    # whole-kernel-wait and graph modes run their two-waves-per-SIMD split-K
+    # builds there, the tile-flag mode its 32-row passes).  At the 70B width
+    # the tile-flag mode is refused (the Down stage's staged input row, 28672
+    # fp32, does not fit in half the LDS, so two stage kernels cannot share a
+    # CU): that refusal is checked instead.
     shape = dict(W.SHAPES[name], n_layers=2)
     modes = MODES if name != "llama70b" else ("wait", "mega", "graph")
-    print(f"{name} x2 layers: oracle weights", flush=True)
-    om = orc.model(shape, seed=W.SEED_WEIGHTS, w_std=w_std)
-    okv = orc.kv(shape, 1, 1040, seed=W.SEED_KV, kv_std=1.0, prefill=[1024])
-    tok0 = W.first_tokens(1, shape["vocab"])[0]
-    ref = oracle_trajectory(orc, om, okv, tok0, 1024, 1)
+    om = _wide_oracle(orc, name, w_std)
+    Bmax = max(batches)
     print(f"{name} x2 layers: GPU model", flush=True)
-    m = gpu_model(ld, shape, 16, 1040, [1024] * 16, w_std=w_std)
+    m = gpu_model(ld, shape, Bmax, 1040, [1024] * Bmax, w_std=w_std)
     if "flags" not in modes:
         with pytest.raises(ld.LdError) as ei:
             m.set_mode("flags")
         assert ei.value.status == ld.LD_EINVAL
-    run = GpuRunner(m, shape["vocab"], 1)
-    for mode in modes:
-        m.fill_kv(W.SEED_KV, 1.0, [1024] * 16)
-        m.set_mode(mode)
-        tok, pos, lg_ref, nref = ref[0]
-        lg, nx = run.step([tok], [pos])
-        err, rel, _ = check_row(lg[0], lg_ref, nx[0], nref, f"{name} B=1 mode={mode}")
-        print(f"{name} x2 B=1 mode={mode} max_abs={err:.2e} rel={rel:.2e}", flush=True)
-    B = 16
-    toks = W.first_tokens(B, shape["vocab"])
-    refs = {}
-    for b in (0, B - 1):
-        okv_b = orc.kv(shape, 1, 1040, seed=W.SEED_KV, kv_std=1.0, prefill=[1024], seq0=b)
-        refs[b] = orc.decode_one(om, okv_b, 0, toks[b], 1024)
-    run16 = GpuRunner(m, shape["vocab"], B)
-    for mode in modes[1:]:
-        m.fill_kv(W.SEED_KV, 1.0, [1024] * B)
-        m.set_mode(mode)
-        lg, nx = run16.step(toks, [1024] * B)
-        for b, (lg_ref, nref) in refs.items():
-            err, rel, _ = check_row(lg[b], lg_ref, nx[b], nref, f"{name} B={B} mode={mode} seq={b}")
-            print(f"{name} x2 B={B} mode={mode} seq={b} max_abs={err:.2e} rel={rel:.2e}", flush=True)
-    # batch 8: the VALU engine's 8-row kernels, whose results are held in
-    # lane slots until a wave's stream ends; at the 70B width a SwiGLU wave has
-    # 14 tasks of 8 results, more than the 64 slots, so the held stores are
-    # also written mid-stream
-    B8 = 8
-    toks8 = W.first_tokens(B8, shape["vocab"])
-    refs8 = {}
-    for b in (0, B8 - 1):
-        okv_b = orc.kv(shape, 1, 1040, seed=W.SEED_KV, kv_std=1.0, prefill=[1024], seq0=b)
-        refs8[b] = orc.decode_one(om, okv_b, 0, toks8[b], 1024)
-    run8 = GpuRunner(m, shape["vocab"], B8)
-    for mode in ("wait", "mega"):
-        m.fill_kv(W.SEED_KV, 1.0, [1024] * B)
-        m.set_mode(mode)
-        lg, nx = run8.step(toks8, [1024] * B8)
-        for b, (lg_ref, nref) in refs8.items():
-            err, rel, _ = check_row(lg[b], lg_ref, nx[b], nref, f"{name} B={B8} mode={mode} seq={b}")
-            print(f"{name} x2 B={B8} mode={mode} seq={b} max_abs={err:.2e} rel={rel:.2e}", flush=True)
+    for B in batches:
+        seqs = (0,) if B == 1 else (0, B - 1)
+        _check_sampled(ld, orc, m, om, shape, B, [1024] * B, modes, seqs, f"{name} x2", 1040)
+    m.free()
+
+
+@pytest.mark.timeout(900)
+def test_long_context_70b_width(ld, orc):
+    # Long generation at the 70B width ("Deep Kernel Fusion for
+    # Transformers", Key points, "Long generation": outputs up to 16384
+    # tokens): two layers, KV length 16384, so attention splits every
+    # sequence's context 64-way (batch 1: 257 splits of at most 64 positions
+    # per kv head; batch 16: ranges of up to 256 positions) and the combine
+    # reads its partial results in several rounds.
+    name, w_std, n = "llama70b", 0.01, 16384
+    shape = dict(W.SHAPES[name], n_layers=2)
+    om = _wide_oracle(orc, name, w_std)
+    m = gpu_model(ld, shape, 16, n + 8, [n] * 16, w_std=w_std)
+    _check_sampled(ld, orc, m, om, shape, 1, [n], ("wait", "mega", "graph"), (0,),
+                   f"{name} x2 KV {n}", n + 8)
+    _check_sampled(ld, orc, m, om, shape, 16, [n] * 16, ("wait", "mega"), (0, 15),
+                   f"{name} x2 KV {n}", n + 8)
     m.free()
 
 
@@ -611,25 +636,104 @@ def test_watchdog_turns_a_stall_into_an_error(ld, tiny_ref, mode):
     m.free()
 
 
-def test_tuning_table_roundtrip(ld, tmp_path, tiny_ref):
+def test_tuning_table_roundtrip(ld, tmp_path):
+    # ld_tune times whole decode steps with each SwiGLU tiling, writes the
+    # winners to a table, and ld_load_tuning restores them.
     shape = W.TINY
-    m = gpu_model(ld, shape, 16, 256, [128] * 16)
+    m = gpu_model(ld, shape, 32, 256, [128] * 32)
+    m.set_mode("mega")
     path = str(tmp_path / "tune.json")
-    ld.ld_tune(m.h, [1, 4, 16], path)
+    ld.ld_tune(m.h, [1, 4, 32], path)
     txt = open(path).read()
-    assert '"swiglu"' in txt and '"16"' in txt
-    chosen = {b: ld.ld_get_swiglu_variant(m.h, b) for b in (1, 4, 16)}
-    for b in (1, 4, 16):
+    assert '"swiglu"' in txt and '"32"' in txt
+    chosen = {b: ld.ld_get_swiglu_variant(m.h, b) for b in (1, 4, 32)}
+    assert all(v in (ld.LD_SWIGLU_COL, ld.LD_SWIGLU_ROW) for v in chosen.values())
+    for b in (1, 4, 32):
         ld.ld_set_swiglu_variant(m.h, b, 1 - chosen[b])
     ld.ld_load_tuning(m.h, path)
-    assert {b: ld.ld_get_swiglu_variant(m.h, b) for b in (1, 4, 16)} == chosen
-    # both tilings compute the same sums in the same order: bitwise equal logits
-    run = GpuRunner(m, shape["vocab"], 16)
-    toks = W.first_tokens(16, shape["vocab"])
-    outs = []
-    for variant in (ld.LD_SWIGLU_COL, ld.LD_SWIGLU_ROW):
-        ld.ld_set_swiglu_variant(m.h, 16, variant)
-        m.fill_kv(W.SEED_KV, 1.0, [128] * 16)
-        outs.append(run.step(toks, [128] * 16)[0])
-    assert np.array_equal(outs[0], outs[1])
+    assert {b: ld.ld_get_swiglu_variant(m.h, b) for b in (1, 4, 32)} == chosen
+    m.free()
+
+
+ROW_CASES = [("tiny", 2), ("tiny", 4), ("tiny", 8), ("tiny", 12), ("tiny", 32), ("tiny", 64),
+             ("llama1b", 4), ("llama1b", 8)]
+
+
+@pytest.mark.parametrize("name,B", ROW_CASES, ids=[f"{n}-B{b}" for n, b in ROW_CASES])
+def test_swiglu_row_major_tiling(ld, orc, name, B):
+    # The row-major SwiGLU tiling (activation reuse: one batch tile, a single
+    # row on the VALU engine or 16 rows on the MFMA engine, stays staged while
+    # every weight tile streams past it, so the weights stream once per batch
+    # tile) against the oracle in every mode, and bitwise against the
+    # column-major tiling (weight reuse: all batch rows per weight tile): both
+    # add the same numbers in the same order.
+    shape = W.SHAPES[name]
+    maxs = 1040 if name == "llama1b" else 256
+    prefill = W.kv_lengths(B, 256, 1024) if name == "llama1b" else W.kv_lengths(B, 1, 200)
+    seqs = range(B) if name == "tiny" else (0, B - 1)
+    om = orc.model(shape, seed=W.SEED_WEIGHTS, w_std=0.02)
+    toks = W.first_tokens(B, shape["vocab"])
+    refs = {}
+    for b in seqs:
+        okv = orc.kv(shape, 1, maxs, seed=W.SEED_KV, kv_std=1.0, prefill=[prefill[b]], seq0=b)
+        refs[b] = orc.decode_one(om, okv, 0, toks[b], prefill[b])
+    m = gpu_model(ld, shape, B, maxs, prefill)
+    run = GpuRunner(m, shape["vocab"], B)
+    for mode in MODES:
+        m.set_mode(mode)
+        outs = {}
+        for variant in (ld.LD_SWIGLU_ROW, ld.LD_SWIGLU_COL):
+            ld.ld_set_swiglu_variant(m.h, B, variant)
+            m.fill_kv(W.SEED_KV, 1.0, prefill)
+            lg, nx = run.step(toks, prefill)
+            outs[variant] = lg
+            if variant == ld.LD_SWIGLU_ROW:
+                for b, (ref, rn) in refs.items():
+                    err, rel, _ = check_row(lg[b], ref, nx[b], rn, f"{name} B={B} row-major mode={mode} seq={b}")
+                print(f"{name} B={B} row-major mode={mode} last seq max_abs={err:.2e} rel={rel:.2e}",
+                      flush=True)
+        assert np.array_equal(outs[ld.LD_SWIGLU_ROW], outs[ld.LD_SWIGLU_COL]), \
+            f"{name} B={B} mode={mode}: row- and column-major tilings differ"
+    m.free()
+
+
+@pytest.mark.parametrize("B", [1, 16])
+def test_position_zero_attention_returns_v(ld, orc, B):
+    # An empty cache: the first token attends to itself only, with weight
+    # e^0 / e^0 = 1, so every head's attention output is exactly f32(bf16(v))
+    # of its kv head (the stored V row), in every mode; the logits match the
+    # oracle's.  From 16 rows the attention output is stored as the MFMA
+    # engine's split-bf16 pair, whose low half is then exactly zero.
+    shape = W.TINY
+    om = orc.model(shape, seed=W.SEED_WEIGHTS, w_std=0.02)
+    toks = W.first_tokens(B, shape["vocab"])
+    okv = orc.kv(shape, 1, 64, seed=W.SEED_KV, kv_std=1.0, prefill=[0])
+    ref, rn = orc.decode_one(om, okv, 0, toks[0], 0)
+    m = gpu_model(ld, shape, B, 64, [0] * B)
+    run = GpuRunner(m, shape["vocab"], B)
+    d, nq, nkv = shape["head_dim"], shape["n_q_heads"], shape["n_kv_heads"]
+    group, qd = nq // nkv, nq * d
+    for mode in MODES:
+        m.fill_kv(W.SEED_KV, 1.0, [0] * B)
+        m.set_mode(mode)
+        lg, nx = run.step(toks, [0] * B)
+        check_row(lg[0], ref, nx[0], rn, f"position 0 B={B} mode={mode}")
+        qkv = m.read_activation(ld.LD_ACT_QKV, B)
+        ao = m.read_activation(ld.LD_ACT_ATTN, B)
+        last = shape["n_layers"] - 1
+        for b in range(B):
+            v = qkv[b, qd + nkv * d:]  # the last layer's v projections
+            _, vc = m.read_kv(last, b, 0, 0, 1)
+            vbf = np.concatenate([m.read_kv(last, b, h, 0, 1)[1][0] for h in range(nkv)])
+            assert np.array_equal(vbf, ((v.view(np.uint32) + 0x7FFF + ((v.view(np.uint32) >> 16) & 1))
+                                        >> 16).astype(np.uint16)), "stored V is not bf16(v)"
+            expect = (vbf.astype(np.uint32) << 16).view(np.float32)
+            for hq in range(nq):
+                got = ao[b, hq * d:(hq + 1) * d]
+                want = expect[(hq // group) * d:(hq // group + 1) * d]
+                if B >= 16:
+                    bits = got.view(np.uint32)
+                    assert np.all(bits >> 16 == 0), f"mode={mode} seq={b} head={hq}: nonzero low part"
+                    got = ((bits & 0xFFFF) << 16).view(np.float32)
+                assert np.array_equal(got, want), f"mode={mode} seq={b} head={hq}: output is not V"
     m.free()
