@@ -257,6 +257,37 @@ def multi_token_bench(shape_name, B, M, steps, warmup, modes):
     return out
 
 
+def tune_tables(shape_name, batches, modes):
+    """The offline SwiGLU tiling choice (ld_tune) at one shape: for each mode,
+    whole decode steps with each tiling at every batch size (KV length 1024,
+    or 512 at the Llama-1B shape); returns {mode: table} as ld_tune writes it."""
+    import tempfile
+    import torch
+    from overlap_decode_step_amd import ld
+    from synth import workloads as W
+    shape = W.SHAPES[shape_name]
+    w_std = W.WORKLOADS["llama70b"]["w_std"] if shape_name.startswith("llama70b") else 0.02
+    prefill = 512 if shape_name == "llama1b" else 1024
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    m = ld.Model(shape, seed=W.SEED_WEIGHTS, w_std=w_std)
+    m.alloc_kv(max(batches), prefill + 1)
+    m.fill_kv(W.SEED_KV, 1.0, [prefill] * max(batches))
+    out = {}
+    for mode in modes:
+        try:
+            m.set_mode(mode)
+        except ld.LdError as e:
+            print(f"# tune mode={mode} refused: {e}", file=sys.stderr, flush=True)
+            continue
+        with tempfile.NamedTemporaryFile("r", suffix=".json") as f:
+            ld.ld_tune(m.h, list(batches), f.name)
+            out[mode] = json.loads(open(f.name).read())
+        print(f"# tune {shape_name} mode={mode}: {json.dumps(out[mode])}", file=sys.stderr, flush=True)
+    m.free()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -283,12 +314,22 @@ def main():
                          "against its two- and four-kernel unfused forms (batch < 16)")
     ap.add_argument("--prefill", type=int, default=None,
                     help="KV prefill per sequence (default 512 for llama1b, else 1024)")
+    ap.add_argument("--tune", default=None,
+                    help="only run the offline SwiGLU tiling choice at this shape for the "
+                         "comma-separated batch sizes of --tune-batches, in every mode")
+    ap.add_argument("--tune-batches", default="1,2,16,64")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU only; --gpus must be 1", file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.tune:
+        batches = [int(b) for b in args.tune_batches.split(",")]
+        tables = tune_tables(args.tune, batches, ["wait", "flags", "mega", "graph"])
+        print(json.dumps({"swiglu_tuning": args.tune, "batches": batches, "tables": tables}),
+              flush=True)
         return
     if args.tokens_per_seq > 1:
         M, B = args.tokens_per_seq, args.batch
