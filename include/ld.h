@@ -126,6 +126,20 @@ ld_status ld_alloc_kv(ld_model* m, void* dev_buf, size_t bytes, int32_t max_batc
 ld_status ld_fill_kv(ld_model* m, uint64_t seed, float kv_std, const int32_t* prefill_len,
                      void* stream);
 
+/* ld_fill_kv without any device allocation, for callers that cannot
+ * allocate (code under stream capture, serving loops, harnesses that forbid
+ * hipMalloc): the same fill, bit for bit, but the device copy of the
+ * lengths lives in a static device array of the library (64 int32 per GPU,
+ * held until the process ends) instead of a buffer from hipMalloc.  The
+ * lengths are passed to the device as kernel arguments, so prefill_len (host
+ * [max_batch]) may be reused when the call returns.  Asynchronous on
+ * `stream`; no allocation, free or synchronisation.  Every call on one GPU
+ * shares that GPU's array: calls that overlap on one GPU (different streams)
+ * race.  Returns LD_EINVAL if max_batch exceeds 64 or a length lies outside
+ * [0, max_seq], LD_ESTATE before ld_alloc_kv, LD_EHIP on a launch failure. */
+ld_status ld_fill_kv_static(ld_model* m, uint64_t seed, float kv_std, const int32_t* prefill_len,
+                            void* stream);
+
 ld_status ld_set_mode(ld_model* m, ld_mode mode);
 
 /* One decode step for `batch` sequences (1 <= batch <= max_batch).

@@ -68,6 +68,10 @@ struct ld_model {
   // modes (a full CU's LDS), used from 16 rows; the tile-flag mode and every
   // step below 16 rows use D.split_len (half a CU's LDS)
   int split_len_full = 0;
+  // device address of the allocation-free KV fill's length array on this
+  // model's device (set up at init), and its capacity
+  int32_t* scratch_lens = nullptr;
+  int scratch_cap = 0;
   uint64_t watchdog_ticks = 0;
   double wall_khz = 100000.0;
   uint32_t inject_next = 0;
@@ -279,6 +283,7 @@ static ld_status setup_launch(ld_model* m) {
       khz > 0)
     m->wall_khz = (double)khz;
   m->watchdog_ticks = (uint64_t)(m->wall_khz * 1000.0 * 2.0);  // 2 s
+  HIPCHK(m, scratch_lens_ptr(&m->scratch_lens, &m->scratch_cap));
   HIPCHK(m, hipStreamCreateWithFlags(&m->s1, hipStreamNonBlocking));
   HIPCHK(m, hipStreamCreateWithFlags(&m->s_cap, hipStreamNonBlocking));
   HIPCHK(m, hipEventCreateWithFlags(&m->ev_fork, hipEventDisableTiming));
@@ -526,6 +531,30 @@ extern "C" ld_status ld_fill_kv(ld_model* m, uint64_t seed, float kv_std,
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   (void)hipFree(len_dev);
   if (e != hipSuccess) return fail(m, LD_EHIP, std::string("KV fill failed: ") + hipGetErrorString(e));
+  return LD_OK;
+}
+
+extern "C" ld_status ld_fill_kv_static(ld_model* m, uint64_t seed, float kv_std,
+                                       const int32_t* prefill_len, void* stream) {
+  if (!m) return fail(nullptr, LD_EINVAL, "null model");
+  if (!m->kv_ready) return fail(m, LD_ESTATE, "ld_alloc_kv first");
+  if (!prefill_len) return fail(m, LD_EINVAL, "null prefill_len");
+  const int B = m->D.max_batch;
+  if (B > m->scratch_cap)
+    return fail(m, LD_EINVAL, "max_batch exceeds the static length array (" +
+                                  std::to_string(m->scratch_cap) + " entries)");
+  for (int b = 0; b < B; ++b)
+    if (prefill_len[b] < 0 || prefill_len[b] > m->D.max_seq)
+      return fail(m, LD_EINVAL, "prefill length outside [0, max_seq]");
+  if (m->scratch_lens == nullptr) return fail(m, LD_EHIP, "static length array unavailable");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  HIPCHK(m, launch_put_lens(m->scratch_lens, prefill_len, B, s));
+  const float kappa = ls_kappa(kv_std);
+  const int64_t per_layer = (int64_t)B * m->D.nkv * m->D.max_seq * m->D.d;
+  for (int l = 0; l < m->D.L; ++l)
+    HIPCHK(m, launch_gen_kv(m->K.kc + l * per_layer, m->K.vc + l * per_layer, m->scratch_lens, B,
+                            m->D.nkv, m->D.max_seq, m->D.d, ls_key(seed, LS_T_KCACHE(l)),
+                            ls_key(seed, LS_T_VCACHE(l)), kappa, s));
   return LD_OK;
 }
 

@@ -10,6 +10,8 @@
 //  k_gen_normal / k_fill16 / k_gen_kv : seeded synthetic inputs.
 // All decode kernels use dynamic LDS: a scratch area, then the staged input
 // vectors or the attention tiles.
+#include <mutex>
+
 #include "ld_launch.h"
 #include "ld_stages.hpp"
 #include "../../synth/ld_synth.h"
@@ -158,6 +160,59 @@ __global__ void k_gen_kv(uint16_t* kc, uint16_t* vc, const int* len, int n_kv, i
     kc[base + e] = ls_normal_bf16(kkey, idx, kappa);
     vc[base + e] = ls_normal_bf16(vkey, idx, kappa);
   }
+}
+
+// ------------------------------------------------ allocation-free KV fill
+//
+// The KV fill reads the prefill lengths from device memory.  ld_fill_kv
+// copies them into a buffer from hipMalloc; its allocation-free variant keeps
+// them in this file-scope device array instead (every GPU the library runs on
+// holds its own copy until the process ends).  Host code reaches the array
+// only through the address hipGetSymbolAddress returns for the current
+// device; its name is not a device address in host code.  Every call on a
+// device shares that device's copy, so such calls that overlap on one device
+// (on different streams) race.
+constexpr int kScratchLens = 64;  // lengths at most (max_batch <= 64)
+static __device__ __align__(256) int32_t scratch[kScratchLens];
+
+struct ScratchLens {
+  int32_t v[kScratchLens];
+};
+
+// Writes the call's n lengths (passed by value) and zeros after them.
+__global__ void k_put_lens(int32_t* dst, ScratchLens lens, int n) {
+  const int i = threadIdx.x;
+  if (i < kScratchLens) dst[i] = i < n ? lens.v[i] : 0;
+}
+
+constexpr int kMaxScratchDevices = 64;
+static std::mutex g_scratch_mu;
+static int32_t* g_scratch[kMaxScratchDevices] = {};
+
+hipError_t scratch_lens_ptr(int32_t** out, int* capacity) {
+  *out = nullptr;
+  *capacity = kScratchLens;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch[dev] = static_cast<int32_t*>(p);
+  }
+  *out = g_scratch[dev];
+  return hipSuccess;
+}
+
+hipError_t launch_put_lens(int32_t* dst, const int32_t* host_lens, int n, hipStream_t s) {
+  if (n < 0 || n > kScratchLens) return hipErrorInvalidValue;
+  ScratchLens lens{};
+  for (int i = 0; i < n; ++i) lens.v[i] = host_lens[i];
+  hipLaunchKernelGGL(k_put_lens, dim3(1), dim3(kScratchLens), 0, s, dst, lens, n);
+  return hipGetLastError();
 }
 
 // ------------------------------------------------------------ wrappers

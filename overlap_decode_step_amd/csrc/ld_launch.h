@@ -29,6 +29,13 @@ size_t best_bytes();
 hipError_t launch_gen_normal(uint16_t* dst, int64_t n, uint64_t key, uint64_t index0, float kappa,
                              hipStream_t s);
 hipError_t launch_fill16(uint16_t* dst, int64_t n, uint16_t v, hipStream_t s);
+// The allocation-free KV fill's device copy of the prefill lengths (a
+// file-scope device array of `capacity` int32) for the current device: its
+// address, looked up once per device.
+hipError_t scratch_lens_ptr(int32_t** out, int* capacity);
+// Write n <= capacity lengths (from host memory, passed as kernel arguments)
+// and zeros after them into that array, on stream s.
+hipError_t launch_put_lens(int32_t* dst, const int32_t* host_lens, int n, hipStream_t s);
 hipError_t launch_gen_kv(uint16_t* kc, uint16_t* vc, const int* len_dev, int batch, int n_kv,
                          int max_seq, int d, uint64_t kkey, uint64_t vkey, float kappa,
                          hipStream_t s);

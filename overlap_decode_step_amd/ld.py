@@ -51,6 +51,7 @@ def _load():
         "ld_kv_bytes": (ctypes.c_size_t, [CP, I32, I32]),
         "ld_alloc_kv": (S, [P, P, ctypes.c_size_t, I32, I32]),
         "ld_fill_kv": (S, [P, U64, F, P, P]),
+        "ld_fill_kv_static": (S, [P, U64, F, P, P]),
         "ld_set_mode": (S, [P, S]),
         "ld_decode_step": (S, [P, P, I32, P, P, P, P]),
         "ld_decode_step_tokens": (S, [P, P, I32, I32, P, P, P, P]),
@@ -117,6 +118,11 @@ def ld_alloc_kv(m, dev_buf, nbytes, max_batch, max_seq):
 def ld_fill_kv(m, seed, kv_std, prefill_len, stream=0):
     arr = (ctypes.c_int32 * len(prefill_len))(*prefill_len)
     return _check(LIB.ld_fill_kv(m, seed, kv_std, arr, stream), m)
+
+
+def ld_fill_kv_static(m, seed, kv_std, prefill_len, stream=0):
+    arr = (ctypes.c_int32 * len(prefill_len))(*prefill_len)
+    return _check(LIB.ld_fill_kv_static(m, seed, kv_std, arr, stream), m)
 
 
 def ld_set_mode(m, mode):
