@@ -33,6 +33,7 @@ struct ld_model {
   bool own_k = false;
   size_t kbytes = 0;
   bool kv_ready = false;
+  int last_rows = 0;  // rows of the last enqueued step
   ld_mode mode = LD_MODE_MEGA;
   int device = 0;
   int n_cu = 0;
@@ -188,7 +189,7 @@ extern "C" size_t ld_weights_bytes(const ld_config* cfg) {
 // KV + workspace arena layout (byte offsets).
 struct KLayout {
   size_t kc, vc, xa, xb, qkv, ao, part, hbuf, gbuf, ubuf, lm_val, lm_idx, rope, ctr, lm_ctr,
-      split_ctr, mctr, mpart, err, tune_ctr, total;
+      split_ctr, mctr, mpart, xa_f, xb_f, ao_f, h_f, ss_a, ss_b, err, tune_ctr, total;
   int split_len, max_splits, max_wg;
 };
 
@@ -252,6 +253,16 @@ static KLayout klayout(const ld_config* c, int maxB, int max_seq) {
   K.part = take((size_t)maxB * c->n_q_heads * K.max_splits * (d + 2) * 4);
   K.hbuf = take((size_t)maxB * I * 4);
   K.mpart = take((size_t)kMaxKSplit * maxB * H * 4);
+  {
+    const size_t Bp = ((size_t)maxB + 15) / 16 * 16, Ht = (H + 15) / 16;
+    const size_t Hp = round32((int)H), qdp = round32((int)qd), Ip = round32((int)I);
+    K.xa_f = take(Bp * Hp * 4);
+    K.xb_f = take(Bp * Hp * 4);
+    K.ao_f = take(Bp * qdp * 4);
+    K.h_f = take(Bp * Ip * 4);
+    K.ss_a = take((size_t)maxB * Ht * 4);
+    K.ss_b = take((size_t)maxB * Ht * 4);
+  }
   K.gbuf = take((size_t)maxB * I * 4);
   K.ubuf = take((size_t)maxB * I * 4);
   K.lm_val = take((size_t)K.max_wg * maxB * 4);
@@ -353,6 +364,10 @@ extern "C" ld_status ld_init_weights(ld_model** out, const ld_config* cfg, void*
   D.kvd = D.nkv * D.d;
   D.qkv_rows = D.qd + 2 * D.kvd;
   D.tied = cfg->tied;
+  D.Hp = round32(D.H);
+  D.qdp = round32(D.qd);
+  D.Ip = round32(D.I);
+  D.Ht = (D.H + 15) / 16;
   D.eps = cfg->rms_eps;
   D.attn_scale = 1.0f / sqrtf((float)D.d);
 
@@ -475,6 +490,12 @@ extern "C" ld_status ld_alloc_kv(ld_model* m, void* dev_buf, size_t bytes, int32
   K.split_ctr = reinterpret_cast<uint32_t*>(base + KL.split_ctr);
   K.mctr = reinterpret_cast<uint32_t*>(base + KL.mctr);
   K.mpart = reinterpret_cast<float*>(base + KL.mpart);
+  K.xa_f = reinterpret_cast<uint32_t*>(base + KL.xa_f);
+  K.xb_f = reinterpret_cast<uint32_t*>(base + KL.xb_f);
+  K.ao_f = reinterpret_cast<uint32_t*>(base + KL.ao_f);
+  K.h_f = reinterpret_cast<uint32_t*>(base + KL.h_f);
+  K.ss_a = reinterpret_cast<float*>(base + KL.ss_a);
+  K.ss_b = reinterpret_cast<float*>(base + KL.ss_b);
   K.err = reinterpret_cast<int*>(base + KL.err);
   m->ctr_bytes = KL.err - KL.ctr;
   K.max_wg = KL.max_wg;
@@ -613,6 +634,7 @@ static ld_status enqueue_step(ld_model* m, const int32_t* tokens, int32_t B, int
   P.S.next = next;
   P.S.B = B;
   P.S.M = M;
+  m->last_rows = B;
   // split length: from 16 rows the modes with a full CU's LDS take longer
   // splits (fewer items and partial results); below 16 rows every mode uses
   // the same splits, so they add the same numbers in the same order
@@ -1060,6 +1082,17 @@ extern "C" ld_status ld_read_activation(ld_model* m, int32_t which, int32_t rows
     default: return fail(m, LD_EINVAL, "unknown work buffer");
   }
   HIPCHK(m, hipDeviceSynchronize());
+  if ((which == LD_ACT_ATTN || which == LD_ACT_H) && m->last_rows >= kMfmaMinBatch) {
+    // the MFMA engine's steps keep these in B-fragment order: gather rows
+    const uint32_t* f = which == LD_ACT_ATTN ? m->K.ao_f : m->K.h_f;
+    const int kp = which == LD_ACT_ATTN ? D.qdp : D.Ip;
+    std::vector<uint32_t> tmp((size_t)((D.max_batch + 15) / 16 * 16) * kp);
+    HIPCHK(m, hipMemcpy(tmp.data(), f, tmp.size() * 4, hipMemcpyDeviceToHost));
+    uint32_t* out = reinterpret_cast<uint32_t*>(host_dst);
+    for (int b = 0; b < rows; ++b)
+      for (size_t c = 0; c < width; ++c) out[(size_t)b * width + c] = tmp[frag_word(b, (int)c, kp)];
+    return LD_OK;
+  }
   HIPCHK(m, hipMemcpy(host_dst, src, (size_t)rows * width * 4, hipMemcpyDeviceToHost));
   return LD_OK;
 }

@@ -44,6 +44,14 @@ struct XSrc {
   // producer wrote split_pair(v)), staged as copied, with no conversion pass;
   // only for inputs without an RMSNorm gain or norm
   bool pairs = false;
+  // MFMA engine only: the same inputs as split-bf16 pairs in B-fragment
+  // order (frag_word, K rounded up to kp), the consumer's gain applied, read
+  // straight into registers; with a deferred norm, ss[b * ss_ld + t] for t <
+  // ss_n are the producer's sums of squares per output tile of row b
+  const uint32_t* frag = nullptr;
+  int kp = 0;
+  const float* ss = nullptr;
+  int ss_n = 0, ss_ld = 0;
 
   __device__ __forceinline__ void raw8(int b, int k, float* o) const {
     if (x) {

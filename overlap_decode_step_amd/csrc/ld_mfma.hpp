@@ -103,7 +103,7 @@ struct SplitK {
 // 5.03 -> 4.53 ms (WAIT), 4.52 -> 4.14 ms (MEGA).  In the tile-flag mode's
 // 128-VGPR builds it spilled registers and was 2% slower.
 template <int NB, int MR>
-constexpr bool kSplitK = NB >= 64 && MR == kMfmaRingBig;
+constexpr bool kSplitK = NB >= 16 && MR == kMfmaRingBig;
 
 // The largest power of two up to kMaxKSplit that divides the grid, leaves
 // every range at least kMfmaMinChunk columns and at most 8 tiles per
@@ -115,6 +115,31 @@ __host__ __device__ constexpr int mfma_splits(int ntile, int K, int nwg) {
     S *= 2;
   return S;
 }
+
+// Activations handed from one MFMA stage to the next are stored in the order
+// the B operand is loaded in, as split-bf16 pairs (split_pair) with the
+// consumer's RMSNorm gain already applied: for K step s (32 columns) of batch
+// tile bt (16 rows) the 64 lanes' fragments lie in one 2 KB block, lane l
+// holding the 8 consecutive columns 8 (l / 16) .. + 7 of batch row l % 16 (32
+// contiguous bytes).  A wave then loads a B fragment with two 16-byte loads
+// per lane straight from memory, like its weight fragments, with no staging
+// copy, conversion pass or workgroup barrier.  kp: the matrix's K rounded up
+// to a multiple of 32 (the padding columns stay zero).  Word offset of
+// element (b, k):
+// frag_word(b, k, kp) (ld_params.hpp).
+
+// Weight-and-activation ring depth (K steps in flight per wave) of a stage
+// that loads its B fragments from memory: each step holds kMfmaTileMats
+// weight fragments (4 VGPRs each) and NBT pairs of 16-byte activation loads
+// (8 VGPRs per batch tile), within kDirectRingVgprs of the 256-VGPR builds
+// and kDirectRingVgprsSmall of the 128-VGPR ones (more spilled registers).
+constexpr int kDirectRingVgprs = 96, kDirectRingVgprsSmall = 56;
+template <int NBT, int RING>
+constexpr int kDirectRingRaw = (RING == kMfmaRingBig ? kDirectRingVgprs : kDirectRingVgprsSmall) /
+                               (4 * kMfmaTileMats + 8 * NBT);
+template <int NBT, int RING>
+constexpr int kDirectRing =
+    kDirectRingRaw<NBT, RING> < 2 ? 2 : (kDirectRingRaw<NBT, RING> > RING ? RING : kDirectRingRaw<NBT, RING>);
 
 // Rows of NT weight matrices in one buffer: tile t, matrix j, row r (0..15).
 struct MatRows {
@@ -131,17 +156,36 @@ struct MatRows {
 // r (r < 16) and batch row b, which is row bl = 16*bt + (lane % 16) of the
 // current batch pass; sc.rs[bl] holds b's deferred-norm factor when `norm`.
 // It is called only for b < B, by the lanes that hold the values; rows past
-// the matrix end are the callee's to skip.  PassEnd(b0, nb) runs (in every
-// thread) after each batch pass.
-template <int NBT, int NT, int RING, class WaitFn, class Epe, class PassEnd>
+// the matrix end are the callee's to skip; it returns the value it stored
+// (0 for a skipped row).  PassEnd(b0, nb) runs (in every thread) after each
+// batch pass.
+//
+// SRC: where the B fragments come from.
+//  kSrcConvert: src.x (fp32) or the embedding rows, staged in LDS in K chunks
+//    and converted there to split-bf16 pairs, gain applied, norm sums taken.
+//  kSrcFragLds: src.frag (B-fragment order, pairs, gain applied), its blocks
+//    copied as they are into LDS once per chunk and shared by the waves;
+//  kSrcDirect: src.frag loaded one K step at a time into registers through
+//    the weight ring, no LDS (each wave reads only its own K steps, so used
+//    when a workgroup holds one column of tiles).
+// With a fragment source the deferred-norm factors come from src.ss, the
+// sums of squares the producer stored per (batch row, 16-row output tile).
+// With ss_out the stage stores those sums for its own outputs: ss_out[b *
+// ss_ld + tile] = sum over the tile's rows of the squares of what Epe
+// returned.  All three give the MFMAs the same fragments in the same order.
+enum : int { kSrcConvert = 0, kSrcFragLds = 1, kSrcDirect = 2 };
+template <int NBT, int NT, int RING, int SRC = kSrcConvert, class WaitFn, class Epe, class PassEnd>
 __device__ __forceinline__ void mfma_stage(const MatRows& mr, int ntile, int K, const uint16_t* wbase,
                                            uint32_t wbytes, const XSrc& src, const uint16_t* gain,
                                            bool norm, float eps, int B, uint32_t x_cap,
                                            const WaitFn& wait, Epe& epe, const PassEnd& pass_end,
                                            int wg, int nwg, char* smem,
                                            const SplitK& sk = SplitK{nullptr, nullptr, 1},
-                                           bool row_major = false) {
+                                           bool row_major = false, float* ss_out = nullptr,
+                                           int ss_ld = 0) {
   constexpr int MT = kMfmaTileMats / NT;  // tiles per wave per tile pass
+  constexpr bool DIRECT = SRC == kSrcDirect, FRAG = SRC != kSrcConvert;
+  constexpr int RR = DIRECT ? kDirectRing<NBT, RING> : RING;  // K steps in flight per wave
   Scratch& sc = *reinterpret_cast<Scratch*>(smem);
   char* xbase = smem + kScratchBytes;
   const int lane = lane_id(), wave = wave_id(), nw = nwaves(), t = tid(), nth = blockDim.x;
@@ -168,10 +212,12 @@ __device__ __forceinline__ void mfma_stage(const MatRows& mr, int ntile, int K, 
   // is in registers), or 16 (row-major: one batch tile stays staged while the
   // whole weight stream passes, once per tile).  The K chunk is the
   // column-major one in both, so both add the same numbers in the same order.
-  const int prow_col = min(mfma_pass_rows(B, x_cap), NBT * 16);
+  const int prow_col = DIRECT ? NBT * 16 : min(mfma_pass_rows(B, x_cap), NBT * 16);
   const int prow = row_major ? 16 : prow_col;
   const int nbpass = (B + prow - 1) / prow;
-  const int KC = mfma_chunk(prow_col, K, x_cap), ldx = KC + kMfmaPad;  // row stride (4-byte words)
+  // (reading fragments from memory, the whole K range is one chunk)
+  const int KC = DIRECT ? round32(K) : mfma_chunk(prow_col, K, x_cap);
+  const int ldx = KC + kMfmaPad;  // staged row stride (4-byte words)
   const int nchunk = (K + KC - 1) / KC;
   const int cs = KC / 32;                 // 32-wide K steps per chunk
   const int spc = (cs + WK - 1) / WK;     // this wave's step slots per chunk (wave wk takes
@@ -206,11 +252,53 @@ __device__ __forceinline__ void mfma_stage(const MatRows& mr, int ntile, int K, 
         f[m][j] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kNt);
       }
   };
+  // direct mode: the B fragments of slot i for batch tiles bt < NBT of the
+  // pass starting at row b0 (agent-coherent loads: other workgroups stored
+  // them during this step); masked past the stream or the pass
+  const __amdgpu_buffer_rsrc_t frs =
+      weight_rsrc(reinterpret_cast<const uint16_t*>(src.frag), DIRECT ? (uint32_t)((size_t)((B + 15) / 16) * src.kp * 64) : 0u);
+  auto issue_b = [&](u32x4 (&fb)[NBT][2], int i, int b0, int nb) {
+    if constexpr (DIRECT) {
+      const int st = wk + i * WK;
+      const bool ok = i < nslot && st < cs;
+      const int sg = (ks0 >> 5) + st;  // K step in the whole matrix
+#pragma unroll
+      for (int bt = 0; bt < NBT; ++bt) {
+        const bool okb = ok && bt * 16 < min(prow, nb);
+        const uint32_t off = okb ? (uint32_t)((((int64_t)((b0 >> 4) + bt) * (src.kp >> 5) + sg) * 128 + lane) * 16) : 0u;
+        const __amdgpu_buffer_rsrc_t r = okb ? frs : weight_rsrc(reinterpret_cast<const uint16_t*>(src.frag), 0u);
+        fb[bt][0] = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kSc1);
+        fb[bt][1] = __builtin_amdgcn_raw_buffer_load_b128(r, off + 1024u, 0, kSc1);
+      }
+    } else {
+      (void)fb, (void)i, (void)b0, (void)nb;
+    }
+  };
   float ssacc = 0.f;  // thread t < nb: row b0 + t's running sum of squares
   // ---- stage rows [b0, b0 + prow) x columns [kc0, kc0 + KC) of chunk c
   auto stage_chunk = [&](int b0, int nb, int c, bool sums) {
     const int kc0 = c * KC;
     __syncthreads();  // the previous chunk's pairs and partial sums are consumed
+    if constexpr (SRC == kSrcFragLds) {
+      // the chunk's fragment blocks (2 KB per batch tile and K step, two
+      // contiguous 1 KB halves) copied as they are: LDS holds [tile][step of
+      // the chunk][half][lane] 16-byte words, one 1 KB half per wave
+      // instruction (agent-coherent: other workgroups wrote them this step)
+      (void)sums;
+      const int ntl = (min(prow, nb) + 15) / 16, spk = KC >> 5;
+      const int ns = min(spk, (K - kc0 + 31) >> 5);  // steps of this chunk
+      const int s0 = (ks0 + kc0) >> 5;                // its first step in the matrix
+      const char* fb = reinterpret_cast<const char*>(src.frag);
+      for (int i = wave; i < ntl * ns * 2; i += nw) {
+        const int bt = i / (ns * 2), r = i - bt * (ns * 2), s = r >> 1, h = r & 1;
+        const char* g = fb + ((((int64_t)((b0 >> 4) + bt) * (src.kp >> 5) + s0 + s) * 2 + h) << 10) + lane * 16;
+        char* dst = reinterpret_cast<char*>(xw) + (((size_t)(bt * spk + s) * 2 + h) << 10);
+        __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)dst, 16, 0, kSc1);
+      }
+      wave_drain();
+      __syncthreads();
+      return;
+    }
     const int gpr = KC / 8;  // 8-column groups per row (a multiple of 64)
     const int ngroup = prow * gpr;
     if (src.x != nullptr) {
@@ -300,11 +388,12 @@ __device__ __forceinline__ void mfma_stage(const MatRows& mr, int ntile, int K, 
   };
 
 
-  u32x4 ring[RING][MT][NT];
+  u32x4 ring[RR][MT][NT];
+  u32x4 bring[DIRECT ? RR : 1][NBT][2];
   set_tiles(0);
   if (wave != 0) {  // weight loads across the wait, except in the polling wave
 #pragma unroll
-    for (int j = 0; j < RING; ++j) issue(ring[j], j);
+    for (int j = 0; j < RR; ++j) issue(ring[j], j);
   }
   wait();
   for (int bp = 0; bp < nbpass; ++bp) {
@@ -316,7 +405,11 @@ __device__ __forceinline__ void mfma_stage(const MatRows& mr, int ntile, int K, 
       if (bp > 0 || tp > 0) set_tiles(m0);
       if (bp > 0 || tp > 0 || wave == 0) {
 #pragma unroll
-        for (int j = 0; j < RING; ++j) issue(ring[j], j);
+        for (int j = 0; j < RR; ++j) issue(ring[j], j);
+      }
+      if constexpr (DIRECT) {
+#pragma unroll
+        for (int j = 0; j < RR; ++j) issue_b(bring[j], j, b0, nb);
       }
       f32x4 acc[MT][NT][NBT];
 #pragma unroll
@@ -325,24 +418,37 @@ __device__ __forceinline__ void mfma_stage(const MatRows& mr, int ntile, int K, 
         for (int j = 0; j < NT; ++j)
 #pragma unroll
           for (int bt = 0; bt < NBT; ++bt) acc[m][j][bt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      stage_chunk(b0, nb, 0, sums);
+      if constexpr (!DIRECT) stage_chunk(b0, nb, 0, sums);
       // ---- one ring over the whole K stream; a chunk boundary restages the
       // inputs while the next chunk's weight loads are already in flight
-      for (int i0 = 0; i0 < nslot; i0 += RING) {
+      for (int i0 = 0; i0 < nslot; i0 += RR) {
 #pragma unroll
-        for (int jj = 0; jj < RING; ++jj) {
+        for (int jj = 0; jj < RR; ++jj) {
           const int i = i0 + jj;
           const int c = i / spc, st = wk + (i - c * spc) * WK;
-          if (i < nslot && i == c * spc && c > 0) stage_chunk(b0, nb, c, sums);
+          if constexpr (!DIRECT) {
+            if (i < nslot && i == c * spc && c > 0) stage_chunk(b0, nb, c, sums);
+          }
           if (i < nslot && st < cs && c * KC + st * 32 < K) {
             const int kl = st * 32 + (lane >> 4) * 8;  // column in the chunk
 #pragma unroll
             for (int bt = 0; bt < NBT; ++bt) {
               if (bt * 16 < prow) {
                 // this batch tile's hi and lo fragments, used by every tile
-                const uint32_t* w = xw + (size_t)(bt * 16 + (lane & 15)) * ldx + kl;
-                const u32x4 p0 = *reinterpret_cast<const u32x4*>(w);
-                const u32x4 p1 = *reinterpret_cast<const u32x4*>(w + 4);
+                u32x4 p0, p1;
+                if constexpr (DIRECT) {
+                  p0 = bring[jj][bt][0];
+                  p1 = bring[jj][bt][1];
+                } else if constexpr (SRC == kSrcFragLds) {
+                  const char* q = reinterpret_cast<const char*>(xw) +
+                                  ((((size_t)bt * (KC >> 5) + st) * 2) << 10) + lane * 16;
+                  p0 = *reinterpret_cast<const u32x4*>(q);
+                  p1 = *reinterpret_cast<const u32x4*>(q + 1024);
+                } else {
+                  const uint32_t* w = xw + (size_t)(bt * 16 + (lane & 15)) * ldx + kl;
+                  p0 = *reinterpret_cast<const u32x4*>(w);
+                  p1 = *reinterpret_cast<const u32x4*>(w + 4);
+                }
                 // (hi | lo << 16) pairs -> 8 hi halves, 8 lo halves
                 const u32x4 hh{(p0.x & 0xFFFFu) | (p0.y << 16), (p0.z & 0xFFFFu) | (p0.w << 16),
                                (p1.x & 0xFFFFu) | (p1.y << 16), (p1.z & 0xFFFFu) | (p1.w << 16)};
@@ -366,11 +472,25 @@ __device__ __forceinline__ void mfma_stage(const MatRows& mr, int ntile, int K, 
               }
             }
           }
-          issue(ring[jj], i + RING);
+          issue(ring[jj], i + RR);
+          if constexpr (DIRECT) issue_b(bring[jj], i + RR, b0, nb);
         }
       }
       // ---- norms of this batch pass (first tile pass only)
-      if (sums) {
+      if constexpr (FRAG) {
+        // from the producer's sums of squares per (row, output tile): thread
+        // t < 8 prow adds tiles p, p + 8, ... of row t / 8 (p = t % 8), then
+        // the 8 lanes of the row are added in a fixed tree
+        if (sums) {
+          const int b = t >> 3, p = t & 7;
+          float s2 = 0.f;
+          if (b < nb)
+            for (int q = p; q < src.ss_n; q += 8) s2 += ld_coh(src.ss + (int64_t)(b0 + b) * src.ss_ld + q);
+          s2 = lane_group_sum(s2, 8);
+          __syncthreads();
+          if (b < nb && p == 7) sc.rs[b] = 1.0f / sqrtf(s2 / (float)Kfull + eps);
+        }
+      } else if (sums) {
         __syncthreads();
         if (t < nb) sc.rs[t] = 1.0f / sqrtf(ssacc / (float)Kfull + eps);
       }
@@ -441,6 +561,7 @@ __device__ __forceinline__ void mfma_stage(const MatRows& mr, int ntile, int K, 
 #pragma unroll
             for (int bt = 0; bt < NBT; ++bt) {
               const int b = bt * 16 + (lane & 15);
+              float s2 = 0.f;  // squares of the stored values of this lane's 4 rows
               if (bt * 16 < prow && b < nb) {
                 if (split) {
                   // every range's partials of the lane's 4 rows in one round
@@ -461,7 +582,8 @@ __device__ __forceinline__ void mfma_stage(const MatRows& mr, int ntile, int K, 
 #pragma unroll
                     for (int q = 1; q < kMaxKSplit; ++q)
                       if (q < S) v[0] += pv[i][q];
-                    epe(tile, (lane >> 4) * 4 + i, b0 + b, b, bt, v);
+                    const float r = epe(tile, (lane >> 4) * 4 + i, b0 + b, b, bt, v);
+                    s2 = fmaf(r, r, s2);
                   }
                 } else {
 #pragma unroll
@@ -469,9 +591,18 @@ __device__ __forceinline__ void mfma_stage(const MatRows& mr, int ntile, int K, 
                     float v[NT];
 #pragma unroll
                     for (int j = 0; j < NT; ++j) v[j] = acc[m][j][bt][i];
-                    epe(tile, (lane >> 4) * 4 + i, b0 + b, b, bt, v);
+                    const float r = epe(tile, (lane >> 4) * 4 + i, b0 + b, b, bt, v);
+                    s2 = fmaf(r, r, s2);
                   }
                 }
+              }
+              if (ss_out != nullptr) {
+                // lanes l, l ^ 16, l ^ 32, l ^ 48 hold the tile's 16 rows of
+                // one batch row: their sum, in a fixed order
+                s2 += __shfl_xor(s2, 16, kWave);
+                s2 += __shfl_xor(s2, 32, kWave);
+                if (lane < 16 && bt * 16 < prow && b < nb)
+                  st_coh(ss_out + (int64_t)(b0 + b) * ss_ld + tile, s2);
               }
             }
           }
@@ -480,6 +611,35 @@ __device__ __forceinline__ void mfma_stage(const MatRows& mr, int ntile, int K, 
     }
     pass_end(b0, nb);
   }
+}
+
+// A fragment-source stage: direct loads when every workgroup holds a single
+// column of 16-row tiles (its waves then split K, so no wave loads another's
+// fragments), otherwise one LDS copy of the fragments shared by the waves.
+// (The decomposition is mfma_stage's: tiles per workgroup of a K range.)
+template <int NBT, int NT, int RING, class WaitFn, class Epe, class PassEnd>
+__device__ __forceinline__ void mfma_stage_frag(const MatRows& mr, int ntile, int K,
+                                                const uint16_t* wbase, uint32_t wbytes,
+                                                const XSrc& src, bool norm, float eps, int B,
+                                                uint32_t x_cap, const WaitFn& wait, Epe& epe,
+                                                const PassEnd& pass_end, int wg, int nwg,
+                                                char* smem,
+                                                const SplitK& sk = SplitK{nullptr, nullptr, 1},
+                                                bool row_major = false, float* ss_out = nullptr,
+                                                int ss_ld = 0) {
+  const int nwr = min(nwg / sk.S, max(1, ntile / kMfmaMinTiles));
+  // (64-row passes would hold 32 VGPRs of fragments per K step: they share one copy)
+  if constexpr (NBT <= 2) {
+    if ((ntile + nwr - 1) / nwr <= 1) {
+      mfma_stage<NBT, NT, RING, kSrcDirect>(mr, ntile, K, wbase, wbytes, src, nullptr, norm, eps, B,
+                                          x_cap, wait, epe, pass_end, wg, nwg, smem, sk, row_major,
+                                          ss_out, ss_ld);
+      return;
+    }
+  }
+  mfma_stage<NBT, NT, RING, kSrcFragLds>(mr, ntile, K, wbase, wbytes, src, nullptr, norm, eps, B,
+                                           x_cap, wait, epe, pass_end, wg, nwg, smem, sk,
+                                           row_major, ss_out, ss_ld);
 }
 
 }  // namespace ld

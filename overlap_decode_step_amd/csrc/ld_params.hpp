@@ -40,12 +40,29 @@ enum : int { kGuCol = 0, kGuRow = 1 };
 enum : int { kMlpGate = 0, kMlpUp = 1, kMlpBoth = 2 };
 enum : int { kMlpSilu = 0, kMlpMul = 1, kMlpSiluMul = 2 };
 
+// K rounded up to whole 32-wide MFMA K steps.
+constexpr int round32(int k) { return (k + 31) / 32 * 32; }
+
+// Word offset of element (b, k) of an activation matrix stored in the MFMA
+// engine's B-fragment order (see ld_mfma.hpp): 2 KB per (16-row batch tile,
+// 32-wide K step), two 1 KB halves, lane l = 16 * ((k / 8) % 4) + b % 16
+// holding columns 8 (k / 8) .. + 3 of its row in the first half and + 4 .. + 7
+// in the second, 16 bytes each, so one 16-byte load per lane reads a
+// contiguous 1 KB.  kp: K rounded up to 32.
+constexpr int64_t frag_word(int b, int k, int kp) {
+  return ((((int64_t)(b >> 4) * (kp >> 5) + (k >> 5)) * 2 + ((k >> 2) & 1)) * 64 +
+          ((((k >> 3) & 3) << 4) | (b & 15))) * 4 +
+         (k & 3);
+}
+
 struct Dims {
   int L, H, nq, nkv, d, I, V, group;
   int qd, kvd, qkv_rows;
   int max_batch, max_seq;
   int split_len, max_splits;  // longest attention split (LDS tiles), splits per sequence at most
   int tied;
+  int Hp, qdp, Ip;  // hidden, n_q * head_dim and intermediate rounded up to 32
+  int Ht;           // 16-row output tiles of a hidden-sized projection
   float eps;
   float attn_scale;  // 1 / sqrt(head_dim)
 };
@@ -83,6 +100,16 @@ struct Work {
   uint32_t* split_ctr;  // attention last-arriver counters [L][maxB][nkv][16]
   uint32_t* mctr;       // split-K last-arriver counters: O, then Down, [kMctrPasses][tiles]
   float* mpart;         // split-K partial tiles [kMaxKSplit][maxB][H]
+  // MFMA engine (16 rows and more): activations handed from one of its stages
+  // to the next in B-fragment order (frag_word; batch rows padded to 16) as
+  // split-bf16 pairs with the consumer's norm gain applied, and the sums of
+  // squares of the two residual streams per (row, 16-row output tile)
+  uint32_t* xa_f;  // layer output, for the next QKV stage or the LM head [Bp][Hp]
+  uint32_t* xb_f;  // O-stage output, for the SwiGLU stage [Bp][Hp]
+  uint32_t* ao_f;  // attention output, for the O stage [Bp][qdp]
+  uint32_t* h_f;   // SwiGLU output, for the Down stage [Bp][Ip]
+  float* ss_a;     // sums of squares of xa [maxB][Ht]
+  float* ss_b;     // sums of squares of xb [maxB][Ht]
   int* err;
   uint64_t* trace;  // optional stage timestamps (see trace_ev), nullptr = off
   uint64_t watchdog;

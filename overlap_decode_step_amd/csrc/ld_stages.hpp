@@ -126,13 +126,27 @@ __device__ __forceinline__ void stage_qkv(const Params& P, int l, int wg, int nw
   const uint32_t wbytes = (uint32_t)((int64_t)rows_total * K * 2);
   if constexpr (NB >= kMfmaMinBatch) {
     Scratch& sc = *reinterpret_cast<Scratch*>(smem);
-    auto epe = [&](int tile, int r, int b, int bl, int, const float* v) {
+    auto epe = [&](int tile, int r, int b, int bl, int, const float* v) -> float {
       const int row = tile * 16 + r;
       if (row < rows_total) st_coh(out + (int64_t)b * rows_total + row, v[0] * sc.rs[bl]);
+      return 0.f;
     };
-    mfma_stage<kMfmaNbt<NB, MR>, 1, MR>(MatRows{Wm, {Wm, Wm}, rows_total, K}, (rows_total + 15) / 16, K, Wm,
-                           wbytes, src, layer_w(P, l, P.W.o_attn_norm), true, D.eps, B, P.S.x_cap,
-                           wait, epe, [](int, int) {}, wg, nwg, smem);
+    const MatRows mr{Wm, {Wm, Wm}, rows_total, K};
+    const int ntile = (rows_total + 15) / 16;
+    if (l == 0) {  // the embedding rows, staged with the gain applied
+      mfma_stage<kMfmaNbt<NB, MR>, 1, MR>(mr, ntile, K, Wm, wbytes, src,
+                                          layer_w(P, l, P.W.o_attn_norm), true, D.eps, B,
+                                          P.S.x_cap, wait, epe, [](int, int) {}, wg, nwg, smem);
+    } else {  // the previous layer's Down stage wrote its output as fragments
+      XSrc fs{nullptr, K, nullptr, nullptr, 0};
+      fs.frag = P.K.xa_f;
+      fs.kp = D.Hp;
+      fs.ss = P.K.ss_a;
+      fs.ss_n = fs.ss_ld = D.Ht;
+      mfma_stage_frag<kMfmaNbt<NB, MR>, 1, MR>(mr, ntile, K, Wm, wbytes, fs, true, D.eps, B,
+                                               P.S.x_cap, wait, epe, [](int, int) {}, wg, nwg,
+                                               smem);
+    }
   } else {
     gemv_stage<NR, UC, NB, kPfQkv>(rowfn, (rows_total + NR - 1) / NR, K, Wm, wbytes, src,
                                    layer_w(P, l, P.W.o_attn_norm), true, D.eps, B,
@@ -182,11 +196,14 @@ __host__ __device__ constexpr size_t attn_smem_bytes(int group, int d, int T, in
          + (size_t)group * 2 * 4;                                  /* (max, sum) per head */
 }
 
-// Attention output for the O stage: fp32 for the VALU engine, split-bf16
-// pairs when the step runs on the MFMA engine (16 rows and more), which then
-// stages them without a conversion pass.
-__device__ __forceinline__ void st_ao(const Params& P, float* p, float v) {
-  st_coh(p, P.S.B >= kMfmaMinBatch ? __uint_as_float(split_pair(v)) : v);
+// Attention output of row b, column c (head-major) for the O stage: fp32 for
+// the VALU engine, a split-bf16 pair in B-fragment order when the step runs
+// on the MFMA engine (16 rows and more), which loads it as it is.
+__device__ __forceinline__ void st_ao(const Params& P, int b, int c, float v) {
+  if (P.S.B >= kMfmaMinBatch)
+    st_coh_u(P.K.ao_f + frag_word(b, c, P.D.qdp), split_pair(v));
+  else
+    st_coh(P.K.ao + (int64_t)b * P.D.qd + c, v);
 }
 
 // Row b of the step (token j = b % M of sequence slot = b / M, at position
@@ -473,14 +490,14 @@ __device__ __forceinline__ void attn_item(const Params& P, int l, const AttnItem
     o4[1] = make_float4(x[4] + y[4], x[5] + y[5], x[6] + y[6], x[7] + y[7]);
   }
   __syncthreads();
-  float* out = P.K.ao + (int64_t)b * D.qd + kvh * gd;
+  const int oc = kvh * gd;  // this group's first output column
   for (int r = tid; r < gd; r += nth) {
     const int g = r >> ld, i = r & (d - 1);
     float o = 0.f;
 #pragma unroll 4
     for (int sl = 0; sl < parts; ++sl) o += s.op[sl * gd + r];
     if (nsplit == 1) {
-      st_ao(P, out + r, o / s.ml[2 * g + 1]);
+      st_ao(P, b, oc + r, o / s.ml[2 * g + 1]);
     } else {
       float* pp = P.K.part + (((int64_t)b * D.nq + kvh * group + g) * D.max_splits + a.s) * (d + 2);
       st_coh(pp + 2 + i, o);
@@ -540,7 +557,7 @@ __device__ __forceinline__ void attn_item(const Params& P, int l, const AttnItem
         L = fmaf(ld_coh(q + s0 * (d + 2) + 1), f, L);
         O = fmaf(ld_coh(q + s0 * (d + 2) + 2 + i), f, O);
       }
-      st_ao(P, out + r, O / L);
+      st_ao(P, b, oc + r, O / L);
     }
   }
   signal_if(P, stage_ctr(P, l, kCAttn), b * D.nkv + kvh);
@@ -676,9 +693,12 @@ __device__ __forceinline__ void stage_o(const Params& P, int l, int wg, int nwg,
   };
   const uint32_t wbytes = (uint32_t)((int64_t)rows_total * K * 2);
   if constexpr (NB >= kMfmaMinBatch) {
-    auto epe = [&](int tile, int r, int b, int, int, const float* v) {
+    // x' = x + Wo . o, stored as fp32 (the Down stage's residual) and as
+    // fragments with the SwiGLU stage's norm gain, with its sums of squares
+    const uint16_t* gm = layer_w(P, l, P.W.o_mlp_norm);
+    auto epe = [&](int tile, int r, int b, int, int, const float* v) -> float {
       const int row = tile * 16 + r;
-      if (row >= rows_total) return;
+      if (row >= rows_total) return 0.f;
       float res;
       if (l == 0) {
         int tk = tok[b];
@@ -687,14 +707,20 @@ __device__ __forceinline__ void stage_o(const Params& P, int l, int wg, int nwg,
       } else {
         res = ld_coh(xa + (int64_t)b * D.H + row);
       }
-      st_coh(xb + (int64_t)b * D.H + row, res + v[0]);
+      const float x = res + v[0];
+      st_coh(xb + (int64_t)b * D.H + row, x);
+      st_coh_u(P.K.xb_f + frag_word(b, row, D.Hp), split_pair(x * bf16f(gm[row])));
+      return x;
     };
-    const XSrc srcp{src.x, src.ldx, nullptr, nullptr, 0, true};  // split-bf16 pairs
+    XSrc fs{nullptr, K, nullptr, nullptr, 0};
+    fs.frag = P.K.ao_f;
+    fs.kp = D.qdp;
     const int ntile = (rows_total + 15) / 16;
     const SplitK sk{P.K.mpart, P.K.mctr, kSplitK<NB, MR> ? mfma_splits(ntile, K, nwg) : 1};
-    mfma_stage<kMfmaNbt<NB, MR>, 1, MR>(MatRows{Wm, {Wm, Wm}, rows_total, K}, ntile, K, Wm,
-                           wbytes, srcp, nullptr, false, D.eps, B, P.S.x_cap, wait, epe,
-                           [](int, int) {}, wg, nwg, smem, sk);
+    mfma_stage_frag<kMfmaNbt<NB, MR>, 1, MR>(MatRows{Wm, {Wm, Wm}, rows_total, K}, ntile, K, Wm,
+                                             wbytes, fs, false, D.eps, B, P.S.x_cap, wait, epe,
+                                             [](int, int) {}, wg, nwg, smem, sk, false, P.K.ss_b,
+                                             D.Ht);
   } else {
     gemv_stage<NR, UC, NB, kPfO>(rowfn, (rows_total + NR - 1) / NR, K, Wm, wbytes, src, nullptr,
                                  false, D.eps, B, batch_tile(P, K, NB), wait, epi, wg, nwg, smem);
@@ -813,18 +839,24 @@ __device__ __forceinline__ void stage_gu(const Params& P, int l, int wg, int nwg
     (void)prefetched;
     (void)bw;
     Scratch& sc = *reinterpret_cast<Scratch*>(smem);
-    auto epe = [&](int tile, int r, int b, int bl, int, const float* v) {
+    auto epe = [&](int tile, int r, int b, int bl, int, const float* v) -> float {
       const int row = tile * 16 + r;
-      if (row >= I) return;
+      if (row >= I) return 0.f;
       const float a = v[0] * sc.rs[bl], u = v[1] * sc.rs[bl];
-      // the Down stage (MFMA engine too) stages h as split-bf16 pairs
-      st_coh(h + (int64_t)b * I + row, __uint_as_float(split_pair(a / (1.0f + expf(-a)) * u)));
+      // for the Down stage (MFMA engine too): fragments of split-bf16 pairs
+      st_coh_u(P.K.h_f + frag_word(b, row, D.Ip), split_pair(a / (1.0f + expf(-a)) * u));
+      return 0.f;
     };
-    mfma_stage<kMfmaNbt<NB, MR>, 2, MR>(MatRows{layer_w(P, l, 0), {rows.Wg, rows.Wu}, I, K}, (I + 15) / 16, K,
-                           layer_w(P, l, 0), (uint32_t)(P.W.layer_stride * 2), src,
-                           layer_w(P, l, P.W.o_mlp_norm), true, D.eps, B, P.S.x_cap, wait, epe,
-                           [](int, int) {}, wg, nwg, smem, SplitK{nullptr, nullptr, 1},
-                           P.S.gu_variant == kGuRow);
+    (void)h;
+    XSrc fs{nullptr, K, nullptr, nullptr, 0};  // the O stage's output as fragments
+    fs.frag = P.K.xb_f;
+    fs.kp = D.Hp;
+    fs.ss = P.K.ss_b;
+    fs.ss_n = fs.ss_ld = D.Ht;
+    mfma_stage_frag<kMfmaNbt<NB, MR>, 2, MR>(
+        MatRows{layer_w(P, l, 0), {rows.Wg, rows.Wu}, I, K}, (I + 15) / 16, K, layer_w(P, l, 0),
+        (uint32_t)(P.W.layer_stride * 2), fs, true, D.eps, B, P.S.x_cap, wait, epe,
+        [](int, int) {}, wg, nwg, smem, SplitK{nullptr, nullptr, 1}, P.S.gu_variant == kGuRow);
   } else {
     gemv_run<NR, kUcGu, NB, kPfGu>(ws, ring, prefetched, src, layer_w(P, l, P.W.o_mlp_norm), true,
                                    D.eps, B, bw, wait, epi, smem,
@@ -978,19 +1010,29 @@ __device__ __forceinline__ void stage_d(const Params& P, int l, int wg, int nwg,
   };
   const uint32_t wbytes = (uint32_t)((int64_t)rows_total * K * 2);
   if constexpr (NB >= kMfmaMinBatch) {
-    auto epe = [&](int tile, int r, int b, int, int, const float* v) {
+    // x'' = x' + Wd . h, stored as fp32 (the next layer's residual) and as
+    // fragments with the norm gain of its consumer (the next layer's QKV
+    // stage, or the LM head after the last layer), with its sums of squares
+    const uint16_t* gn = l + 1 < D.L ? layer_w(P, l + 1, P.W.o_attn_norm) : P.W.final_norm;
+    auto epe = [&](int tile, int r, int b, int, int, const float* v) -> float {
       const int row = tile * 16 + r;
-      if (row >= rows_total) return;
+      if (row >= rows_total) return 0.f;
       const int64_t o = (int64_t)b * D.H + row;
-      st_coh(xa + o, ld_coh(xb + o) + v[0]);
+      const float x = ld_coh(xb + o) + v[0];
+      st_coh(xa + o, x);
+      st_coh_u(P.K.xa_f + frag_word(b, row, D.Hp), split_pair(x * bf16f(gn[row])));
+      return x;
     };
-    const XSrc srcp{src.x, src.ldx, nullptr, nullptr, 0, true};  // split-bf16 pairs
+    XSrc fs{nullptr, K, nullptr, nullptr, 0};  // the SwiGLU output as fragments
+    fs.frag = P.K.h_f;
+    fs.kp = D.Ip;
     const int ntile = (rows_total + 15) / 16;
     const SplitK sk{P.K.mpart, P.K.mctr + kMctrPasses * ntile,
                     kSplitK<NB, MR> ? mfma_splits(ntile, K, nwg) : 1};
-    mfma_stage<kMfmaNbt<NB, MR>, 1, MR>(MatRows{Wm, {Wm, Wm}, rows_total, K}, ntile, K, Wm,
-                           wbytes, srcp, nullptr, false, D.eps, B, P.S.x_cap, wait, epe,
-                           [](int, int) {}, wg, nwg, smem, sk);
+    mfma_stage_frag<kMfmaNbt<NB, MR>, 1, MR>(MatRows{Wm, {Wm, Wm}, rows_total, K}, ntile, K, Wm,
+                                             wbytes, fs, false, D.eps, B, P.S.x_cap, wait, epe,
+                                             [](int, int) {}, wg, nwg, smem, sk, false, P.K.ss_a,
+                                             D.Ht);
   } else {
     gemv_stage<NR, UC, NB, kPfD, kStageGroupsD<NB>>(rowfn, (rows_total + NR - 1) / NR, K, Wm,
                                                      wbytes, src, nullptr, false, D.eps, B,
@@ -1080,15 +1122,16 @@ __device__ __forceinline__ void stage_lm(const Params& P, int wg, int nwg, char*
       bv[bt] = -INFINITY;
       bi[bt] = 0x7FFFFFFF;
     }
-    auto epe = [&](int tile, int r, int b, int bl, int bt, const float* v) {
+    auto epe = [&](int tile, int r, int b, int bl, int bt, const float* v) -> float {
       const int row = tile * 16 + r;
-      if (row >= rows_total) return;
+      if (row >= rows_total) return 0.f;
       const float val = v[0] * sc.rs[bl];
       logits[(int64_t)b * D.V + row] = val;
       if (better(val, row, bv[bt], bi[bt])) {
         bv[bt] = val;
         bi[bt] = row;
       }
+      return 0.f;
     };
     auto pass_end = [&](int b0, int nb) {
 #pragma unroll
@@ -1114,9 +1157,14 @@ __device__ __forceinline__ void stage_lm(const Params& P, int wg, int nwg, char*
         bi[bt] = 0x7FFFFFFF;
       }
     };
-    mfma_stage<NBT, 1, MR>(MatRows{Wm, {Wm, Wm}, rows_total, K}, (rows_total + 15) / 16, K, Wm, wbytes,
-                       src, P.W.final_norm, true, D.eps, B, P.S.x_cap, wait, epe, pass_end, wg,
-                       nwg, smem);
+    XSrc fs{nullptr, K, nullptr, nullptr, 0};  // the last Down stage's output as fragments
+    fs.frag = P.K.xa_f;
+    fs.kp = D.Hp;
+    fs.ss = P.K.ss_a;
+    fs.ss_n = fs.ss_ld = D.Ht;
+    mfma_stage_frag<NBT, 1, MR>(MatRows{Wm, {Wm, Wm}, rows_total, K}, (rows_total + 15) / 16, K,
+                                Wm, wbytes, fs, true, D.eps, B, P.S.x_cap, wait, epe, pass_end, wg,
+                                nwg, smem);
   } else {
     gemv_stage<NR, UC, NB, kPfLm>(rowfn, (rows_total + NR - 1) / NR, K, Wm, wbytes, src,
                                   P.W.final_norm, true, D.eps, B, batch_tile(P, K, NB), wait, epi,
