@@ -312,6 +312,8 @@ def main():
     ap.add_argument("--mlp-ablation", action="store_true",
                     help="also time the whole-kernel-wait step with the fused SwiGLU stage "
                          "against its two- and four-kernel unfused forms (batch < 16)")
+    ap.add_argument("--sync", default="auto", choices=["auto", "tile", "stage"],
+                    help="readiness granularity of the tile-flag and persistent modes")
     ap.add_argument("--prefill", type=int, default=None,
                     help="KV prefill per sequence (default 512 for llama1b, else 1024)")
     ap.add_argument("--tune", default=None,
@@ -364,6 +366,7 @@ def main():
     m = ld.Model(shape, seed=W.SEED_WEIGHTS, w_std=w_std)
     m.alloc_kv(B, max_seq)
     m.fill_kv(W.SEED_KV, 1.0, [prefill] * B)
+    m.set_sync(args.sync)
     torch.cuda.synchronize()
     logits = torch.empty((B, shape["vocab"]), dtype=torch.float32, device=dev)
     toks = torch.tensor(W.first_tokens(B, shape["vocab"]), dtype=torch.int32, device=dev)
@@ -464,7 +467,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{args.shape}-shape decode, batch {B}, KV prefill {prefill}, "
                                f"positions {prefill}..{prefill + steps - 1}",
-                   "mode": args.mode, "batch": B},
+                   "mode": args.mode, "batch": B, "sync": args.sync},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": read_traffic(args.mode, B) if headline else None,

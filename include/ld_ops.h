@@ -66,6 +66,21 @@ int32_t ld_get_swiglu_variant(const ld_model* m, int32_t batch);
 enum { LD_MLP_FUSED = 0, LD_MLP_TWO_KERNELS = 1, LD_MLP_FOUR_KERNELS = 2 };
 ld_status ld_set_mlp_variant(ld_model* m, int32_t variant);
 
+/* Readiness granularity of the tile-flag and persistent modes (MegaOps
+ * summary, "In plain words": a consumer starts once the particular pieces of
+ * shared data it needs are ready).  LD_SYNC_TILE: each attention item waits
+ * only for the q, k and v rows of its own kv group, and the Down stage only
+ * for the SwiGLU output chunks (1024 rows each) of the K range it reads (all
+ * of them on the VALU engine, its own range in a split-K stage of the MFMA
+ * engine), through row-count counters.  LD_SYNC_STAGE: those consumers wait
+ * for their whole producer stage.  LD_SYNC_AUTO (the default): LD_SYNC_TILE
+ * in the tile-flag mode below 64 rows, LD_SYNC_STAGE otherwise (the faster
+ * of the two as measured on MI355X).  Results are bitwise the same either
+ * way.  Shapes with more than 64 kv groups or SwiGLU chunks per layer always
+ * use LD_SYNC_STAGE.  Returns LD_EINVAL for another value. */
+enum { LD_SYNC_STAGE = 0, LD_SYNC_TILE = 1, LD_SYNC_AUTO = 2 };
+ld_status ld_set_sync(ld_model* m, int32_t granularity);
+
 /* Spin limit of every device-side readiness wait (default 2 s). */
 ld_status ld_set_watchdog(ld_model* m, double seconds);
 

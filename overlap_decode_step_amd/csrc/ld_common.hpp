@@ -226,6 +226,45 @@ __device__ __forceinline__ void wg_wait(const SyncArgs& s, const uint32_t* ctr, 
   __syncthreads();
 }
 
+// Workgroup-wide wait until each of the n counters ctr0 + i * kCtrWords
+// (i < n) has reached target(i).  Wave 0 polls four counters per wave-wide
+// load (lane 16 c + leaf reads leaf `leaf` of counter c), adds each counter's
+// 16 leaves within its lane row, and repeats until every counter has reached
+// its target (or another workgroup timed out); same watchdog as wg_wait.
+template <class TargetFn>
+__device__ __forceinline__ void wg_wait_all(const SyncArgs& s, const uint32_t* ctr0, int n,
+                                            const TargetFn& target, int stage) {
+  if (n > 0 && wave_id() == 0) {
+    const int lane = lane_id(), sub = lane >> 4, leaf = lane & (kLeaves - 1);
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    bool done = false;
+    while (!done) {
+      bool all = true;
+      for (int g = 0; g < n; g += 4) {
+        const int i = g + sub;
+        uint32_t v = __hip_atomic_load(ctr0 + (int64_t)min(i, n - 1) * kCtrWords + leaf * kLeafStride,
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        v += dpp_u<0xB1, 0xF>(0u, v);   // quad_perm [1,0,3,2]
+        v += dpp_u<0x4E, 0xF>(0u, v);   // quad_perm [2,3,0,1]
+        v += dpp_u<0x124, 0xF>(0u, v);  // row_ror:4
+        v += dpp_u<0x128, 0xF>(0u, v);  // row_ror:8: every lane of the row holds its sum
+        const bool ok = i >= n || reached(v, target(i));
+        all = all && __ballot(ok) == ~0ull;
+      }
+      const int e = ld_coh_i(s.err);
+      done = all || (e & 0xFF) == kErrTimeout;
+      if (!done) {
+        __builtin_amdgcn_s_sleep(1);
+        if (__builtin_amdgcn_s_memrealtime() - t0 > s.watchdog) {
+          if (lane == 0) raise_error(s.err, kErrTimeout | (stage << 8));
+          done = true;
+        }
+      }
+    }
+  }
+  __syncthreads();
+}
+
 // Workgroup-wide signal after this workgroup's outputs are stored.
 __device__ __forceinline__ void wg_signal(uint32_t* ctr, int who) {
   wave_drain();

@@ -73,6 +73,7 @@ struct Scratch {
   int pos[64];    // positions of the step (valid once pos_ok is set)
   int pos_ok;
   int flag[4];
+  int cnt[kMaxTileCtrs];  // rows this workgroup wrote per row-count counter
 };
 
 // A stage's write-through results held in registers until the wave's

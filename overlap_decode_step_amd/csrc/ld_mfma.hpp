@@ -395,7 +395,7 @@ __device__ __forceinline__ void mfma_stage(const MatRows& mr, int ntile, int K, 
 #pragma unroll
     for (int j = 0; j < RR; ++j) issue(ring[j], j);
   }
-  wait();
+  wait(ks0, ks0 + K);  // (the K range this workgroup reads)
   for (int bp = 0; bp < nbpass; ++bp) {
     const int b0 = bp * prow, nb = min(prow, B - b0);
     ssacc = 0.f;

@@ -15,6 +15,16 @@ constexpr int kLeaves = 16;
 constexpr int kLeafStride = 32;  // uint32 slots between leaves (128 bytes)
 constexpr int kCtrWords = (kLeaves + 1) * kLeafStride;
 
+// Tile-granular readiness.  Besides its stage counter, a stage can signal
+// row-count counters: the QKV stage one per (layer, kv group), counting the
+// q, k and v rows of the group it has written, and the SwiGLU stage one per
+// (layer, chunk of kHChunk rows of its output), so that an attention item
+// waits only for its own group's projections and the Down stage takes its
+// input chunk by chunk (a split-K range waits only for its own chunks).
+// A counter's target after n signalling steps is n times the rows it covers.
+constexpr int kHChunk = 1024;
+constexpr int kMaxTileCtrs = 64;  // kv groups, and chunks, per layer at most
+
 // Stage ids (watchdog error codes and schedule bookkeeping).  kSMlpProj is
 // the projection kernel of the unfused-MLP ablation (kernel lookup only).
 enum : int { kSQkv = 1, kSAttn = 2, kSO = 3, kSGu = 4, kSD = 5, kSLm = 6, kSMlpProj = 7 };
@@ -63,6 +73,7 @@ struct Dims {
   int tied;
   int Hp, qdp, Ip;  // hidden, n_q * head_dim and intermediate rounded up to 32
   int Ht;           // 16-row output tiles of a hidden-sized projection
+  int nhc;          // chunks of kHChunk rows of the SwiGLU output
   float eps;
   float attn_scale;  // 1 / sqrt(head_dim)
 };
@@ -99,6 +110,8 @@ struct Work {
   uint32_t* lm_ctr;     // LM-head last-arriver counter
   uint32_t* split_ctr;  // attention last-arriver counters [L][maxB][nkv][16]
   uint32_t* mctr;       // split-K last-arriver counters: O, then Down, [kMctrPasses][tiles]
+  uint32_t* qg_ctr;     // QKV rows written per (layer, kv group) [L][nkv][counter words]
+  uint32_t* hc_ctr;     // SwiGLU rows written per (layer, chunk) [L][nhc][counter words]
   float* mpart;         // split-K partial tiles [kMaxKSplit][maxB][H]
   // MFMA engine (16 rows and more): activations handed from one of its stages
   // to the next in B-fragment order (frag_word; batch rows padded to 16) as
@@ -127,6 +140,8 @@ struct Step {
   // cumulative counter targets once this step's signals are in
   uint32_t t_qkv, t_attn, t_o, t_gu, t_d, t_lm;
   uint32_t inject;  // debug: added to one wait target to force a watchdog timeout
+  uint32_t n_sig;   // signalling steps enqueued so far, this one included
+  int tile_sync;    // 1: attention and Down wait on the row-count counters
   uint32_t x_cap;   // bytes of LDS for staged input vectors
   int T;            // attention split length of this step (<= Dims::split_len)
   int M;            // tokens per sequence: rows b*M .. b*M + M - 1 are sequence b's

@@ -69,6 +69,45 @@ __device__ __forceinline__ void signal_if(const Params& P, uint32_t* ctr, int wh
   if (!P.S.wait) wg_signal(ctr, who);
 }
 
+// ---- row-count counters (tile-granular readiness, see ld_params.hpp)
+
+__device__ __forceinline__ uint32_t* qg_ctr(const Params& P, int l, int g) {
+  return P.K.qg_ctr + ((int64_t)l * P.D.nkv + g) * kCtrWords;
+}
+__device__ __forceinline__ uint32_t* hc_ctr(const Params& P, int l, int c) {
+  return P.K.hc_ctr + ((int64_t)l * P.D.nhc + c) * kCtrWords;
+}
+// kv group of a QKV output row (q rows of its query heads, then k, then v)
+__device__ __forceinline__ int qkv_group(const Dims& D, int row) {
+  if (row < D.qd) return row / (D.group * D.d);
+  row -= D.qd;
+  if (row >= D.kvd) row -= D.kvd;
+  return row / D.d;
+}
+// rows of the QKV output in one kv group, and of the SwiGLU output in chunk c
+__device__ __forceinline__ uint32_t qkv_group_rows(const Dims& D) { return (uint32_t)((D.group + 2) * D.d); }
+__device__ __forceinline__ uint32_t h_chunk_rows(const Dims& D, int c) {
+  return (uint32_t)min(kHChunk, D.I - c * kHChunk);
+}
+__device__ __forceinline__ bool tile_counting(const Params& P) { return !P.S.wait && P.S.tile_sync; }
+// At stage entry: the workgroup's row counts start at zero (the stage's own
+// barriers order this before its first epilogue).
+__device__ __forceinline__ void counts_clear(const Params& P, Scratch& sc, int n) {
+  if (tile_counting(P) && tid() < n) sc.cnt[tid()] = 0;
+}
+// One output row written (counted once per row, whatever the batch).
+__device__ __forceinline__ void count_row(Scratch& sc, int i) { atomicAdd(&sc.cnt[i], 1); }
+// After the workgroup's outputs are stored: every wave waits for its stores,
+// then counter i gains the rows the workgroup wrote for it (leaf `who`).
+__device__ __forceinline__ void wg_signal_counts(const Params& P, Scratch& sc, uint32_t* (*ctr)(const Params&, int, int),
+                                                 int l, int n, int who) {
+  wave_drain();
+  __syncthreads();
+  if (tid() < n && sc.cnt[tid()] > 0)
+    __hip_atomic_fetch_add(ctr(P, l, tid()) + (who & (kLeaves - 1)) * kLeafStride, (uint32_t)sc.cnt[tid()],
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Optional timeline: thread 0 of each workgroup stores the constant-rate
 // clock (s_memrealtime) at stage entry (ev 0), after the readiness wait
 // (ev 1), after the compute (ev 2) and at stage exit (ev 3), at
@@ -104,7 +143,10 @@ __device__ __forceinline__ void stage_qkv(const Params& P, int l, int wg, int nw
     if (j > 0 && p != P.S.pos[tid() - j] + j) raise_error(P.K.err, kErrPos);
   }
   trace_ev(P, l, kSQkv, 0, wg);
-  auto wait = [&]() {
+  Scratch& scq = *reinterpret_cast<Scratch*>(smem);
+  counts_clear(P, scq, D.nkv);
+  const bool counting = tile_counting(P);
+  auto wait = [&](int = 0, int = 0) {
     if (!P.S.wait && l > 0) wg_wait(sync_of(P), stage_ctr(P, l - 1, kCD), P.S.t_d, kSQkv);
     trace_ev(P, l, kSQkv, 1, wg);
   };
@@ -122,13 +164,21 @@ __device__ __forceinline__ void stage_qkv(const Params& P, int l, int wg, int nw
         if (b < nb && row < rows_total && lane == base + r * NB + b)
           held.hold(out + (int64_t)(b0 + b) * rows_total + row, acc[r][b] * sc.rs[b]);
       }
+    if (counting && b0 == 0 && lane == 0) {
+#pragma unroll
+      for (int r = 0; r < NR; ++r)
+        if (t * NR + r < rows_total) count_row(sc, qkv_group(D, t * NR + r));
+    }
   };
   const uint32_t wbytes = (uint32_t)((int64_t)rows_total * K * 2);
   if constexpr (NB >= kMfmaMinBatch) {
     Scratch& sc = *reinterpret_cast<Scratch*>(smem);
     auto epe = [&](int tile, int r, int b, int bl, int, const float* v) -> float {
       const int row = tile * 16 + r;
-      if (row < rows_total) st_coh(out + (int64_t)b * rows_total + row, v[0] * sc.rs[bl]);
+      if (row < rows_total) {
+        st_coh(out + (int64_t)b * rows_total + row, v[0] * sc.rs[bl]);
+        if (counting && b == 0) count_row(sc, qkv_group(D, row));
+      }
       return 0.f;
     };
     const MatRows mr{Wm, {Wm, Wm}, rows_total, K};
@@ -154,7 +204,10 @@ __device__ __forceinline__ void stage_qkv(const Params& P, int l, int wg, int nw
     held.flush();
   }
   trace_ev(P, l, kSQkv, 2, wg);
-  signal_if(P, stage_ctr(P, l, kCQkv), wg);
+  if (counting)
+    wg_signal_counts(P, scq, qg_ctr, l, D.nkv, wg);
+  else
+    signal_if(P, stage_ctr(P, l, kCQkv), wg);
   trace_ev(P, l, kSQkv, 3, wg);
 }
 
@@ -591,9 +644,19 @@ __device__ __forceinline__ void stage_attn(const Params& P, int l, int wg, int n
   // persistent kernel's SwiGLU weight loads then drain while the items
   // compute, instead of during their combine), and the next stage's wait on
   // this stage's counter orders it after the QKV stage as before.
+  // the item's input: with tile-granular readiness the q, k and v rows of
+  // its own kv group (each item waits for its group), otherwise the whole
+  // QKV stage (one wait covers every item)
+  auto wait_input = [&](int kvh) {
+    if (P.S.wait) return;
+    if (P.S.tile_sync)
+      wg_wait(sync_of(P), qg_ctr(P, l, kvh), P.S.n_sig * qkv_group_rows(D) + P.S.inject, kSAttn);
+    else
+      wg_wait(sync_of(P), stage_ctr(P, l, kCQkv), P.S.t_qkv + P.S.inject, kSAttn);
+  };
   if (any) {
     attn_copy_tiles(P, l, a, smem, !P.S.wait);
-    if (!P.S.wait) wg_wait(sync_of(P), stage_ctr(P, l, kCQkv), P.S.t_qkv + P.S.inject, kSAttn);
+    wait_input(a.kvh);
   } else {
     idle_hook();
   }
@@ -607,6 +670,7 @@ __device__ __forceinline__ void stage_attn(const Params& P, int l, int wg, int n
       it += nwg;
       if (!attn_item_at<MULTI>(P, sc, T, it, a)) break;
       attn_copy_tiles(P, l, a, smem, false);
+      if (P.S.tile_sync) wait_input(a.kvh);
     }
   };
   // the shapes of the Llama-1B, 8B and 70B configurations run with their
@@ -661,7 +725,7 @@ __device__ __forceinline__ void stage_o(const Params& P, int l, int wg, int nwg,
   // stage has run), so the epilogue does not wait for them
   const int t0 = wg * nwaves() + wave_id();
   float pre[NR][NB];
-  auto wait = [&]() {
+  auto wait = [&](int = 0, int = 0) {
     if constexpr (NB < kMfmaMinBatch) {
 #pragma unroll
       for (int r = 0; r < NR; ++r)
@@ -813,7 +877,10 @@ __device__ __forceinline__ void stage_gu(const Params& P, int l, int wg, int nwg
   const GuStream ws(rows, gu_tiles(P), K, layer_w(P, l, 0), (uint32_t)(P.W.layer_stride * 2), wg,
                     nwg);
   trace_ev(P, l, kSGu, 0, wg);
-  auto wait = [&]() {
+  Scratch& scg = *reinterpret_cast<Scratch*>(smem);
+  counts_clear(P, scg, D.nhc);
+  const bool counting = tile_counting(P);
+  auto wait = [&](int = 0, int = 0) {
     if (!P.S.wait) wg_wait(sync_of(P), stage_ctr(P, l, kCO), P.S.t_o, kSGu);
     trace_ev(P, l, kSGu, 1, wg);
   };
@@ -832,6 +899,11 @@ __device__ __forceinline__ void stage_gu(const Params& P, int l, int wg, int nwg
           held.hold(h + (int64_t)(b0 + b) * I + row, a / (1.0f + expf(-a)) * u);
         }
       }
+    if (counting && b0 == 0 && lane == 0) {
+#pragma unroll
+      for (int r = 0; r < NP; ++r)
+        if (t * NP + r < I) count_row(sc, (t * NP + r) / kHChunk);
+    }
   };
   const int bw = (P.S.gu_variant == kGuRow) ? 1 : batch_tile(P, K, NB);
   if constexpr (NB >= kMfmaMinBatch) {
@@ -845,6 +917,7 @@ __device__ __forceinline__ void stage_gu(const Params& P, int l, int wg, int nwg
       const float a = v[0] * sc.rs[bl], u = v[1] * sc.rs[bl];
       // for the Down stage (MFMA engine too): fragments of split-bf16 pairs
       st_coh_u(P.K.h_f + frag_word(b, row, D.Ip), split_pair(a / (1.0f + expf(-a)) * u));
+      if (counting && b == 0) count_row(sc, row / kHChunk);
       return 0.f;
     };
     (void)h;
@@ -865,7 +938,10 @@ __device__ __forceinline__ void stage_gu(const Params& P, int l, int wg, int nwg
     held.flush();
   }
   trace_ev(P, l, kSGu, 2, wg);
-  signal_if(P, stage_ctr(P, l, kCGu), wg);
+  if (counting)
+    wg_signal_counts(P, scg, hc_ctr, l, D.nhc, wg);
+  else
+    signal_if(P, stage_ctr(P, l, kCGu), wg);
   trace_ev(P, l, kSGu, 3, wg);
 }
 
@@ -978,7 +1054,7 @@ __device__ __forceinline__ void stage_d(const Params& P, int l, int wg, int nwg,
   // before the readiness wait
   const int t0 = wg * nwaves() + wave_id();
   float pre[NR][NB];
-  auto wait = [&]() {
+  auto wait = [&](int k0 = 0, int k1 = 0x7FFFFFFF) {
     if constexpr (NB < kMfmaMinBatch) {
 #pragma unroll
       for (int r = 0; r < NR; ++r)
@@ -990,7 +1066,18 @@ __device__ __forceinline__ void stage_d(const Params& P, int l, int wg, int nwg,
                           : 0.f;
         }
     }
-    if (!P.S.wait) wg_wait(sync_of(P), stage_ctr(P, l, kCGu), P.S.t_gu, kSD);
+    if (!P.S.wait) {
+      if (P.S.tile_sync) {
+        // only the SwiGLU output chunks of the workgroup's K range [k0, k1)
+        // (all of them for the VALU engine), polled together
+        const int c0 = k0 / kHChunk, c1 = min(D.nhc, (min(k1, D.I) + kHChunk - 1) / kHChunk);
+        const uint32_t n = P.S.n_sig;
+        wg_wait_all(sync_of(P), hc_ctr(P, l, c0), c1 - c0,
+                    [&](int i) { return n * h_chunk_rows(D, c0 + i); }, kSD);
+      } else {
+        wg_wait(sync_of(P), stage_ctr(P, l, kCGu), P.S.t_gu, kSD);
+      }
+    }
     trace_ev(P, l, kSD, 1, wg);
   };
   HeldStores<(NB > 1)> held;
@@ -1075,7 +1162,7 @@ __device__ __forceinline__ void stage_lm(const Params& P, int wg, int nwg, char*
     }
   };
   trace_ev(P, D.L, kSLm, 0, wg);
-  auto wait = [&]() {
+  auto wait = [&](int = 0, int = 0) {
     if (!P.S.wait) wg_wait(sync_of(P), stage_ctr(P, D.L - 1, kCD), P.S.t_d, kSLm);
     trace_ev(P, D.L, kSLm, 1, wg);
   };

@@ -17,6 +17,8 @@ LD_MODE_WAIT, LD_MODE_FLAGS, LD_MODE_MEGA, LD_MODE_GRAPH = 0, 1, 2, 3
 MODES = {"wait": LD_MODE_WAIT, "flags": LD_MODE_FLAGS, "mega": LD_MODE_MEGA, "graph": LD_MODE_GRAPH}
 LD_SWIGLU_COL, LD_SWIGLU_ROW = 0, 1
 LD_ACT_X, LD_ACT_QKV, LD_ACT_ATTN, LD_ACT_H = 0, 1, 2, 3
+LD_SYNC_STAGE, LD_SYNC_TILE, LD_SYNC_AUTO = 0, 1, 2
+SYNC = {"stage": LD_SYNC_STAGE, "tile": LD_SYNC_TILE, "auto": LD_SYNC_AUTO}
 LD_MLP_FUSED, LD_MLP_TWO_KERNELS, LD_MLP_FOUR_KERNELS = 0, 1, 2
 MLP_VARIANTS = {"fused": LD_MLP_FUSED, "two": LD_MLP_TWO_KERNELS, "four": LD_MLP_FOUR_KERNELS}
 (LD_W_EMBED, LD_W_ATTN_NORM, LD_W_Q, LD_W_K, LD_W_V, LD_W_O, LD_W_MLP_NORM, LD_W_GATE, LD_W_UP,
@@ -68,6 +70,7 @@ def _load():
         "ld_set_mlp_variant": (S, [P, I32]),
         "ld_get_swiglu_variant": (I32, [P, I32]),
         "ld_set_watchdog": (S, [P, D]),
+        "ld_set_sync": (S, [P, I32]),
         "ld_debug_inject_stall": (S, [P]),
         "ld_launch_info": (S, [P, P, I32]),
         "ld_read_activation": (S, [P, I32, I32, P]),
@@ -192,6 +195,10 @@ def ld_get_swiglu_variant(m, batch):
     return int(LIB.ld_get_swiglu_variant(m, batch))
 
 
+def ld_set_sync(m, granularity):
+    return _check(LIB.ld_set_sync(m, SYNC.get(granularity, granularity)), m)
+
+
 def ld_set_watchdog(m, seconds):
     return _check(LIB.ld_set_watchdog(m, seconds), m)
 
@@ -271,6 +278,9 @@ class Model:
 
     def set_mode(self, mode):
         ld_set_mode(self.h, mode)
+
+    def set_sync(self, granularity):
+        ld_set_sync(self.h, granularity)
 
     def set_mlp_variant(self, variant):
         ld_set_mlp_variant(self.h, variant)

@@ -737,3 +737,43 @@ def test_position_zero_attention_returns_v(ld, orc, B):
                     got = ((bits & 0xFFFF) << 16).view(np.float32)
                 assert np.array_equal(got, want), f"mode={mode} seq={b} head={hq}: output is not V"
     m.free()
+
+
+SYNC_CASES = [("tiny", 1), ("tiny", 5), ("tiny", 16), ("tiny", 45), ("ragged", 3), ("llama1b", 1),
+              ("llama1b", 16)]
+
+
+@pytest.mark.parametrize("name,B", SYNC_CASES, ids=[f"{n}-B{b}" for n, b in SYNC_CASES])
+def test_tile_granular_readiness(ld, orc, name, B):
+    # The two readiness granularities of the tile-flag and persistent modes:
+    # per kv group (QKV -> attention) and per 1024-row chunk (SwiGLU -> Down)
+    # against whole-stage counters.  Both give bitwise-equal logits, every row
+    # matches the oracle, and steps may switch granularity in between (each
+    # counter advances only on the steps that signal it).
+    shape = RAGGED if name == "ragged" else W.SHAPES[name]
+    w_std = 0.05 if name == "ragged" else 0.02
+    maxs = 1200 if name == "ragged" else (1040 if name == "llama1b" else 256)
+    prefill = ([1100, 512, 1] if name == "ragged" else
+               W.kv_lengths(B, 256, 1024) if name == "llama1b" else W.kv_lengths(B, 1, 200))
+    om = orc.model(shape, seed=W.SEED_WEIGHTS, w_std=w_std)
+    toks = W.first_tokens(B, shape["vocab"])
+    seqs = range(B) if B <= 5 else (0, B - 1)
+    refs = {}
+    for b in seqs:
+        okv = orc.kv(shape, 1, maxs, seed=W.SEED_KV, kv_std=1.0, prefill=[prefill[b]], seq0=b)
+        refs[b] = orc.decode_one(om, okv, 0, toks[b], prefill[b])
+    m = gpu_model(ld, shape, B, maxs, prefill, w_std=w_std)
+    run = GpuRunner(m, shape["vocab"], B)
+    for mode in ("flags", "mega"):
+        m.set_mode(mode)
+        outs = []
+        for sync in ("tile", "stage", "tile"):
+            m.set_sync(sync)
+            m.fill_kv(W.SEED_KV, 1.0, prefill)
+            lg, nx = run.step(toks, prefill)
+            for b, (ref, rn) in refs.items():
+                check_row(lg[b], ref, nx[b], rn, f"{name} B={B} mode={mode} sync={sync} seq={b}")
+            outs.append(lg)
+        assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2]), \
+            f"{name} B={B} mode={mode}: the readiness granularity changed the results"
+    m.free()
