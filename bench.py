@@ -288,6 +288,60 @@ def tune_tables(shape_name, batches, modes):
     return out
 
 
+def long_generation(batches=(1, 4, 16), prefills=(1024, 16384), modes=("wait", "mega"),
+                    steps=4, warmup=2):
+    """Long generation at the Llama-70B shape (80 layers, about 141 GB of
+    bf16 weights, N(0, 0.01)) on one GPU: every sequence of the batch at KV
+    length p, `steps` greedy steps timed after `warmup`, for each batch size,
+    KV length and mode.  Returns rows of (batch, prefill, mode, ms per step,
+    tokens/s, algorithmic bytes per step, fraction of 8 TB/s)."""
+    import torch
+    from overlap_decode_step_amd import ld
+    from synth import workloads as W
+    shape = W.LLAMA_70B
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    maxb, maxs = max(batches), max(prefills) + steps + warmup + 8
+    m = ld.Model(shape, seed=W.SEED_WEIGHTS, w_std=W.WORKLOADS["llama70b"]["w_std"])
+    m.alloc_kv(maxb, maxs)
+    stream = torch.cuda.current_stream()
+    rows = []
+    for B in batches:
+        logits = torch.empty((B, shape["vocab"]), dtype=torch.float32, device=dev)
+        toks = torch.tensor(W.first_tokens(B, shape["vocab"]), dtype=torch.int32, device=dev)
+        tbuf = [toks.clone(), torch.empty_like(toks)]
+        for p in prefills:
+            pos = [torch.full((B,), p + i, dtype=torch.int32, device=dev)
+                   for i in range(steps + warmup)]
+            for mode in modes:
+                m.set_mode(mode)
+                m.fill_kv(W.SEED_KV, 1.0, [p] * B + [0] * (maxb - B))
+                tbuf[0].copy_(toks)
+                for i in range(warmup):
+                    m.step(tbuf[i & 1], pos[i], logits, tbuf[(i + 1) & 1])
+                torch.cuda.synchronize()
+                ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                ev0.record(stream)
+                for i in range(warmup, warmup + steps):
+                    m.step(tbuf[i & 1], pos[i], logits, tbuf[(i + 1) & 1])
+                ev1.record(stream)
+                torch.cuda.synchronize()
+                if m.device_error() != 0:
+                    raise RuntimeError(f"device error at batch {B} KV {p} mode {mode}")
+                ms = ev0.elapsed_time(ev1) / steps
+                nbytes = sum(algorithmic_bytes(shape, B, [p + i] * B)
+                             for i in range(warmup, warmup + steps)) / steps
+                row = {"batch": B, "kv": p, "mode": mode, "ms_per_step": ms,
+                       "tokens_per_s": B * 1000.0 / ms, "bytes_per_step": nbytes,
+                       "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+                rows.append(row)
+                print(f"# long-gen batch={B} kv={p} mode={mode} ms/step={ms:.3f} "
+                      f"tok/s={row['tokens_per_s']:.1f} frac={row['hbm_frac']:.3f}",
+                      file=sys.stderr, flush=True)
+    m.free()
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -316,6 +370,11 @@ def main():
                     help="readiness granularity of the tile-flag and persistent modes")
     ap.add_argument("--prefill", type=int, default=None,
                     help="KV prefill per sequence (default 512 for llama1b, else 1024)")
+    ap.add_argument("--no-free", action="store_true",
+                    help="leave the model to be freed at interpreter exit")
+    ap.add_argument("--long-gen", action="store_true",
+                    help="only run long generation at the Llama-70B shape (batch 1, 4, 16; "
+                         "KV 1024 and 16384; whole-kernel-wait and persistent modes)")
     ap.add_argument("--tune", default=None,
                     help="only run the offline SwiGLU tiling choice at this shape for the "
                          "comma-separated batch sizes of --tune-batches, in every mode")
@@ -326,6 +385,10 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.long_gen:
+        rows = long_generation()
+        print(json.dumps({"long_generation": "llama70b", "rows": rows}), flush=True)
         return
     if args.tune:
         batches = [int(b) for b in args.tune_batches.split(",")]
@@ -430,8 +493,9 @@ def main():
             print(f"# mlp={variant} mode=wait batch={B} ms/step={ablation[variant]:.4f}",
                   file=sys.stderr, flush=True)
         m.set_mlp_variant("fused")
-    m.free()
-    del m
+    if not args.no_free:
+        m.free()
+        del m
     torch.cuda.synchronize()
     positions = [prefill + i for i in range(steps)]
     bytes_avg = sum(algorithmic_bytes(shape, B, [p] * B) for p in positions) / steps

@@ -654,7 +654,8 @@ static ld_status enqueue_step(ld_model* m, const int32_t* tokens, int32_t B, int
   // splits (fewer items and partial results); below 16 rows every mode uses
   // the same splits, so they add the same numbers in the same order
   if (m->mode != LD_MODE_FLAGS) P.D.split_len = m->split_len_full;
-  P.S.T = step_split_len(B >= kMfmaMinBatch ? P.D.split_len : m->D.split_len, B);
+  P.S.Tmax = B >= kMfmaMinBatch ? P.D.split_len : m->D.split_len;
+  P.S.T = step_split_len(P.S.Tmax, B);
   P.S.gu_variant = m->gu_variant[m->mode][B];
   P.S.inject = m->inject_next;
   m->inject_next = 0;

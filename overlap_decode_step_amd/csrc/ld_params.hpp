@@ -144,6 +144,7 @@ struct Step {
   int tile_sync;    // 1: attention and Down wait on the row-count counters
   uint32_t x_cap;   // bytes of LDS for staged input vectors
   int T;            // attention split length of this step (<= Dims::split_len)
+  int Tmax;         // longest split a long context may take (<= Dims::split_len)
   int M;            // tokens per sequence: rows b*M .. b*M + M - 1 are sequence b's
                     // consecutive positions (KV cache slot b); 1 for a decode step
 };

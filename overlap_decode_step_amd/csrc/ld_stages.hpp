@@ -575,42 +575,47 @@ __device__ __forceinline__ void attn_item(const Params& P, int l, const AttnItem
     __syncthreads();
     trace_ev(P, l, 7, 3, blockIdx.x);
     if (!sc.flag[0]) return;
-    // per output channel: M = max_s m_s, f_s = e^(m_s - M), L = sum_s l_s f_s,
-    // o = (sum_s o_s f_s) / L, splits in ascending order.  Up to kCombBatch
-    // splits' (m, l, o) are loaded in one round and kept in registers.
+    // M = max_s m_s, f_s = e^(m_s - M), L = sum_s l_s f_s and, per output
+    // channel, o = (sum_s o_s f_s) / L.  First M and L per head: wave g takes
+    // head g with its lanes over the splits (lane-local in ascending split
+    // order, then a fixed wave-wide tree).  Then each thread's channels, the
+    // splits in ascending order, kCombBatch splits' (m, o) loaded per round.
     const float* pbase = P.K.part + ((int64_t)b * D.nq + kvh * group) * D.max_splits * (d + 2);
+    __syncthreads();  // (s.ml is reused)
+    for (int g = wave; g < group; g += nwaves()) {
+      const float* q = pbase + (int64_t)g * D.max_splits * (d + 2);
+      float M = -INFINITY;
+      for (int u = lane; u < nsplit; u += kWave) M = fmaxf(M, ld_coh(q + u * (d + 2)));
+      M = wave_max(M);
+      float Ls = 0.f;
+      for (int u = lane; u < nsplit; u += kWave)
+        Ls = fmaf(ld_coh(q + u * (d + 2) + 1), expf(ld_coh(q + u * (d + 2)) - M), Ls);
+      Ls = wave_sum(Ls);
+      if (lane == 0) {
+        s.ml[2 * g] = M;
+        s.ml[2 * g + 1] = Ls;
+      }
+    }
+    __syncthreads();
     for (int r = tid; r < gd; r += nth) {
       const int g = r >> ld, i = r & (d - 1);
       const float* q = pbase + (int64_t)g * D.max_splits * (d + 2);
-      float mv[kCombBatch], lv[kCombBatch], ov[kCombBatch];
+      const float M = s.ml[2 * g];
+      float O = 0.f;
+      for (int s0 = 0; s0 < nsplit; s0 += kCombBatch) {
+        float mv[kCombBatch], ov[kCombBatch];
 #pragma unroll
-      for (int u = 0; u < kCombBatch; ++u) {
-        if (u < nsplit) {
-          mv[u] = ld_coh(q + u * (d + 2));
-          lv[u] = ld_coh(q + u * (d + 2) + 1);
-          ov[u] = ld_coh(q + u * (d + 2) + 2 + i);
+        for (int u = 0; u < kCombBatch; ++u) {
+          if (s0 + u < nsplit) {
+            mv[u] = ld_coh(q + (s0 + u) * (d + 2));
+            ov[u] = ld_coh(q + (s0 + u) * (d + 2) + 2 + i);
+          }
         }
-      }
-      float M = -INFINITY;
 #pragma unroll
-      for (int u = 0; u < kCombBatch; ++u)
-        if (u < nsplit) M = fmaxf(M, mv[u]);
-      for (int s0 = kCombBatch; s0 < nsplit; ++s0) M = fmaxf(M, ld_coh(q + s0 * (d + 2)));
-      float L = 0.f, O = 0.f;
-#pragma unroll
-      for (int u = 0; u < kCombBatch; ++u) {
-        if (u < nsplit) {
-          const float f = expf(mv[u] - M);
-          L = fmaf(lv[u], f, L);
-          O = fmaf(ov[u], f, O);
-        }
+        for (int u = 0; u < kCombBatch; ++u)
+          if (s0 + u < nsplit) O = fmaf(ov[u], expf(mv[u] - M), O);
       }
-      for (int s0 = kCombBatch; s0 < nsplit; ++s0) {
-        const float f = expf(ld_coh(q + s0 * (d + 2)) - M);
-        L = fmaf(ld_coh(q + s0 * (d + 2) + 1), f, L);
-        O = fmaf(ld_coh(q + s0 * (d + 2) + 2 + i), f, O);
-      }
-      st_ao(P, b, oc + r, O / L);
+      st_ao(P, b, oc + r, O / s.ml[2 * g + 1]);
     }
   }
   signal_if(P, stage_ctr(P, l, kCAttn), b * D.nkv + kvh);
@@ -635,7 +640,18 @@ __device__ __forceinline__ void stage_attn(const Params& P, int l, int wg, int n
     __syncthreads();
     if (tid() == 0) sc.pos_ok = 1;
   }
-  const int T = P.S.T;
+  // split length: the step's (from its batch size), or longer when the
+  // step's contexts would otherwise make far more items than workgroups (a
+  // long context), up to the LDS tiles' capacity.  It depends on the
+  // positions and the grid only, so every workgroup (and every mode) finds
+  // the same one.
+  int T = P.S.T;
+  {
+    int64_t total = 0;
+    for (int b = 0; b < P.S.B; ++b) total += sc.pos[b] + 1;
+    const int64_t need = (total * D.nkv + nwg - 1) / nwg;
+    if (need > T) T = (int)min((int64_t)P.S.Tmax, (need + 31) / 32 * 32);
+  }
   AttnItem a;
   const bool any = attn_item_at<MULTI>(P, sc, T, wg, a);
   // the first item's cached rows are copied while this stage's input is
