@@ -72,6 +72,7 @@ struct Scratch {
   float rs[64];   // deferred-norm factors of the staged batch rows
   int pos[64];    // positions of the step (valid once pos_ok is set)
   int pos_ok;
+  int attn_T;     // the attention stage's split length (set with pos)
   int flag[4];
   int cnt[kMaxTileCtrs];  // rows this workgroup wrote per row-count counter
 };

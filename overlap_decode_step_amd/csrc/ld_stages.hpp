@@ -259,13 +259,13 @@ __device__ __forceinline__ void st_ao(const Params& P, int b, int c, float v) {
     st_coh(P.K.ao + (int64_t)b * P.D.qd + c, v);
 }
 
+constexpr int kCombBatch = 16;  // splits combined from registers in one round of loads
+
 // Row b of the step (token j = b % M of sequence slot = b / M, at position
 // p = p0 + j, where p0 is the sequence's first position of this step).
 struct AttnItem {
   int b, kvh, s, ns, p, slot, p0;
 };
-
-constexpr int kCombBatch = 16;  // splits combined from registers in one round of loads
 
 // Item `it` of the step (sequence-major, then kv head, then split).
 // MULTI: the step may hold several tokens per sequence (P.S.M > 1); the
@@ -576,46 +576,45 @@ __device__ __forceinline__ void attn_item(const Params& P, int l, const AttnItem
     trace_ev(P, l, 7, 3, blockIdx.x);
     if (!sc.flag[0]) return;
     // M = max_s m_s, f_s = e^(m_s - M), L = sum_s l_s f_s and, per output
-    // channel, o = (sum_s o_s f_s) / L.  First M and L per head: wave g takes
-    // head g with its lanes over the splits (lane-local in ascending split
-    // order, then a fixed wave-wide tree).  Then each thread's channels, the
-    // splits in ascending order, kCombBatch splits' (m, o) loaded per round.
+    // channel, o = (sum_s o_s f_s) / L: per channel, the splits in ascending
+    // order, kCombBatch splits' (m, l, o) loaded per round; from a second
+    // round on (more than kCombBatch splits: a long context) the running L
+    // and O are rescaled by e^(M_old - M_new) when the maximum grows.
     const float* pbase = P.K.part + ((int64_t)b * D.nq + kvh * group) * D.max_splits * (d + 2);
-    __syncthreads();  // (s.ml is reused)
-    for (int g = wave; g < group; g += nwaves()) {
-      const float* q = pbase + (int64_t)g * D.max_splits * (d + 2);
-      float M = -INFINITY;
-      for (int u = lane; u < nsplit; u += kWave) M = fmaxf(M, ld_coh(q + u * (d + 2)));
-      M = wave_max(M);
-      float Ls = 0.f;
-      for (int u = lane; u < nsplit; u += kWave)
-        Ls = fmaf(ld_coh(q + u * (d + 2) + 1), expf(ld_coh(q + u * (d + 2)) - M), Ls);
-      Ls = wave_sum(Ls);
-      if (lane == 0) {
-        s.ml[2 * g] = M;
-        s.ml[2 * g + 1] = Ls;
-      }
-    }
-    __syncthreads();
     for (int r = tid; r < gd; r += nth) {
       const int g = r >> ld, i = r & (d - 1);
       const float* q = pbase + (int64_t)g * D.max_splits * (d + 2);
-      const float M = s.ml[2 * g];
-      float O = 0.f;
+      float M = -INFINITY, L = 0.f, O = 0.f;
       for (int s0 = 0; s0 < nsplit; s0 += kCombBatch) {
-        float mv[kCombBatch], ov[kCombBatch];
+        float mv[kCombBatch], lv[kCombBatch], ov[kCombBatch];
 #pragma unroll
         for (int u = 0; u < kCombBatch; ++u) {
           if (s0 + u < nsplit) {
             mv[u] = ld_coh(q + (s0 + u) * (d + 2));
+            lv[u] = ld_coh(q + (s0 + u) * (d + 2) + 1);
             ov[u] = ld_coh(q + (s0 + u) * (d + 2) + 2 + i);
           }
         }
+        float Mn = M;
 #pragma unroll
         for (int u = 0; u < kCombBatch; ++u)
-          if (s0 + u < nsplit) O = fmaf(ov[u], expf(mv[u] - M), O);
+          if (s0 + u < nsplit) Mn = fmaxf(Mn, mv[u]);
+        if (s0 > 0) {  // (first round: L = O = 0, nothing to rescale)
+          const float c = expf(M - Mn);
+          L *= c;
+          O *= c;
+        }
+        M = Mn;
+#pragma unroll
+        for (int u = 0; u < kCombBatch; ++u) {
+          if (s0 + u < nsplit) {
+            const float f = expf(mv[u] - M);
+            L = fmaf(lv[u], f, L);
+            O = fmaf(ov[u], f, O);
+          }
+        }
       }
-      st_ao(P, b, oc + r, O / s.ml[2 * g + 1]);
+      st_ao(P, b, oc + r, O / L);
     }
   }
   signal_if(P, stage_ctr(P, l, kCAttn), b * D.nkv + kvh);
@@ -635,23 +634,26 @@ __device__ __forceinline__ void stage_attn(const Params& P, int l, int wg, int n
   const Dims& D = P.D;
   trace_ev(P, l, kSAttn, 0, wg);
   Scratch& sc = *reinterpret_cast<Scratch*>(smem);
-  if (!sc.pos_ok) {  // positions of the step, read once per kernel
-    if (tid() < P.S.B) sc.pos[tid()] = clamp_pos(P, tid());
-    __syncthreads();
-    if (tid() == 0) sc.pos_ok = 1;
-  }
   // split length: the step's (from its batch size), or longer when the
   // step's contexts would otherwise make far more items than workgroups (a
   // long context), up to the LDS tiles' capacity.  It depends on the
   // positions and the grid only, so every workgroup (and every mode) finds
-  // the same one.
-  int T = P.S.T;
-  {
-    int64_t total = 0;
-    for (int b = 0; b < P.S.B; ++b) total += sc.pos[b] + 1;
-    const int64_t need = (total * D.nkv + nwg - 1) / nwg;
-    if (need > T) T = (int)min((int64_t)P.S.Tmax, (need + 31) / 32 * 32);
+  // the same one.  Positions and split length are found once per kernel.
+  if (!sc.pos_ok) {
+    if (tid() < P.S.B) sc.pos[tid()] = clamp_pos(P, tid());
+    __syncthreads();
+    if (tid() == 0) {
+      int64_t total = 0;
+      for (int b = 0; b < P.S.B; ++b) total += sc.pos[b] + 1;
+      const int64_t need = (total * D.nkv + nwg - 1) / nwg;
+      int T = P.S.T;
+      if (need > T) T = (int)min((int64_t)P.S.Tmax, (need + 31) / 32 * 32);
+      sc.attn_T = T;
+      sc.pos_ok = 1;
+    }
+    __syncthreads();
   }
+  const int T = __builtin_amdgcn_readfirstlane(sc.attn_T);
   AttnItem a;
   const bool any = attn_item_at<MULTI>(P, sc, T, wg, a);
   // the first item's cached rows are copied while this stage's input is
