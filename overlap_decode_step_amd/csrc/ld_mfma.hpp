@@ -141,6 +141,34 @@ template <int NBT, int RING>
 constexpr int kDirectRing =
     kDirectRingRaw<NBT, RING> < 2 ? 2 : (kDirectRingRaw<NBT, RING> > RING ? RING : kDirectRingRaw<NBT, RING>);
 
+// Deferred-norm sums from a fragment source: ss[b * ss_ld + q], q < ss_n,
+// are the producer's sums of squares per (batch row, 16-row output tile).
+// Row b of a pass is read by the kSsGroup threads t = 8 b .. 8 b + 7, thread
+// p adding tiles p, p + 8, ... in ascending order, U of its loads issued
+// before any is used (a clamped index past the end reads a valid word that
+// is not added); the group then adds its 8 partials in a fixed tree
+// (lane_group_sum), the sum landing in its last lane.  The group size is
+// fixed, so every pass size, tiling and mode adds the same numbers in the
+// same order.
+constexpr int kSsGroup = 8;
+__device__ __forceinline__ float ss_partial(const XSrc& src, int b0, int nb, int t) {
+  constexpr int U = 16, G = kSsGroup;
+  const int b = t / G, p = t - b * G;
+  float s2 = 0.f;
+  if (b < nb) {
+    const float* row = src.ss + (int64_t)(b0 + b) * src.ss_ld;
+    for (int q0 = p; q0 < src.ss_n; q0 += U * G) {
+      float v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = ld_coh(row + min(q0 + u * G, src.ss_n - 1));
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (q0 + u * G < src.ss_n) s2 += v[u];
+    }
+  }
+  return s2;
+}
+
 // Rows of NT weight matrices in one buffer: tile t, matrix j, row r (0..15).
 struct MatRows {
   const uint16_t* base;
@@ -419,6 +447,12 @@ __device__ __forceinline__ void mfma_stage(const MatRows& mr, int ntile, int K, 
 #pragma unroll
           for (int bt = 0; bt < NBT; ++bt) acc[m][j][bt] = f32x4{0.f, 0.f, 0.f, 0.f};
       if constexpr (!DIRECT) stage_chunk(b0, nb, 0, sums);
+      // fragment source: this thread's share of the norm sums, read before
+      // the K loop (its loads overlap the first K steps' loads)
+      float ssp = 0.f;
+      if constexpr (FRAG) {
+        if (sums) ssp = ss_partial(src, b0, nb, t);
+      }
       // ---- one ring over the whole K stream; a chunk boundary restages the
       // inputs while the next chunk's weight loads are already in flight
       for (int i0 = 0; i0 < nslot; i0 += RR) {
@@ -478,17 +512,14 @@ __device__ __forceinline__ void mfma_stage(const MatRows& mr, int ntile, int K, 
       }
       // ---- norms of this batch pass (first tile pass only)
       if constexpr (FRAG) {
-        // from the producer's sums of squares per (row, output tile): thread
-        // t < 8 prow adds tiles p, p + 8, ... of row t / 8 (p = t % 8), then
-        // the 8 lanes of the row are added in a fixed tree
+        // from the producer's sums of squares (ss_partial, read before the
+        // K loop): each row's group of kSsGroup threads adds its partials
         if (sums) {
-          const int b = t >> 3, p = t & 7;
-          float s2 = 0.f;
-          if (b < nb)
-            for (int q = p; q < src.ss_n; q += 8) s2 += ld_coh(src.ss + (int64_t)(b0 + b) * src.ss_ld + q);
-          s2 = lane_group_sum(s2, 8);
+          const float s2 = lane_group_sum(ssp, kSsGroup);
           __syncthreads();
-          if (b < nb && p == 7) sc.rs[b] = 1.0f / sqrtf(s2 / (float)Kfull + eps);
+          const int b = t / kSsGroup;
+          if (b < nb && t - b * kSsGroup == kSsGroup - 1)
+            sc.rs[b] = 1.0f / sqrtf(s2 / (float)Kfull + eps);
         }
       } else if (sums) {
         __syncthreads();

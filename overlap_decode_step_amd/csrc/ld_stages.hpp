@@ -1295,41 +1295,57 @@ __device__ __forceinline__ void stage_lm(const Params& P, int wg, int nwg, char*
   __syncthreads();
   trace_ev(P, D.L, kSLm, 3, wg);
   if (!sc.flag[1] || P.S.next == nullptr) return;
-  // last arriver: reduce the partials of every workgroup, per sequence
-  for (int b = 0; b < B; ++b) {
-    float bv = -INFINITY;
-    int bi = 0x7FFFFFFF;
-    for (int w = tid(); w < nwg; w += blockDim.x) {
-      const float v = ld_coh(P.K.lm_val + (int64_t)w * D.max_batch + b);
-      const int i = ld_coh_i(P.K.lm_idx + (int64_t)w * D.max_batch + b);
-      if (better(v, i, bv, bi)) {
-        bv = v;
-        bi = i;
-      }
+  // last arriver: reduce the partials of every workgroup, per sequence.  Wave
+  // w takes rows w, w + nw, ... four at a time, its lanes reading the
+  // partials of workgroups lane, lane + 64, ... (every load of a round issued
+  // before any is used; a clamped index past the end reads a valid partial
+  // that is not compared), then a wave-wide argmax.  The comparison (larger
+  // value, then lower index; NaN never wins) makes the result independent of
+  // the order.
+  constexpr int RB = 4, WU = 4;  // rows and workgroup partials per lane per round
+  const int nw = nwaves();
+  for (int r0 = wave; r0 < B; r0 += RB * nw) {
+    float bv[RB];
+    int bi[RB];
+#pragma unroll
+    for (int k = 0; k < RB; ++k) {
+      bv[k] = -INFINITY;
+      bi[k] = 0x7FFFFFFF;
+    }
+    for (int w0 = lane; w0 < nwg; w0 += WU * kWave) {
+      float v[RB][WU];
+      int ix[RB][WU];
+#pragma unroll
+      for (int k = 0; k < RB; ++k)
+#pragma unroll
+        for (int u = 0; u < WU; ++u) {
+          const int b = min(r0 + k * nw, B - 1), w = min(w0 + u * kWave, nwg - 1);
+          v[k][u] = ld_coh(P.K.lm_val + (int64_t)w * D.max_batch + b);
+          ix[k][u] = ld_coh_i(P.K.lm_idx + (int64_t)w * D.max_batch + b);
+        }
+#pragma unroll
+      for (int k = 0; k < RB; ++k)
+#pragma unroll
+        for (int u = 0; u < WU; ++u)
+          if (w0 + u * kWave < nwg && better(v[k][u], ix[k][u], bv[k], bi[k])) {
+            bv[k] = v[k][u];
+            bi[k] = ix[k][u];
+          }
     }
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off, kWave);
-      const int oi = __shfl_xor(bi, off, kWave);
-      if (better(ov, oi, bv, bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
-    if (lane == 0) {
-      bs.v[wave][0] = bv;
-      bs.i[wave][0] = bi;
-    }
-    __syncthreads();
-    if (tid() == 0) {
-      for (int w = 1; w < nwaves(); ++w)
-        if (better(bs.v[w][0], bs.i[w][0], bv, bi)) {
-          bv = bs.v[w][0];
-          bi = bs.i[w][0];
+    for (int k = 0; k < RB; ++k) {
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        const float ov = __shfl_xor(bv[k], off, kWave);
+        const int oi = __shfl_xor(bi[k], off, kWave);
+        if (better(ov, oi, bv[k], bi[k])) {
+          bv[k] = ov;
+          bi[k] = oi;
         }
-      P.S.next[b] = (bi == 0x7FFFFFFF) ? 0 : bi;
+      }
+      const int b = r0 + k * nw;
+      if (lane == 0 && b < B) P.S.next[b] = (bi[k] == 0x7FFFFFFF) ? 0 : bi[k];
     }
-    __syncthreads();
   }
 }
 
