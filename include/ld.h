@@ -85,7 +85,8 @@ typedef enum {
   LD_EHIP = -3,     /* a HIP runtime call failed */
   LD_ETIMEOUT = -4, /* a device-side wait exceeded the watchdog */
   LD_ESTATE = -5,   /* call out of order (e.g. decode before ld_alloc_kv) */
-  LD_EDEVICE = -6   /* device input error (bad token or position) */
+  LD_EDEVICE = -6,  /* device input error (bad token or position) */
+  LD_EAUDIT = -7    /* ld_audit found a counter off its expected value */
 } ld_status;
 
 typedef enum { LD_MODE_WAIT = 0, LD_MODE_FLAGS = 1, LD_MODE_MEGA = 2, LD_MODE_GRAPH = 3 } ld_mode;

@@ -90,6 +90,35 @@ ld_status ld_set_watchdog(ld_model* m, double seconds);
  * exits; ld_device_error() then reports LD_ETIMEOUT and resets the counters. */
 ld_status ld_debug_inject_stall(ld_model* m);
 
+/* Debug mechanisms (race and protocol checks; off by default).
+ *
+ * ld_set_debug(m, LD_DEBUG_POISON): before every following decode step (same
+ * stream, asynchronous like the step) every activation, partial-result and
+ * hand-off buffer of the work arena, the caller's logits rows and next
+ * tokens, and the KV-cache rows the step appends (each row's position, every
+ * layer and kv head) are filled with quiet NaNs.  A stage that reads a word
+ * before its producer wrote it then turns the logits into NaN; a correct
+ * step returns exactly the logits it returns without the poison.  Fragment
+ * buffers of the MFMA engine whose K (hidden, n_q d or intermediate) is not a
+ * multiple of 32 are left out (their padding columns must stay zero).
+ * flags 0 turns it off; LD_EINVAL for an unknown flag.
+ *
+ * ld_audit(m): synchronises, then checks every readiness counter against
+ * what the steps enqueued so far imply: each layer's stage counters equal the
+ * host's running totals (their leaves added modulo 2^32), the row-count
+ * counters the tile-granular steps times the rows of their kv group or
+ * SwiGLU chunk, and every last-arriver counter (LM head, attention splits,
+ * split K) and the device error word zero.  Returns LD_OK, LD_EAUDIT with up
+ * to four mismatches in ld_last_error(), or LD_ESTATE before ld_alloc_kv.
+ * After LD_ETIMEOUT (which resets the counters) the audit starts over.
+ *
+ * Environment (read when a model is created): LD_MODE = wait | flags | mega
+ * | graph sets the starting mode, LD_WATCHDOG_US the watchdog in
+ * microseconds; another value makes ld_init_weights return LD_EINVAL. */
+enum { LD_DEBUG_POISON = 1 };
+ld_status ld_set_debug(ld_model* m, int32_t flags);
+ld_status ld_audit(ld_model* m);
+
 /* Stage timeline (profiling).  When dev_buf is not NULL every decode kernel
  * stores, for each workgroup w < 1024, the GPU's constant 100 MHz clock
  * (s_memrealtime) at stage entry (ev 0), after the readiness wait (ev 1),

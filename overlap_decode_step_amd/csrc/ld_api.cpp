@@ -7,6 +7,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -87,6 +88,10 @@ struct ld_model {
   uint32_t inject_next = 0;
   uint32_t* tune_ctr = nullptr;  // counter slots for standalone tuning launches
   size_t ctr_bytes = 0;          // bytes of all counters (stage, LM, split)
+  // debug mechanisms (ld_set_debug): flags, and the work-arena byte ranges
+  // a poisoned step fills with NaN (set by ld_alloc_kv)
+  int debug = 0;
+  std::vector<std::pair<size_t, size_t>> poison;
   std::string err;
 };
 
@@ -305,6 +310,22 @@ static ld_status setup_launch(ld_model* m) {
       khz > 0)
     m->wall_khz = (double)khz;
   m->watchdog_ticks = (uint64_t)(m->wall_khz * 1000.0 * 2.0);  // 2 s
+  // harness overrides from the environment: the starting mode, the watchdog
+  if (const char* e = std::getenv("LD_MODE")) {
+    const std::string v(e);
+    if (v == "wait") m->mode = LD_MODE_WAIT;
+    else if (v == "flags") m->mode = LD_MODE_FLAGS;
+    else if (v == "mega") m->mode = LD_MODE_MEGA;
+    else if (v == "graph") m->mode = LD_MODE_GRAPH;
+    else return fail(m, LD_EINVAL, "LD_MODE must be wait, flags, mega or graph");
+  }
+  if (const char* e = std::getenv("LD_WATCHDOG_US")) {
+    char* end = nullptr;
+    const double us = std::strtod(e, &end);
+    if (end == e || *end != '\0' || !(us > 0.0) || us > 3.6e9)
+      return fail(m, LD_EINVAL, "LD_WATCHDOG_US must be a number of microseconds in (0, 3.6e9]");
+    m->watchdog_ticks = (uint64_t)(m->wall_khz * 1e-3 * us);
+  }
   HIPCHK(m, scratch_lens_ptr(&m->scratch_lens, &m->scratch_cap));
   HIPCHK(m, hipStreamCreateWithFlags(&m->s1, hipStreamNonBlocking));
   HIPCHK(m, hipStreamCreateWithFlags(&m->s_cap, hipStreamNonBlocking));
@@ -523,6 +544,19 @@ extern "C" ld_status ld_alloc_kv(ld_model* m, void* dev_buf, size_t bytes, int32
     m->split_len_full += 32;
   m->D.max_splits = KL.max_splits;
 
+  // poisoned steps: the activations, partial results and fragment buffers
+  // (xa .. the RoPE table, contiguous), except a fragment buffer whose K is
+  // not a multiple of 32: its padding columns must stay zero (the MFMA engine
+  // multiplies them by masked, zero, weights)
+  {
+    m->poison.clear();
+    const bool keep[4] = {m->D.H % 32 == 0, m->D.H % 32 == 0, m->D.qd % 32 == 0, m->D.I % 32 == 0};
+    const size_t fb[5] = {KL.xa_f, KL.xb_f, KL.ao_f, KL.h_f, KL.ss_a};
+    m->poison.push_back({KL.xa, KL.xa_f - KL.xa});
+    for (int i = 0; i < 4; ++i)
+      if (keep[i]) m->poison.push_back({fb[i], fb[i + 1] - fb[i]});
+    m->poison.push_back({KL.ss_a, KL.rope - KL.ss_a});
+  }
   // zero everything except the caches, then counters and error word
   HIPCHK(m, hipMemset(base + KL.xa, 0, KL.total - KL.xa));
   // RoPE table: angle p * theta^(-2i/d) in double, cos and sin rounded to fp32
@@ -650,6 +684,22 @@ static ld_status enqueue_step(ld_model* m, const int32_t* tokens, int32_t B, int
   P.S.B = B;
   P.S.M = M;
   m->last_rows = B;
+  if (m->debug & LD_DEBUG_POISON) {
+    PoisonRanges r{};
+    char* base = static_cast<char*>(m->karena);
+    for (const auto& pr : m->poison) {
+      r.p[r.count] = reinterpret_cast<uint32_t*>(base + pr.first);
+      r.n[r.count++] = (int64_t)(pr.second / 4);
+    }
+    r.p[r.count] = reinterpret_cast<uint32_t*>(logits);
+    r.n[r.count++] = (int64_t)B * m->D.V;
+    if (next) {
+      r.p[r.count] = reinterpret_cast<uint32_t*>(next);
+      r.n[r.count++] = B;
+    }
+    HIPCHK(m, launch_poison(r, m->K.kc, m->K.vc, pos, B, M, m->D.L, m->D.max_batch, m->D.nkv,
+                            m->D.max_seq, m->D.d, s0));
+  }
   // split length: from 16 rows the modes with a full CU's LDS take longer
   // splits (fewer items and partial results); below 16 rows every mode uses
   // the same splits, so they add the same numbers in the same order
@@ -1155,6 +1205,67 @@ extern "C" ld_status ld_set_watchdog(ld_model* m, double seconds) {
   m->watchdog_ticks = (uint64_t)(m->wall_khz * 1000.0 * seconds);
   m->K.watchdog = m->watchdog_ticks;
   return LD_OK;
+}
+
+extern "C" ld_status ld_set_debug(ld_model* m, int32_t flags) {
+  if (!m) return fail(nullptr, LD_EINVAL, "null model");
+  if (flags & ~LD_DEBUG_POISON) return fail(m, LD_EINVAL, "unknown debug flag");
+  m->debug = flags;
+  return LD_OK;
+}
+
+extern "C" ld_status ld_audit(ld_model* m) {
+  if (!m) return fail(nullptr, LD_EINVAL, "null model");
+  if (!m->kv_ready) return fail(m, LD_ESTATE, "ld_alloc_kv first");
+  HIPCHK(m, hipDeviceSynchronize());
+  std::vector<uint32_t> c(m->ctr_bytes / 4);
+  HIPCHK(m, hipMemcpy(c.data(), m->K.ctr, m->ctr_bytes, hipMemcpyDeviceToHost));
+  int err = 0;
+  HIPCHK(m, hipMemcpy(&err, m->K.err, sizeof(int), hipMemcpyDeviceToHost));
+  const Dims& D = m->D;
+  auto at = [&](const uint32_t* p) { return (size_t)(p - m->K.ctr); };
+  auto leaves = [&](size_t o) {
+    uint32_t t = 0;  // (the waits add the leaves modulo 2^32 too)
+    for (int lf = 0; lf < kLeaves; ++lf) t += c[o + (size_t)lf * kLeafStride];
+    return t;
+  };
+  std::string bad;
+  int nbad = 0;
+  auto check = [&](const char* what, int l, int i, uint32_t got, uint32_t want) {
+    if (got == want) return;
+    if (nbad++ < 4) {
+      char buf[128];
+      snprintf(buf, sizeof buf, "%s%s[layer %d][%d] = %u, expected %u", bad.empty() ? "" : "; ",
+               what, l, i, got, want);
+      bad += buf;
+    }
+  };
+  // whole-stage counters: every step that signals adds the host's totals
+  const uint32_t tot[kStageCtrs] = {m->tot_qkv, m->tot_attn, m->tot_o, m->tot_gu, m->tot_d};
+  static const char* names[kStageCtrs] = {"qkv", "attention", "o", "swiglu", "down"};
+  for (int l = 0; l < D.L; ++l)
+    for (int st = 0; st < kStageCtrs; ++st) {
+      const size_t o = ((size_t)l * kStageCtrs + st) * kCtrWords;
+      check(names[st], l, 0, leaves(o), tot[st]);
+      check(names[st], l, 1, c[o + (size_t)kLeaves * kLeafStride], 0u);
+    }
+  // row-count counters: each tile-granular step adds every row once
+  for (int l = 0; l < D.L; ++l) {
+    for (int g = 0; g < D.nkv; ++g)
+      check("qkv rows of kv group", l, g,
+            leaves(at(m->K.qg_ctr) + ((size_t)l * D.nkv + g) * kCtrWords),
+            m->n_tile * (uint32_t)((D.group + 2) * D.d));
+    for (int ch = 0; ch < D.nhc; ++ch)
+      check("swiglu rows of chunk", l, ch,
+            leaves(at(m->K.hc_ctr) + ((size_t)l * D.nhc + ch) * kCtrWords),
+            m->n_tile * (uint32_t)std::min(kHChunk, D.I - ch * kHChunk));
+  }
+  // last-arriver counters (LM head, attention splits, split K) return to zero
+  for (size_t o = at(m->K.lm_ctr); o < at(m->K.qg_ctr); ++o)
+    if (c[o] != 0) check("last-arriver counter word", -1, (int)(o - at(m->K.lm_ctr)), c[o], 0u);
+  if (err != 0) check("device error word", -1, 0, (uint32_t)err, 0u);
+  if (nbad == 0) return LD_OK;
+  return fail(m, LD_EAUDIT, std::to_string(nbad) + " counter mismatches: " + bad);
 }
 
 extern "C" ld_status ld_debug_inject_stall(ld_model* m) {

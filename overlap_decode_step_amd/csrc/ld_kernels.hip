@@ -147,6 +147,35 @@ __global__ void k_fill16(uint16_t* dst, int64_t n, uint16_t v) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) dst[i] = v;
 }
 
+// Debug poison: blockIdx.y < r.count fills range blockIdx.y with fp32 quiet
+// NaNs; blockIdx.y == r.count fills the appended cache rows with bf16 quiet
+// NaNs (a position outside [0, max_seq) is skipped: the step reports it).
+__global__ void k_poison(PoisonRanges r, uint16_t* kc, uint16_t* vc, const int32_t* pos, int rows,
+                         int M, int L, int max_batch, int nkv, int max_seq, int d) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if ((int)blockIdx.y < r.count) {
+    uint32_t* p = r.p[blockIdx.y];
+    for (int64_t i = i0; i < r.n[blockIdx.y]; i += stride) p[i] = 0x7FC00000u;
+    return;
+  }
+  // (row, layer, kv head, channel)
+  const int64_t n = (int64_t)rows * L * nkv * d;
+  for (int64_t e = i0; e < n; e += stride) {
+    const int c = (int)(e % d);
+    int64_t q = e / d;
+    const int h = (int)(q % nkv);
+    q /= nkv;
+    const int l = (int)(q % L);
+    const int b = (int)(q / L);
+    const int p = pos[b];
+    if ((unsigned)p >= (unsigned)max_seq) continue;
+    const int64_t off = ((((int64_t)l * max_batch + b / M) * nkv + h) * max_seq + p) * d + c;
+    kc[off] = 0x7FC0u;
+    vc[off] = 0x7FC0u;
+  }
+}
+
 // KV prefill of one layer: blockIdx.y = seq * n_kv + head; positions < len[seq].
 __global__ void k_gen_kv(uint16_t* kc, uint16_t* vc, const int* len, int n_kv, int max_seq,
                          int d, uint64_t kkey, uint64_t vkey, float kappa) {
@@ -320,6 +349,14 @@ hipError_t launch_gen_normal(uint16_t* dst, int64_t n, uint64_t key, uint64_t in
   const int64_t blocks = (n + 255) / 256;
   const int grid = (int)(blocks < 65536 ? blocks : 65536);
   hipLaunchKernelGGL(k_gen_normal, dim3(grid), dim3(256), 0, s, dst, n, key, index0, kappa);
+  return hipGetLastError();
+}
+
+hipError_t launch_poison(const PoisonRanges& r, uint16_t* kc, uint16_t* vc, const int32_t* pos,
+                         int rows, int M, int L, int max_batch, int nkv, int max_seq, int d,
+                         hipStream_t s) {
+  hipLaunchKernelGGL(k_poison, dim3(256, r.count + 1), dim3(256), 0, s, r, kc, vc, pos, rows, M, L,
+                     max_batch, nkv, max_seq, d);
   return hipGetLastError();
 }
 

@@ -26,6 +26,19 @@ size_t scratch_bytes();
 size_t attn_smem(int group, int d, int T, int max_splits);
 size_t best_bytes();
 
+// Debug poison (see ld_set_debug): quiet NaNs into n ranges of 32-bit words
+// and into the KV-cache rows the step appends (row b of the step, of
+// sequence b / M, at position pos[b], in every layer and kv head).
+constexpr int kPoisonRanges = 24;
+struct PoisonRanges {
+  uint32_t* p[kPoisonRanges];
+  int64_t n[kPoisonRanges];
+  int count;
+};
+hipError_t launch_poison(const PoisonRanges& r, uint16_t* kc, uint16_t* vc, const int32_t* pos,
+                         int rows, int M, int L, int max_batch, int nkv, int max_seq, int d,
+                         hipStream_t s);
+
 hipError_t launch_gen_normal(uint16_t* dst, int64_t n, uint64_t key, uint64_t index0, float kappa,
                              hipStream_t s);
 hipError_t launch_fill16(uint16_t* dst, int64_t n, uint16_t v, hipStream_t s);

@@ -12,7 +12,9 @@ import weakref
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libld.so")
 
-LD_OK, LD_EINVAL, LD_ENOMEM, LD_EHIP, LD_ETIMEOUT, LD_ESTATE, LD_EDEVICE = 0, -1, -2, -3, -4, -5, -6
+LD_OK, LD_EINVAL, LD_ENOMEM, LD_EHIP, LD_ETIMEOUT, LD_ESTATE, LD_EDEVICE, LD_EAUDIT = (
+    0, -1, -2, -3, -4, -5, -6, -7)
+LD_DEBUG_POISON = 1
 LD_MODE_WAIT, LD_MODE_FLAGS, LD_MODE_MEGA, LD_MODE_GRAPH = 0, 1, 2, 3
 MODES = {"wait": LD_MODE_WAIT, "flags": LD_MODE_FLAGS, "mega": LD_MODE_MEGA, "graph": LD_MODE_GRAPH}
 LD_SWIGLU_COL, LD_SWIGLU_ROW = 0, 1
@@ -72,6 +74,8 @@ def _load():
         "ld_set_watchdog": (S, [P, D]),
         "ld_set_sync": (S, [P, I32]),
         "ld_debug_inject_stall": (S, [P]),
+        "ld_set_debug": (S, [P, I32]),
+        "ld_audit": (S, [P]),
         "ld_launch_info": (S, [P, P, I32]),
         "ld_read_activation": (S, [P, I32, I32, P]),
         "ld_trace_bytes": (ctypes.c_size_t, [CP]),
@@ -207,6 +211,15 @@ def ld_debug_inject_stall(m):
     return _check(LIB.ld_debug_inject_stall(m), m)
 
 
+def ld_set_debug(m, flags):
+    return _check(LIB.ld_set_debug(m, flags), m)
+
+
+def ld_audit(m):
+    """LD_OK or LD_EAUDIT (the mismatches in ld_last_error); does not raise."""
+    return int(LIB.ld_audit(m))
+
+
 def ld_trace_bytes(shape):
     return int(LIB.ld_trace_bytes(ctypes.byref(_cfg(shape))))
 
@@ -284,6 +297,12 @@ class Model:
 
     def set_mlp_variant(self, variant):
         ld_set_mlp_variant(self.h, variant)
+
+    def set_debug(self, flags):
+        ld_set_debug(self.h, flags)
+
+    def audit(self):
+        return ld_audit(self.h)
 
     def step(self, tokens, positions, logits, next_tokens=None):
         """tokens/positions: cuda int32 [B]; logits: cuda float32 [B, vocab]."""
