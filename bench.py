@@ -365,7 +365,7 @@ def main():
                          "times ld_decode_step_tokens in every mode instead of the decode step")
     ap.add_argument("--mlp-ablation", action="store_true",
                     help="also time the whole-kernel-wait step with the fused SwiGLU stage "
-                         "against its two- and four-kernel unfused forms (batch < 16)")
+                         "against its two- and four-kernel unfused forms")
     ap.add_argument("--sync", default="auto", choices=["auto", "tile", "stage"],
                     help="readiness granularity of the tile-flag and persistent modes")
     ap.add_argument("--prefill", type=int, default=None,

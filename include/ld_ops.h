@@ -58,11 +58,12 @@ int32_t ld_get_swiglu_variant(const ld_model* m, int32_t batch);
  * out).  LD_MLP_FUSED (the default) runs the fused SwiGLU stage;
  * LD_MLP_TWO_KERNELS one GEMV writing the gate and up projections, then a
  * silu-product kernel; LD_MLP_FOUR_KERNELS the gate GEMV, the up GEMV, silu
- * in place and the product.  All three give bitwise-equal results.  The
+ * in place and the product.  All three give bitwise-equal results, on both
+ * engines (below 16 rows the VALU engine, from 16 the MFMA engine, whose
+ * projections are the fused stage's tiles with a different epilogue and
+ * whose product kernel writes the Down stage's split-bf16 fragments).  The
  * unfused forms apply to the whole-kernel-wait mode only (the other modes
- * always run the fused stage) and to batches below 16 (the VALU engine): a
- * step outside that returns LD_EINVAL.  Returns LD_EINVAL for an unknown
- * variant. */
+ * always run the fused stage).  Returns LD_EINVAL for an unknown variant. */
 enum { LD_MLP_FUSED = 0, LD_MLP_TWO_KERNELS = 1, LD_MLP_FOUR_KERNELS = 2 };
 ld_status ld_set_mlp_variant(ld_model* m, int32_t variant);
 

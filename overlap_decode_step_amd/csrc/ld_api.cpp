@@ -467,7 +467,8 @@ static ld_status compute_grids(ld_model* m) {
       HIPCHK(m, set_max_dynamic_smem(st, nb, sm));
       if (st > 0 && nb == 64) HIPCHK(m, set_max_dynamic_smem(st, nb, m->smem_wait, true));
     }
-    if (nb < kMfmaMinBatch) HIPCHK(m, set_max_dynamic_smem(kSMlpProj, nb, m->smem_wait));
+    HIPCHK(m, set_max_dynamic_smem(kSMlpProj, nb, m->smem_wait));
+    if (nb == 64) HIPCHK(m, set_max_dynamic_smem(kSMlpProj, nb, m->smem_wait, true));
     int occ = 0;
     HIPCHK(m, occupancy(0, nb, m->thr_mega, m->smem_mega, &occ));
     if (occ < 1) return fail(m, LD_EINVAL, "persistent kernel does not fit on a CU");
@@ -801,8 +802,6 @@ static ld_status enqueue_step(ld_model* m, const int32_t* tokens, int32_t B, int
   };
   // the first MLP stage: fused, or an unfused form of the ablation
   const int mlp = flags ? LD_MLP_FUSED : m->mlp_variant;
-  if (mlp != LD_MLP_FUSED && B >= kMfmaMinBatch)
-    return fail(m, LD_EINVAL, "the unfused-MLP forms run on the VALU engine only (batch < 16)");
   auto launch_mlp = [&](int l) -> hipError_t {
     if (mlp == LD_MLP_FUSED) return launch(kSGu, l);
     hipError_t e;

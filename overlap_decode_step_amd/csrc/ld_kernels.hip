@@ -73,11 +73,11 @@ __global__ __launch_bounds__(kMaxThreads, WPS) void k_lm(Params P, int l) {
 }
 
 // unfused-MLP ablation: the projection GEMVs and the elementwise kernels
-template <int NB>
-__global__ __launch_bounds__(kMaxThreads, kStageWavesPerSimd) void k_mlp_proj(Params P, int l,
-                                                                             int which) {
+// (the same builds per batch size as the fused stage's kernel they replace)
+template <int NB, int WPS = kStageWavesPerSimd>
+__global__ __launch_bounds__(kMaxThreads, WPS) void k_mlp_proj(Params P, int l, int which) {
   extern __shared__ __align__(16) char smem[];
-  stage_mlp_proj<NB>(P, l, which, blockIdx.x, gridDim.x, smem);
+  stage_mlp_proj<NB, kStageRing<WPS>>(P, l, which, blockIdx.x, gridDim.x, smem);
 }
 
 __global__ void k_mlp_elem(Params P, int op, int64_t n) {
@@ -256,15 +256,13 @@ static const void* stage_fn(int stage) {
     case kSGu: return reinterpret_cast<const void*>(&k_gu<NB, WPS>);
     case kSD: return reinterpret_cast<const void*>(&k_d<NB, WPS>);
     case kSLm: return reinterpret_cast<const void*>(&k_lm<NB, WPS>);
-    case kSMlpProj:  // VALU engine only
-      if constexpr (NB < kMfmaMinBatch) return reinterpret_cast<const void*>(&k_mlp_proj<NB>);
-      return nullptr;
+    case kSMlpProj: return reinterpret_cast<const void*>(&k_mlp_proj<NB, WPS>);
     default: return nullptr;
   }
 }
 
 static const void* kernel_ptr(int stage, int nb, bool full = false) {
-  if (full && nb == kFullNb && stage != kSMlpProj) return stage_fn<kFullNb, kStageWavesFull>(stage);
+  if (full && nb == kFullNb) return stage_fn<kFullNb, kStageWavesFull>(stage);
   switch (nb) {
     case 1: return stage_fn<1>(stage);
     case 2: return stage_fn<2>(stage);
@@ -308,7 +306,7 @@ hipError_t launch_mega(const Params& P, int grid, int threads, size_t smem, hipS
 
 hipError_t launch_mlp_proj(int which, const Params& P, int l, int grid, int threads, size_t smem,
                            hipStream_t s) {
-  const void* fn = kernel_ptr(kSMlpProj, nb_for_batch(P.S.B));
+  const void* fn = kernel_ptr(kSMlpProj, nb_for_batch(P.S.B), P.S.wait != 0);
   if (!fn) return hipErrorInvalidValue;
   Params p = P;
   void* args[] = {&p, &l, &which};

@@ -963,7 +963,7 @@ __device__ __forceinline__ void stage_gu(const Params& P, int l, int wg, int nwg
   trace_ev(P, l, kSGu, 3, wg);
 }
 
-// ------------------------------------------ unfused-MLP ablation (VALU)
+// ------------------------------------------------- unfused-MLP ablation
 //
 // The fused SwiGLU stage measured against two unfused forms of the same
 // first MLP stage (the fused form, Deep Kernel Fusion for Transformers, "Key
@@ -978,7 +978,7 @@ __device__ __forceinline__ void stage_gu(const Params& P, int l, int wg, int nwg
 // results.  Whole-kernel-wait launches only: they wait on nothing and signal
 // nothing.  (The kMlp* codes are in ld_params.hpp.)
 
-template <int NB>
+template <int NB, int MR = kMfmaRingSmall>
 __device__ __forceinline__ void stage_mlp_proj(const Params& P, int l, int which, int wg, int nwg,
                                                char* smem) {
   const Dims& D = P.D;
@@ -990,6 +990,48 @@ __device__ __forceinline__ void stage_mlp_proj(const Params& P, int l, int which
   const uint16_t* gain = layer_w(P, l, P.W.o_mlp_norm);
   const int bw = batch_tile(P, K, NB);
   auto nowait = [] {};
+  if constexpr (NB >= kMfmaMinBatch) {
+    // MFMA engine: the fused stage's call (the O stage's fragments and sums
+    // of squares, the same tiling and K order), with an epilogue that stores
+    // the scaled projections instead of the activation
+    (void)lane, (void)src, (void)gain, (void)bw, (void)nowait;
+    Scratch& sc = *reinterpret_cast<Scratch*>(smem);
+    XSrc fs{nullptr, K, nullptr, nullptr, 0};
+    fs.frag = P.K.xb_f;
+    fs.kp = D.Hp;
+    fs.ss = P.K.ss_b;
+    fs.ss_n = fs.ss_ld = D.Ht;
+    const bool row_major = P.S.gu_variant == kGuRow;
+    auto none = [](int = 0, int = 0) {};
+    if (which == kMlpBoth) {
+      const GuRows rows = gu_rows(P, l);
+      auto epe = [&](int tile, int r, int b, int bl, int, const float* v) -> float {
+        const int row = tile * 16 + r;
+        if (row < I) {
+          st_coh(P.K.gbuf + (int64_t)b * I + row, v[0] * sc.rs[bl]);
+          st_coh(P.K.ubuf + (int64_t)b * I + row, v[1] * sc.rs[bl]);
+        }
+        return 0.f;
+      };
+      mfma_stage_frag<kMfmaNbt<NB, MR>, 2, MR>(
+          MatRows{base, {rows.Wg, rows.Wu}, I, K}, (I + 15) / 16, K, base, bytes, fs, true, D.eps,
+          B, P.S.x_cap, none, epe, [](int, int) {}, wg, nwg, smem, SplitK{nullptr, nullptr, 1},
+          row_major);
+    } else {
+      const uint16_t* Wm = which == kMlpGate ? layer_w(P, l, P.W.o_wg) : layer_w(P, l, P.W.o_wu);
+      float* out = which == kMlpGate ? P.K.gbuf : P.K.ubuf;
+      auto epe = [&](int tile, int r, int b, int bl, int, const float* v) -> float {
+        const int row = tile * 16 + r;
+        if (row < I) st_coh(out + (int64_t)b * I + row, v[0] * sc.rs[bl]);
+        return 0.f;
+      };
+      mfma_stage_frag<kMfmaNbt<NB, MR>, 1, MR>(
+          MatRows{base, {Wm, Wm}, I, K}, (I + 15) / 16, K, base, bytes, fs, true, D.eps, B,
+          P.S.x_cap, none, epe, [](int, int) {}, wg, nwg, smem, SplitK{nullptr, nullptr, 1},
+          row_major);
+    }
+    return;
+  }
   if (which == kMlpBoth) {
     constexpr int NP = kPairsGu, NR = 2 * kPairsGu;
     const GuRows rows = gu_rows(P, l);
@@ -1034,7 +1076,9 @@ __device__ __forceinline__ void stage_mlp_proj(const Params& P, int l, int which
 }
 
 // The elementwise kernels of the unfused forms over [B][I]: silu(g) in place
-// (kMlpSilu), h = g * u (kMlpMul), or h = silu(g) * u (kMlpSiluMul).
+// (kMlpSilu), h = g * u (kMlpMul), or h = silu(g) * u (kMlpSiluMul).  From 16
+// rows h goes where the Down stage's MFMA engine reads it, as the fused
+// stage writes it: split-bf16 pairs in B-fragment order.
 __device__ __forceinline__ void mlp_elementwise(const Params& P, int op, int64_t i) {
   float* g = P.K.gbuf;
   const float a = ld_coh(g + i);
@@ -1043,7 +1087,12 @@ __device__ __forceinline__ void mlp_elementwise(const Params& P, int op, int64_t
   } else {
     const float u = ld_coh(P.K.ubuf + i);
     const float s = op == kMlpSiluMul ? a / (1.0f + expf(-a)) : a;
-    st_coh(P.K.hbuf + i, s * u);
+    if (P.S.B >= kMfmaMinBatch) {
+      const int b = (int)(i / P.D.I), row = (int)(i - (int64_t)b * P.D.I);
+      st_coh_u(P.K.h_f + frag_word(b, row, P.D.Ip), split_pair(s * u));
+    } else {
+      st_coh(P.K.hbuf + i, s * u);
+    }
   }
 }
 

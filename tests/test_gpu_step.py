@@ -527,21 +527,27 @@ def test_multi_token_positions_must_be_consecutive(ld):
 
 # --------------------------------------------- unfused-MLP ablation
 
-@pytest.mark.parametrize("name,B", [("tiny", 1), ("tiny", 3), ("llama1b", 1)])
+ABLATION_CASES = [("tiny", 1), ("tiny", 3), ("tiny", 16), ("tiny", 45), ("llama1b", 1),
+                  ("llama1b", 16), ("llama1b", 64)]
+
+
+@pytest.mark.parametrize("name,B", ABLATION_CASES, ids=[f"{n}-B{b}" for n, b in ABLATION_CASES])
 def test_mlp_ablation_bitwise(ld, name, B):
     # The fused SwiGLU stage and its two- and four-kernel unfused forms add
-    # the same numbers in the same order: whole-kernel-wait steps agree bit
-    # for bit.  Other modes keep the fused stage whatever the setting, and
-    # the unfused forms refuse the MFMA engine's batch sizes.
+    # the same numbers in the same order, on the VALU engine (below 16 rows)
+    # and the MFMA engine (from 16): whole-kernel-wait steps agree bit for
+    # bit.  Other modes keep the fused stage whatever the setting.
     shape = W.SHAPES[name]
     steps = 3 if name == "tiny" else 1
     prefill = [128] * B if name == "tiny" else [512] * B
-    m = gpu_model(ld, shape, 16, 700, prefill + [128] * (16 - B))
-    run = GpuRunner(m, shape["vocab"], 16)
+    maxb = max(16, B)
+    m = gpu_model(ld, shape, maxb, 700, prefill + [128] * (maxb - B))
+    run = GpuRunner(m, shape["vocab"], maxb)
     toks = W.first_tokens(B, shape["vocab"])
     outs = {}
-    for mode, variant in (("wait", "fused"), ("wait", "two"), ("wait", "four"), ("mega", "four")):
-        m.fill_kv(W.SEED_KV, 1.0, prefill + [128] * (16 - B))
+    for mode, variant in (("wait", "fused"), ("wait", "two"), ("wait", "four"), ("mega", "fused"),
+                          ("mega", "four")):
+        m.fill_kv(W.SEED_KV, 1.0, prefill + [128] * (maxb - B))
         m.set_mode(mode)
         m.set_mlp_variant(variant)
         t = list(toks)
@@ -551,14 +557,14 @@ def test_mlp_ablation_bitwise(ld, name, B):
             seq.append(lg)
             t = list(nx)
         outs[(mode, variant)] = seq
-    ref = outs[("wait", "fused")]
-    for key in (("wait", "two"), ("wait", "four"), ("mega", "four")):
-        for s, (a, b) in enumerate(zip(ref, outs[key])):
-            assert np.array_equal(a, b), f"{name} B={B} {key} step {s} differs from the fused stage"
-    m.set_mode("wait")
-    m.set_mlp_variant("two")
+    # (from 16 rows the persistent mode's splits and passes differ from the
+    # whole-kernel-wait mode's, so each mode is compared with its own fused run)
+    for key, ref in ((("wait", "two"), ("wait", "fused")), (("wait", "four"), ("wait", "fused")),
+                     (("mega", "four"), ("mega", "fused"))):
+        for s, (a, b) in enumerate(zip(outs[ref], outs[key])):
+            assert np.array_equal(a, b), f"{name} B={B} {key} step {s} differs from {ref}"
     with pytest.raises(ld.LdError) as ei:
-        run.step(W.first_tokens(16, shape["vocab"]), [128] * 16)
+        ld.ld_set_mlp_variant(m.h, 3)
     assert ei.value.status == ld.LD_EINVAL
     m.set_mlp_variant("fused")
     m.free()
