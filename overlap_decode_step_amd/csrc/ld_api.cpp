@@ -703,10 +703,12 @@ static ld_status enqueue_step(ld_model* m, const int32_t* tokens, int32_t B, int
   }
   // split length: from 16 rows the modes with a full CU's LDS take longer
   // splits (fewer items and partial results); below 16 rows every mode uses
-  // the same splits, so they add the same numbers in the same order
+  // the same splits, so they add the same numbers in the same order.  The
+  // long-context rule (on the device: far more items than workgroups) may
+  // lengthen them up to the mode's whole tile area at any batch size.
   if (m->mode != LD_MODE_FLAGS) P.D.split_len = m->split_len_full;
-  P.S.Tmax = B >= kMfmaMinBatch ? P.D.split_len : m->D.split_len;
-  P.S.T = step_split_len(P.S.Tmax, B);
+  P.S.T = step_split_len(B >= kMfmaMinBatch ? P.D.split_len : m->D.split_len, B);
+  P.S.Tmax = P.D.split_len;
   P.S.gu_variant = m->gu_variant[m->mode][B];
   P.S.inject = m->inject_next;
   m->inject_next = 0;

@@ -260,6 +260,10 @@ __device__ __forceinline__ void st_ao(const Params& P, int b, int c, float v) {
 }
 
 constexpr int kCombBatch = 16;  // splits combined from registers in one round of loads
+template <int N>
+struct CInt {
+  static constexpr int value = N;
+};
 
 // Row b of the step (token j = b % M of sequence slot = b / M, at position
 // p = p0 + j, where p0 is the sequence's first position of this step).
@@ -579,43 +583,63 @@ __device__ __forceinline__ void attn_item(const Params& P, int l, const AttnItem
     // channel, o = (sum_s o_s f_s) / L: per channel, the splits in ascending
     // order, kCombBatch splits' (m, l, o) loaded per round; from a second
     // round on (more than kCombBatch splits: a long context) the running L
-    // and O are rescaled by e^(M_old - M_new) when the maximum grows.
+    // and O are rescaled by e^(M_old - M_new) when the maximum grows.  With
+    // more output channels than threads (CPT = 2) a thread takes two
+    // adjacent channels of one head, which share the round's m and l loads;
+    // each channel's arithmetic is the same either way.
     const float* pbase = P.K.part + ((int64_t)b * D.nq + kvh * group) * D.max_splits * (d + 2);
-    for (int r = tid; r < gd; r += nth) {
-      const int g = r >> ld, i = r & (d - 1);
-      const float* q = pbase + (int64_t)g * D.max_splits * (d + 2);
-      float M = -INFINITY, L = 0.f, O = 0.f;
-      for (int s0 = 0; s0 < nsplit; s0 += kCombBatch) {
-        float mv[kCombBatch], lv[kCombBatch], ov[kCombBatch];
+    auto combine = [&](auto cpt) {
+      constexpr int CPT = decltype(cpt)::value;
+      for (int r = tid * CPT; r < gd; r += nth * CPT) {
+        const int g = r >> ld, i = r & (d - 1);
+        const float* q = pbase + (int64_t)g * D.max_splits * (d + 2);
+        float M = -INFINITY, L = 0.f, O[CPT];
 #pragma unroll
-        for (int u = 0; u < kCombBatch; ++u) {
-          if (s0 + u < nsplit) {
-            mv[u] = ld_coh(q + (s0 + u) * (d + 2));
-            lv[u] = ld_coh(q + (s0 + u) * (d + 2) + 1);
-            ov[u] = ld_coh(q + (s0 + u) * (d + 2) + 2 + i);
+        for (int c = 0; c < CPT; ++c) O[c] = 0.f;
+        for (int s0 = 0; s0 < nsplit; s0 += kCombBatch) {
+          float mv[kCombBatch], lv[kCombBatch], ov[kCombBatch][CPT];
+#pragma unroll
+          for (int u = 0; u < kCombBatch; ++u) {
+            if (s0 + u < nsplit) {
+              const float* rec = q + (s0 + u) * (d + 2);
+              mv[u] = ld_coh(rec);
+              lv[u] = ld_coh(rec + 1);
+#pragma unroll
+              for (int c = 0; c < CPT; ++c) ov[u][c] = ld_coh(rec + 2 + i + c);
+            }
+          }
+          float Mn = M;
+#pragma unroll
+          for (int u = 0; u < kCombBatch; ++u)
+            if (s0 + u < nsplit) Mn = fmaxf(Mn, mv[u]);
+          if (s0 > 0) {  // (first round: L = O = 0, nothing to rescale)
+            const float e = expf(M - Mn);
+            L *= e;
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) O[c] *= e;
+          }
+          M = Mn;
+#pragma unroll
+          for (int u = 0; u < kCombBatch; ++u) {
+            if (s0 + u < nsplit) {
+              const float f = expf(mv[u] - M);
+              L = fmaf(lv[u], f, L);
+#pragma unroll
+              for (int c = 0; c < CPT; ++c) O[c] = fmaf(ov[u][c], f, O[c]);
+            }
           }
         }
-        float Mn = M;
 #pragma unroll
-        for (int u = 0; u < kCombBatch; ++u)
-          if (s0 + u < nsplit) Mn = fmaxf(Mn, mv[u]);
-        if (s0 > 0) {  // (first round: L = O = 0, nothing to rescale)
-          const float c = expf(M - Mn);
-          L *= c;
-          O *= c;
-        }
-        M = Mn;
-#pragma unroll
-        for (int u = 0; u < kCombBatch; ++u) {
-          if (s0 + u < nsplit) {
-            const float f = expf(mv[u] - M);
-            L = fmaf(lv[u], f, L);
-            O = fmaf(ov[u], f, O);
-          }
-        }
+        for (int c = 0; c < CPT; ++c) st_ao(P, b, oc + r + c, O[c] / L);
       }
-      st_ao(P, b, oc + r, O / L);
-    }
+    };
+    // (two channels per thread only where the shape is known at compile
+    // time: the general form stays one channel per thread, which keeps the
+    // persistent kernel's register use where it was)
+    if constexpr (G > 0 && DH > 0)
+      combine(CInt<(G * DH > kBlockThreads) ? 2 : 1>{});
+    else
+      combine(CInt<1>{});
   }
   signal_if(P, stage_ctr(P, l, kCAttn), b * D.nkv + kvh);
 }
