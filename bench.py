@@ -342,6 +342,91 @@ def long_generation(batches=(1, 4, 16), prefills=(1024, 16384), modes=("wait", "
     return rows
 
 
+def stage_trace(shape_name, B, prefill, modes, reps=3):
+    """Per-stage timeline of one decode step (ld_set_trace): per layer, the time
+    from the end of one stage (its last workgroup) to the end of the next,
+    averaged over layers 1..L-1; the LM head; and the spread over workgroups
+    of the attention items' events and of the SwiGLU stage's end.  Printed as
+    text lines and returned as a dict."""
+    import numpy as np
+    import torch
+    from overlap_decode_step_amd import ld
+    from synth import workloads as W
+    shape = W.SHAPES[shape_name]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    m = ld.Model(shape, seed=W.SEED_WEIGHTS, w_std=0.01 if shape_name.startswith("llama70b") else 0.02)
+    m.alloc_kv(B, prefill + reps + 8)
+    m.fill_kv(W.SEED_KV, 1.0, [prefill] * B)
+    L = shape["n_layers"]
+    nbytes = ld.ld_trace_bytes(shape)
+    tr = torch.zeros(nbytes // 8, dtype=torch.int64, device=dev)
+    lg = torch.empty((B, shape["vocab"]), dtype=torch.float32, device=dev)
+    nx = torch.empty(B, dtype=torch.int32, device=dev)
+    toks = torch.tensor(W.first_tokens(B, shape["vocab"]), dtype=torch.int32, device=dev)
+    names = ["qkv", "attention", "o", "swiglu", "down"]
+    out = {}
+    for mode in modes:
+        m.set_mode(mode)
+        acc = []
+        for rep in range(reps):
+            pos = torch.full((B,), prefill + rep, dtype=torch.int32, device=dev)
+            for _ in range(3):
+                m.step(toks, pos, lg, nx)
+            torch.cuda.synchronize()
+            tr.zero_()
+            ld.ld_set_trace(m.h, tr.data_ptr(), nbytes)
+            m.step(toks, pos, lg, nx)
+            torch.cuda.synchronize()
+            ld.ld_set_trace(m.h, None, 0)
+            if m.device_error() != 0:
+                raise RuntimeError(f"device error in the traced step ({mode})")
+            t = tr.cpu().numpy().reshape(L + 1, 8, 4, 1024).astype(np.float64)
+            t0 = t[t > 0].min()
+            t = np.where(t > 0, (t - t0) / 100.0, np.nan)  # microseconds (100 MHz clock)
+            per = {k: [] for k in names}
+            items = []
+            gu_end = []
+            for l in range(1, L):
+                prev = np.nanmax(t[l - 1, 5, 3])
+                for s_, k in enumerate(names, start=1):
+                    end = np.nanmax(t[l, s_, 3])
+                    per[k].append(end - prev)
+                    prev = end
+                qkv_end = np.nanmax(t[l, 1, 3])
+                ev = [t[l, 6, 0], t[l, 7, 0], t[l, 7, 1], t[l, 7, 2], t[l, 7, 3], t[l, 2, 3]]
+                items.append([np.nanmedian(e - qkv_end) if np.isfinite(e).any() else np.nan for e in ev]
+                             + [np.nanmax(t[l, 2, 3]) - qkv_end])
+                o_end = np.nanmax(t[l, 3, 3])
+                ge = t[l, 4, 3] - o_end
+                gu_end.append((np.nanmedian(ge), np.nanmax(ge)))
+            lm = np.nanmax(t[L, 6, 3]) - np.nanmax(t[L - 1, 5, 3])
+            acc.append((per, np.nanmean(items, axis=0), np.mean(gu_end, axis=0), lm))
+        row = {k: float(np.mean([np.mean(a[0][k]) for a in acc])) for k in names}
+        it = np.mean([a[1] for a in acc], axis=0)
+        ge = np.mean([a[2] for a in acc], axis=0)
+        lm = float(np.mean([a[3] for a in acc]))
+        row["layer"] = sum(row[k] for k in names)
+        row["lm_head"] = lm
+        row["attention_items_us_after_qkv_end"] = {
+            "item_start": float(it[0]), "tiles_ready": float(it[1]), "scores_done": float(it[2]),
+            "outputs_stored": float(it[3]), "split_counter": float(it[4]),
+            "stage_end_median": float(it[5]), "stage_end_last": float(it[6])}
+        row["swiglu_end_after_o_us"] = {"median": float(ge[0]), "last": float(ge[1])}
+        out[mode] = row
+        print(f"# stage-trace {shape_name} batch={B} mode={mode} per-layer us: "
+              + " ".join(f"{k}={row[k]:.2f}" for k in names)
+              + f" layer={row['layer']:.2f} lm_head={lm:.1f}", file=sys.stderr, flush=True)
+        print(f"#   attention (us after QKV's end, medians): item start {it[0]:.2f}, tiles "
+              f"{it[1]:.2f}, scores {it[2]:.2f}, outputs stored {it[3]:.2f}, split counter "
+              f"{it[4]:.2f}; stage end median {it[5]:.2f}, last {it[6]:.2f}", file=sys.stderr,
+              flush=True)
+        print(f"#   swiglu end after O's end: median {ge[0]:.2f} us, last {ge[1]:.2f} us",
+              file=sys.stderr, flush=True)
+    m.free()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -379,12 +464,22 @@ def main():
                     help="only run the offline SwiGLU tiling choice at this shape for the "
                          "comma-separated batch sizes of --tune-batches, in every mode")
     ap.add_argument("--tune-batches", default="1,2,16,64")
+    ap.add_argument("--stage-trace", action="store_true",
+                    help="only trace one step per stage (ld_set_trace) at --shape/--batch "
+                         "and print the per-layer breakdown, in each of --trace-modes")
+    ap.add_argument("--trace-modes", default="mega,wait,flags")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU only; --gpus must be 1", file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.stage_trace:
+        prefill = args.prefill or (512 if args.shape == "llama1b" else 1024)
+        rows = stage_trace(args.shape, args.batch, prefill, args.trace_modes.split(","))
+        print(json.dumps({"stage_trace": args.shape, "batch": args.batch, "prefill": prefill,
+                          "modes": rows}), flush=True)
         return
     if args.long_gen:
         rows = long_generation()

@@ -126,7 +126,11 @@ ld_status ld_audit(ld_model* m);
  * after the compute (ev 2) and at stage exit (ev 3), as uint64 at
  * dev_buf[((layer * 8 + stage) * 4 + ev) * 1024 + w]; stage ids 1..5 are
  * QKV, attention, O, SwiGLU, Down and the LM head is stage 6 of layer
- * n_layers.  NULL turns it off.  bytes >= ld_trace_bytes(cfg). */
+ * n_layers.  Slots 6 and 7 of a layer hold the attention items' own events,
+ * for each workgroup's last item: (6, 0) item start, (7, 0) its K/V tiles and
+ * new rows in LDS, (7, 1) scores and softmax done, (7, 2) outputs stored,
+ * (7, 3) split counter returned (several splits only).  NULL turns it off.
+ * bytes >= ld_trace_bytes(cfg). */
 size_t ld_trace_bytes(const ld_config* cfg);
 ld_status ld_set_trace(ld_model* m, void* dev_buf, size_t bytes);
 
