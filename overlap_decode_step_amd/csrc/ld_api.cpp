@@ -203,7 +203,7 @@ extern "C" size_t ld_weights_bytes(const ld_config* cfg) {
 // KV + workspace arena layout (byte offsets).
 struct KLayout {
   size_t kc, vc, xa, xb, qkv, ao, part, hbuf, gbuf, ubuf, lm_val, lm_idx, rope, ctr, lm_ctr,
-      split_ctr, mctr, qg_ctr, hc_ctr, mpart, xa_f, xb_f, ao_f, h_f, ss_a, ss_b, err, tune_ctr, total;
+      split_ctr, mctr, aph, qg_ctr, hc_ctr, mpart, xa_f, xb_f, ao_f, h_f, ss_a, ss_b, err, tune_ctr, total;
   int split_len, max_splits, max_wg;
 };
 
@@ -287,6 +287,7 @@ static KLayout klayout(const ld_config* c, int maxB, int max_seq) {
   K.lm_ctr = take((size_t)kCtrWords * 4);
   K.split_ctr = take((size_t)c->n_layers * maxB * c->n_kv_heads * 16 * 4);
   K.mctr = take((size_t)2 * kMctrPasses * ((H + 15) / 16) * 4);
+  K.aph = take((size_t)c->n_layers * 2 * kCtrWords * 4);
   K.qg_ctr = take((size_t)c->n_layers * c->n_kv_heads * kCtrWords * 4);
   K.hc_ctr = take((size_t)c->n_layers * ((I + kHChunk - 1) / kHChunk) * kCtrWords * 4);
   K.err = take(256);
@@ -523,6 +524,7 @@ extern "C" ld_status ld_alloc_kv(ld_model* m, void* dev_buf, size_t bytes, int32
   K.lm_ctr = reinterpret_cast<uint32_t*>(base + KL.lm_ctr);
   K.split_ctr = reinterpret_cast<uint32_t*>(base + KL.split_ctr);
   K.mctr = reinterpret_cast<uint32_t*>(base + KL.mctr);
+  K.aph = reinterpret_cast<uint32_t*>(base + KL.aph);
   K.qg_ctr = reinterpret_cast<uint32_t*>(base + KL.qg_ctr);
   K.hc_ctr = reinterpret_cast<uint32_t*>(base + KL.hc_ctr);
   K.mpart = reinterpret_cast<float*>(base + KL.mpart);

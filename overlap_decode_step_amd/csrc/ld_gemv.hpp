@@ -73,6 +73,8 @@ struct Scratch {
   int pos[64];    // positions of the step (valid once pos_ok is set)
   int pos_ok;
   int attn_T;     // the attention stage's split length (set with pos)
+  int attn_items; // its items, and whether the step combines its splits in a
+  int attn_phase; // phase of its own (set with pos)
   int flag[4];
   int cnt[kMaxTileCtrs];  // rows this workgroup wrote per row-count counter
 };

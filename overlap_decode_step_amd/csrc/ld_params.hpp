@@ -110,6 +110,7 @@ struct Work {
   uint32_t* lm_ctr;     // LM-head last-arriver counter
   uint32_t* split_ctr;  // attention last-arriver counters [L][maxB][nkv][16]
   uint32_t* mctr;       // split-K last-arriver counters: O, then Down, [kMctrPasses][tiles]
+  uint32_t* aph;        // long-context combine phase: per layer, items done, then workgroups past [L][2][counter words]
   uint32_t* qg_ctr;     // QKV rows written per (layer, kv group) [L][nkv][counter words]
   uint32_t* hc_ctr;     // SwiGLU rows written per (layer, chunk) [L][nhc][counter words]
   float* mpart;         // split-K partial tiles [kMaxKSplit][maxB][H]

@@ -50,6 +50,12 @@ __device__ __forceinline__ uint32_t* split_ctr(const Params& P, int l, int b, in
   return P.K.split_ctr + (((int64_t)l * P.D.max_batch + b) * P.D.nkv + kvh) * 16;
 }
 
+// The long-context combine phase's counters of layer l: 0 = attention items
+// done, 1 = workgroups past the wait for them.
+__device__ __forceinline__ uint32_t* aph_ctr(const Params& P, int l, int which) {
+  return P.K.aph + ((int64_t)l * 2 + which) * kCtrWords;
+}
+
 __device__ __forceinline__ SyncArgs sync_of(const Params& P) {
   return SyncArgs{P.K.err, P.K.watchdog};
 }
@@ -565,6 +571,13 @@ __device__ __forceinline__ void attn_item(const Params& P, int l, const AttnItem
     }
   }
   trace_ev(P, l, 7, 2, blockIdx.x);
+  // a step with a long context combines its splits in a phase of its own
+  // (stage_attn): the item only counts itself as done
+  const bool phase = __builtin_amdgcn_readfirstlane(sc.attn_phase) != 0;
+  if (nsplit > 1 && phase) {
+    wg_signal(aph_ctr(P, l, 0), blockIdx.x);
+    return;
+  }
   if (nsplit > 1) {
     // last-arriving split combines all splits in fixed order
     wave_drain();
@@ -642,6 +655,62 @@ __device__ __forceinline__ void attn_item(const Params& P, int l, const AttnItem
       combine(CInt<1>{});
   }
   signal_if(P, stage_ctr(P, l, kCAttn), b * D.nkv + kvh);
+  if (phase) wg_signal(aph_ctr(P, l, 0), blockIdx.x);  // (an unsplit row of a phase step)
+}
+
+// The split combine of one (row b, kv head) in the combine phase: the same
+// arithmetic as the last-arriving split's (per channel, the splits in
+// ascending order, kCombBatch per round of loads, rescaled from a second
+// round on), CPT adjacent channels of one head per thread.
+template <int CPT>
+__device__ __forceinline__ void attn_combine_unit(const Params& P, int b, int kvh, int nsplit) {
+  const Dims& D = P.D;
+  const int d = D.d, group = D.group, gd = group * d, ld = 31 - __builtin_clz(d);
+  const int tid = ld::tid(), nth = blockDim.x;
+  const float* pbase = P.K.part + ((int64_t)b * D.nq + kvh * group) * D.max_splits * (d + 2);
+  const int oc = kvh * gd;
+  for (int r = tid * CPT; r < gd; r += nth * CPT) {
+    const int g = r >> ld, i = r & (d - 1);
+    const float* q = pbase + (int64_t)g * D.max_splits * (d + 2);
+    float M = -INFINITY, L = 0.f, O[CPT];
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) O[c] = 0.f;
+    for (int s0 = 0; s0 < nsplit; s0 += kCombBatch) {
+      float mv[kCombBatch], lv[kCombBatch], ov[kCombBatch][CPT];
+#pragma unroll
+      for (int u = 0; u < kCombBatch; ++u) {
+        if (s0 + u < nsplit) {
+          const float* rec = q + (s0 + u) * (d + 2);
+          mv[u] = ld_coh(rec);
+          lv[u] = ld_coh(rec + 1);
+#pragma unroll
+          for (int c = 0; c < CPT; ++c) ov[u][c] = ld_coh(rec + 2 + i + c);
+        }
+      }
+      float Mn = M;
+#pragma unroll
+      for (int u = 0; u < kCombBatch; ++u)
+        if (s0 + u < nsplit) Mn = fmaxf(Mn, mv[u]);
+      if (s0 > 0) {
+        const float e = expf(M - Mn);
+        L *= e;
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) O[c] *= e;
+      }
+      M = Mn;
+#pragma unroll
+      for (int u = 0; u < kCombBatch; ++u) {
+        if (s0 + u < nsplit) {
+          const float f = expf(mv[u] - M);
+          L = fmaf(lv[u], f, L);
+#pragma unroll
+          for (int c = 0; c < CPT; ++c) O[c] = fmaf(ov[u][c], f, O[c]);
+        }
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) st_ao(P, b, oc + r + c, O[c] / L);
+  }
 }
 
 template <int G, int DH>
@@ -673,6 +742,20 @@ __device__ __forceinline__ void stage_attn(const Params& P, int l, int wg, int n
       int T = P.S.T;
       if (need > T) T = (int)min((int64_t)P.S.Tmax, (need + 31) / 32 * 32);
       sc.attn_T = T;
+      // the items (row b at position p_b has (p_b + T) / T splits), and the
+      // combine phase when some row has more splits than one round of the
+      // combine takes (a long context)
+      const int M = MULTI ? P.S.M : 1;
+      int items = 0, maxns = 0;
+      for (int b = 0; b < P.S.B; ++b) {
+        const int slot = b / M;
+        const int p = min(sc.pos[slot * M] + (b - slot * M), D.max_seq - 1);
+        const int ns = (p + T) / T;
+        items += D.nkv * ns;
+        maxns = max(maxns, ns);
+      }
+      sc.attn_items = items;
+      sc.attn_phase = maxns > kCombBatch;
       sc.pos_ok = 1;
     }
     __syncthreads();
@@ -726,6 +809,33 @@ __device__ __forceinline__ void stage_attn(const Params& P, int l, int wg, int n
       items(AttnShape<8, 128>{});
     else
       items(AttnShape<0, 0>{});
+  }
+  // combine phase (long context): once every item has stored its partial
+  // results, the (row, kv head) combines are dealt to the whole grid instead
+  // of running one after another in whichever workgroups arrived last
+  if (__builtin_amdgcn_readfirstlane(sc.attn_phase) != 0) {
+    const int n_items = __builtin_amdgcn_readfirstlane(sc.attn_items);
+    wg_wait(sync_of(P), aph_ctr(P, l, 0), (uint32_t)n_items, kSAttn);
+    // the last workgroup past the wait clears the item counter for the next
+    // layer (every other one has passed it)
+    if (tid() == 0) sc.flag[2] = last_arriver(aph_ctr(P, l, 1), wg, nwg);
+    __syncthreads();
+    if (sc.flag[2] && tid() < kLeaves)
+      __hip_atomic_store(aph_ctr(P, l, 0) + tid() * kLeafStride, 0u, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    const int M = MULTI ? P.S.M : 1;
+    for (int u = wg; u < P.S.B * D.nkv; u += nwg) {
+      const int b = u / D.nkv, kvh = u - b * D.nkv, slot = b / M;
+      const int p = min(sc.pos[slot * M] + (b - slot * M), D.max_seq - 1);
+      const int ns = (p + T) / T;
+      if (ns > 1) {
+        if (D.group * D.d > (int)blockDim.x)
+          attn_combine_unit<2>(P, b, kvh, ns);
+        else
+          attn_combine_unit<1>(P, b, kvh, ns);
+        signal_if(P, stage_ctr(P, l, kCAttn), u);
+      }
+    }
   }
   (void)D;
   trace_ev(P, l, kSAttn, 3, wg);

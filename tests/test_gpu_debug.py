@@ -41,14 +41,19 @@ def _model(ld, shape, B, max_seq, prefill, w_std=0.02):
 
 # batch sizes of both engines, ragged batch tiles, and the ragged shape
 POISON_CASES = [("tiny", 1), ("tiny", 5), ("tiny", 16), ("tiny", 45), ("ragged", 3),
-                ("llama1b", 1), ("llama1b", 16), ("llama1b", 64)]
+                ("llama1b", 1), ("llama1b", 16), ("llama1b", 64),
+                ("tiny-long", 1), ("tiny-long", 3), ("tiny-long", 16)]
 
 
 @pytest.mark.parametrize("name,B", POISON_CASES, ids=[f"{n}-B{b}" for n, b in POISON_CASES])
 def test_poison_changes_nothing_and_counters_audit(ld, name, B):
-    shape = SHAPES[name]
+    shape = SHAPES["tiny" if name == "tiny-long" else name]
     if name == "llama1b":
         maxs, prefill = 1040, W.kv_lengths(B, 256, 1024)
+    elif name == "tiny-long":
+        # 1900..2050 positions: more than 16 splits per head, so the step
+        # combines its splits in a phase of its own
+        maxs, prefill = 2100, W.kv_lengths(B, 1900, 2050)
     elif name == "ragged":
         maxs, prefill = 1200, [1100, 512, 1][:B]
     else:

@@ -21,7 +21,9 @@ capacity; the tile-flag (FLAGS) schedule is one launch per stage on two
 alternating streams, two workgroups per CU.  The decompositions mirror the
 device code: the VALU engine's round-robin deal of row tasks to waves, the
 MFMA engine's tiles per workgroup and K ranges (split K), and the attention
-items per (row, kv head, split) with the split length's long-context rule.
+items per (row, kv head, split) with the split length's long-context rule
+and, past 16 splits per head, the combine phase (every workgroup waits for
+all items, then the combines are dealt to the grid).
 """
 import random
 
@@ -184,6 +186,11 @@ def layer_programs(shape, l, B, pos, nwg, nwaves, Tmax, tile=False):
                 ops += [("signal", key, n) for key, n in sorted(counts.items())]
             else:
                 ops.append(("signal", ("ctr", l, st), 1))
+    # a long context (some row with more than 16 splits) combines its splits
+    # in a phase of its own: every item counts itself, every workgroup waits
+    # for all of them, then the (row, kv head) combines are dealt to the grid
+    ns_of = {b: ns for (b, _, _, ns, _, _) in items}
+    phase = max(ns_of.values()) > 16
     for wg in range(nwg):
         ops = progs["attn"][wg]
         for it in range(wg, len(items), nwg):
@@ -193,7 +200,18 @@ def layer_programs(shape, l, B, pos, nwg, nwaves, Tmax, tile=False):
             else:
                 ops.append(("wait", ("ctr", l, "qkv"), g))
             ops.append(("work", "attn", l, (b, kvh, s)))
-            ops.append(("split", ("split", l, b, kvh), ns, ("ctr", l, "attn")))
+            if phase:
+                if ns == 1:
+                    ops.append(("signal", ("ctr", l, "attn"), 1))
+                ops.append(("signal", ("aph", l), 1))
+            else:
+                ops.append(("split", ("split", l, b, kvh), ns, ("ctr", l, "attn")))
+        if phase:
+            ops.append(("wait", ("aph", l), len(items)))
+            for u in range(wg, B * shape.nkv, nwg):
+                if ns_of[u // shape.nkv] > 1:
+                    ops.append(("work", "combine", l, u))
+                    ops.append(("signal", ("ctr", l, "attn"), 1))
     return progs
 
 
@@ -302,6 +320,9 @@ def expected_units(shape, B, pos, nwg, nwaves, Tmax):
                 exp |= {(st, l, u) for u in units}
         items, _ = attn_items(pos, shape.nkv, nwg, Tmax)
         exp |= {("attn", l, (b, kvh, s)) for (b, kvh, s, _, _, _) in items}
+        ns_of = {b: ns for (b, _, _, ns, _, _) in items}
+        if max(ns_of.values()) > 16:
+            exp |= {("combine", l, u) for u in range(B * shape.nkv) if ns_of[u // shape.nkv] > 1}
     for units in stage_units(shape, "lm", B, nwg, nwaves).values():
         exp |= {("lm", shape.L, u) for u in units}
     return exp
@@ -323,11 +344,17 @@ def test_mega_schedule_finishes_and_produces_each_unit_once(B, tile):
     rng = random.Random(1000 + B)
     nwg, nwaves = 12, 8    # a small GPU: 12 CUs, one persistent workgroup each
     for trial in range(6):
-        pos = _positions(rng, B, 0, 300)
-        kern = mega_kernel(TINY, B, pos, nwg, nwaves, Tmax=256, tile=tile)
+        # (long contexts with short tiles in half the trials at small batch:
+        # more than 16 splits per head, so the combine phase runs)
+        long_ctx = trial % 2 == 1 and B <= 5
+        pos = _positions(rng, B, 1500, 3000) if long_ctx else _positions(rng, B, 0, 300)
+        Tmax = 64 if long_ctx else 256
+        kern = mega_kernel(TINY, B, pos, nwg, nwaves, Tmax=Tmax, tile=tile)
         produced = simulate(kern, slots=nwg, rng=rng)
         assert all(c == 1 for c in produced.values())
-        assert set(produced) == expected_units(TINY, B, pos, nwg, nwaves, 256)
+        assert set(produced) == expected_units(TINY, B, pos, nwg, nwaves, Tmax)
+        if long_ctx:
+            assert any(u[0] == "combine" for u in produced)
 
 
 def test_mega_schedule_deadlocks_without_every_workgroup_resident():
@@ -352,11 +379,15 @@ def test_flags_schedule_needs_two_workgroups_per_cu(B, tile):
     rng = random.Random(2000 + B)
     ncu, nwaves = 8, 8
     for trial in range(6):
-        pos = _positions(rng, B, 0, 300)
-        kern = flags_kernels(TINY, B, pos, ncu, nwaves, Tmax=256, tile=tile)
+        long_ctx = trial % 2 == 1 and B <= 5
+        pos = _positions(rng, B, 1500, 3000) if long_ctx else _positions(rng, B, 0, 300)
+        Tmax = 64 if long_ctx else 256
+        kern = flags_kernels(TINY, B, pos, ncu, nwaves, Tmax=Tmax, tile=tile)
         produced = simulate(kern, slots=2 * ncu, rng=rng)
         assert all(c == 1 for c in produced.values())
-        assert set(produced) == expected_units(TINY, B, pos, ncu, nwaves, 256)
+        assert set(produced) == expected_units(TINY, B, pos, ncu, nwaves, Tmax)
+        if long_ctx:
+            assert any(u[0] == "combine" for u in produced)
     dead = 0
     for trial in range(20):
         pos = _positions(rng, B, 0, 300)
