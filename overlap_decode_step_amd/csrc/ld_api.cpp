@@ -447,8 +447,9 @@ static ld_status compute_grids(ld_model* m) {
   const Dims& D = m->D;
   const int maxnb = nb_for_batch(D.max_batch);
   const size_t scratch = scratch_bytes(), best = best_bytes();
+  // whole-kernel wait and persistent modes: one 512-thread workgroup per CU,
+  // whose staging area holds one whole input row of every stage
   const size_t kmax = (size_t)std::max(std::max(D.H, D.I), D.qd) * 4;  // longest staged input row
-  // whole-kernel wait and persistent modes: one 512-thread workgroup per CU
   const uint32_t xcap_full = (uint32_t)((kLdsPerCu - scratch - best) / 256 * 256);
   if (kmax > xcap_full) return fail(m, LD_EINVAL, "input rows longer than the LDS staging area");
   m->xcap_wait = m->xcap_mega = xcap_full;
@@ -461,7 +462,10 @@ static ld_status compute_grids(ld_model* m) {
   m->xcap_flags = (uint32_t)(half - scratch - best);
   const size_t attn_half = attn_smem(D.group, D.d, D.split_len, D.max_splits);
   m->smem_flags = scratch + std::max<size_t>(m->xcap_flags + best, attn_half);
-  m->flags_ok = (kmax <= m->xcap_flags) && (m->smem_flags <= half);
+  // (the stages with a deferred norm stage whole hidden-size rows there; O
+  // and Down may take theirs in column chunks of two blocks)
+  const size_t kmax_flags = std::max((size_t)D.H * 4, (size_t)2 * kKChunkMinBytes);
+  m->flags_ok = (kmax_flags <= m->xcap_flags) && (m->smem_flags <= half);
   for (int nb = 1; nb <= maxnb; nb *= 2) {
     for (int st = 0; st <= kSLm; ++st) {
       const size_t sm = (st == 0) ? m->smem_mega : std::max(m->smem_wait, m->smem_flags);

@@ -456,15 +456,184 @@ __device__ __forceinline__ void gemv_run(const WStream<NR, UC, RowFn>& ws,
   }
 }
 
-// A whole GEMV stage with its own ring.
-template <int NR, int UC, int NB, int PF, int SU = 1, class RowFn, class WaitFn, class Epi>
+// Stage columns [k0, k0 + kn) of batch rows [b0, b0 + nb) into xs with row
+// stride ldx (inputs without gain or norm).  A thread takes the 8-column
+// groups j = tid, tid + blockDim, ... and keeps V groups' loads in flight
+// (V groups of one row, V / 2 of two rows, ..., or one group of V rows)
+// before it stores any.
+template <int NB, int V>
+__device__ __forceinline__ void stage_x_cols(const XSrc& src, int b0, int nb, int k0, int kn,
+                                             int ldx, float* xs) {
+  constexpr int RB = NB < V ? NB : V, U = V / RB;  // rows and groups per round
+  const int n8 = kn >> 3, nth = blockDim.x;
+  for (int j0 = tid(); j0 < n8; j0 += U * nth) {
+    for (int r0 = 0; r0 < nb; r0 += RB) {
+      float v[U][RB][8];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int b = 0; b < RB; ++b)
+          if (r0 + b < nb && j0 + u * nth < n8) src.raw8(b0 + r0 + b, k0 + (j0 + u * nth) * 8, v[u][b]);
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int b = 0; b < RB; ++b)
+          if (r0 + b < nb && j0 + u * nth < n8) {
+            float4* d = reinterpret_cast<float4*>(xs + (int64_t)(r0 + b) * ldx + (j0 + u * nth) * 8);
+            d[0] = make_float4(v[u][b][0], v[u][b][1], v[u][b][2], v[u][b][3]);
+            d[1] = make_float4(v[u][b][4], v[u][b][5], v[u][b][6], v[u][b][7]);
+          }
+    }
+  }
+  __syncthreads();
+}
+
+// K-chunked GEMV: for inputs whose whole rows would not fit the LDS staging
+// area for the batch (gemv_run would then stream the weights once per batch
+// tile), the batch is staged in column chunks of KC (a multiple of a block's
+// UC * kChunk columns) and each wave takes its tasks in groups of G, whose
+// per-lane sums stay in registers from chunk to chunk.  Per chunk, the
+// group's tasks are streamed one after another, each over its blocks in the
+// chunk.  A task's lanes add the same blocks in the same order as in
+// gemv_run (its blocks in increasing column order, then one wave sum), so
+// the results are bitwise the same, but the weights stream once per batch
+// tile of bw rows, where bw * KC fits the staging area rather than bw * K.
+// The stream is a fixed sequence per (group, chunk) segment of G tasks x
+// nbp blocks (the chunk's blocks padded to a multiple of PF with masked
+// ones; missing tasks masked too), the same in every wave, so the chunk
+// restaging barriers line up; the ring of PF blocks runs across segments.
+template <int NR, int UC, int NB, int PF, int G, int V, class RowFn, class WaitFn, class Epi>
+__device__ __forceinline__ void gemv_run_kc(const WStream<NR, UC, RowFn>& ws, int ntile,
+                                            WBlock<NR, UC> (&ring)[PF], const XSrc& src, int B,
+                                            int bw, int KC, const WaitFn& wait, Epi& epi,
+                                            char* smem) {
+  Scratch& sc = *reinterpret_cast<Scratch*>(smem);
+  float* xs = reinterpret_cast<float*>(smem + kScratchBytes);
+  const int lane = lane_id(), wave = wave_id();
+  const int K = ws.K, bpt = ws.bpt;
+  const int bpc = KC / (UC * kChunk);               // blocks per chunk per task
+  const int nkc = (K + KC - 1) / KC;                // chunks
+  const int nbp = (bpc + PF - 1) / PF * PF;         // padded blocks per segment row
+  const int first0 = ws.first - wave;               // the workgroup's wave 0
+  const int ntask0 = first0 < ntile ? (ntile - 1 - first0) / ws.stride + 1 : 0;
+  const int ntask = ws.nblk / bpt;                  // this wave's tasks
+  const int ngr = (ntask0 + G - 1) / G;             // groups (the same in every wave)
+  const int seg = G * nbp, nseq = ngr * nkc * seg;
+  // element e of the sequence -> block of the task-major stream (masked
+  // past the end of a task, a chunk or the wave's tasks)
+  auto block_of = [&](int e) -> int {
+    if (e >= nseq) return ws.nblk;
+    const int gk = e / seg, r = e - gk * seg;
+    const int g = gk / nkc, kc = gk - g * nkc;
+    const int t = r / nbp, cb = r - t * nbp;
+    const int q = g * G + t, bk = kc * bpc + cb;
+    return (q < ntask && cb < bpc && bk < bpt) ? q * bpt + bk : ws.nblk;
+  };
+  const int nbt = (B + bw - 1) / bw;
+  for (int bt = 0; bt < nbt; ++bt) {
+    const int b0 = bt * bw, nb = min(bw, B - b0);
+    if (bt == 0) {
+      // the first blocks before the readiness wait, except in the polling wave
+      if (wave != 0) {
+#pragma unroll
+        for (int j = 0; j < PF; ++j) ws.issue(ring[j], block_of(j), lane);
+      }
+      wait();
+    }
+    if (bt > 0 || wave == 0) {
+#pragma unroll
+      for (int j = 0; j < PF; ++j) ws.issue(ring[j], block_of(j), lane);
+    }
+    for (int g = 0; g < ngr; ++g) {
+      float acc[G][NR][NB];
+#pragma unroll
+      for (int t = 0; t < G; ++t)
+#pragma unroll
+        for (int r = 0; r < NR; ++r)
+#pragma unroll
+          for (int b = 0; b < NB; ++b) acc[t][r][b] = 0.f;
+      for (int kc = 0; kc < nkc; ++kc) {
+        const int k0 = kc * KC;
+        if (bt > 0 || g > 0 || kc > 0) __syncthreads();  // every wave is done with xs
+        stage_x_cols<NB, V>(src, b0, nb, k0, min(KC, K - k0), KC, xs);
+        const float* xk = xs - k0;  // column k of row b at xk[b * KC + k]
+        const int ebase = (g * nkc + kc) * seg;
+#pragma unroll
+        for (int t = 0; t < G; ++t) {
+          for (int c0 = 0; c0 < nbp; c0 += PF) {
+#pragma unroll
+            for (int j = 0; j < PF; ++j) {
+              const int e = ebase + t * nbp + c0 + j;
+              const int blk = block_of(e);
+              if (blk < ws.nblk) ring[j].template fma<NB>(xk, KC, nb, K, (blk % bpt) * UC, lane, acc[t]);
+              ws.issue(ring[j], block_of(e + PF), lane);
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < G; ++t) {
+        const int q = g * G + t;
+        if (q < ntask) {
+#pragma unroll
+          for (int r = 0; r < NR; ++r)
+#pragma unroll
+            for (int b = 0; b < NB; ++b) acc[t][r][b] = wave_sum(acc[t][r][b]);
+          epi(ws.task(q), b0, nb, acc[t], sc);
+        }
+      }
+    }
+  }
+}
+
+// A whole GEMV stage with its own ring.  KCM > 0 and xcap (the LDS staging
+// area's bytes) given: an input without gain or norm may be taken in column
+// chunks (gemv_run_kc) when that needs fewer passes over the weights than
+// whole rows in batch tiles (ties keep whole rows).  A chunk of PF blocks
+// per task keeps the ring full; a chunk of one block (half the ring's slots
+// then masked padding) is used only where it saves a further pass.  KCM = 1
+// (stage kernels held to 128 VGPRs): at most 2 tasks and 2 staged groups in
+// registers; KCM = 2: up to 4 of each.
+template <int NR, int UC, int NB, int PF, int SU = 1, int KCM = 0, class RowFn, class WaitFn,
+          class Epi>
 __device__ __forceinline__ void gemv_stage(const RowFn& rowfn, int ntile, int K,
                                            const uint16_t* wbase, uint32_t wbytes, const XSrc& src,
                                            const uint16_t* gain, bool norm, float eps, int B,
                                            int bw, const WaitFn& wait, Epi& epi, int wg, int nwg,
-                                           char* smem) {
+                                           char* smem, uint32_t xcap = 0) {
   const WStream<NR, UC, RowFn> ws(rowfn, ntile, K, wbase, wbytes, wg, nwg);
   WBlock<NR, UC> ring[PF];
+  if constexpr (KCM > 0) {
+    const int rows = min(B, NB);
+    if (xcap > 0 && gain == nullptr && !norm && (int64_t)K * 4 * rows > (int64_t)xcap) {
+      constexpr int CB = UC * kChunk;  // columns of one block
+      auto passes = [&](int w) { return w > 0 ? (rows + w - 1) / w : 0x7FFF; };
+      const int fitw = (int)(xcap / ((uint32_t)K * 4));
+      const int w2 = min(rows, (int)(xcap / ((uint32_t)PF * CB * 4)));  // chunks of PF blocks
+      const int w1 = min(rows, (int)(xcap / ((uint32_t)CB * 4)));       // chunks of one block
+      int bwk = 0, KC = 0;
+      if (passes(w2) < passes(fitw)) {
+        bwk = w2;
+        KC = min((K + PF * CB - 1) / (PF * CB), (int)(xcap / ((uint32_t)w2 * PF * CB * 4))) * PF * CB;
+      }
+      if (passes(w1) < min(passes(fitw), passes(w2))) {
+        bwk = w1;
+        KC = min((K + CB - 1) / CB, (int)(xcap / ((uint32_t)w1 * CB * 4))) * CB;
+      }
+      if (bwk > 0) {
+        constexpr int GM = KCM == 1 ? 2 : 4, V = KCM == 1 ? 2 : 4;
+        const int first0 = wg * nwaves();
+        const int ntask0 = first0 < ntile ? (ntile - 1 - first0) / (nwg * nwaves()) + 1 : 0;
+        if (ntask0 <= 1)
+          gemv_run_kc<NR, UC, NB, PF, 1, V>(ws, ntile, ring, src, B, bwk, KC, wait, epi, smem);
+        else if (ntask0 <= 2 || GM == 2 || NB > 4)
+          gemv_run_kc<NR, UC, NB, PF, 2, V>(ws, ntile, ring, src, B, bwk, KC, wait, epi, smem);
+        else
+          gemv_run_kc<NR, UC, NB, PF, GM, V>(ws, ntile, ring, src, B, bwk, KC, wait, epi, smem);
+        return;
+      }
+    }
+  }
   gemv_run<NR, UC, NB, PF, SU>(ws, ring, false, src, gain, norm, eps, B, bw, wait, epi, smem);
 }
 

@@ -25,6 +25,12 @@ constexpr int kCtrWords = (kLeaves + 1) * kLeafStride;
 constexpr int kHChunk = 1024;
 constexpr int kMaxTileCtrs = 64;  // kv groups, and chunks, per layer at most
 
+// The norm-free stages of the VALU engine (O, Down) can stage their input in
+// column chunks of whole weight blocks: the staging area must hold at least
+// one such chunk of one row (8 KB-wide blocks of 8 x 512 bf16 columns, fp32
+// inputs); the stages with a deferred norm stage whole rows.
+constexpr int kKChunkMinBytes = 8 * 512 * 4;
+
 // Stage ids (watchdog error codes and schedule bookkeeping).  kSMlpProj is
 // the projection kernel of the unfused-MLP ablation (kernel lookup only).
 enum : int { kSQkv = 1, kSAttn = 2, kSO = 3, kSGu = 4, kSD = 5, kSLm = 6, kSMlpProj = 7 };

@@ -37,6 +37,16 @@ constexpr int kNrD = 1, kUcD = 8, kPfD = 2;
 template <int NB>
 constexpr int kStageGroupsD = NB == 1 ? 4 : 1;
 constexpr int kNrLm = 2, kUcLm = 4, kPfLm = 2;
+// the norm-free stages (O, Down) may take their input in column chunks of
+// whole blocks, which the host sizes the staging area for.  Column chunks
+// in a build (gemv_stage's KCM): none in the persistent kernel's one-row
+// build (the host requires whole input rows to fit a CU's staging area, so
+// one row always does), the register-lean form elsewhere (the full form
+// made the persistent kernel's 2- to 8-row builds spill).
+template <int NB, int MR>
+constexpr int kKcMode = (NB == 1 && MR == kMfmaRingBig) ? 0 : 1;
+static_assert(kUcO * kChunk * 4 <= kKChunkMinBytes && kUcD * kChunk * 4 <= kKChunkMinBytes,
+              "a block's columns must fit the staging area");
 
 __device__ __forceinline__ const uint16_t* layer_w(const Params& P, int l, int64_t off) {
   return P.W.layer0 + (int64_t)l * P.W.layer_stride + off;
@@ -69,6 +79,16 @@ __device__ __forceinline__ int clamp_pos(const Params& P, int b) {
 __device__ __forceinline__ int batch_tile(const Params& P, int K, int NB) {
   const int fit = (int)(P.S.x_cap / ((size_t)K * 4));
   return max(1, min(NB, fit));
+}
+
+// LDS staging bytes of the batch tiles of whole rows the O and SwiGLU stages
+// read (hidden-size and attention-output rows): the persistent kernel keeps
+// SwiGLU weight blocks copied ahead of time above this, so the O stage, even
+// when it takes its input in column chunks, stays below it.
+template <int NB>
+__device__ __forceinline__ size_t row_stage_bytes(const Params& P) {
+  const Dims& D = P.D;
+  return max((size_t)batch_tile(P, D.H, NB) * D.H, (size_t)batch_tile(P, D.qd, NB) * D.qd) * 4;
 }
 
 __device__ __forceinline__ void signal_if(const Params& P, uint32_t* ctr, int who) {
@@ -938,8 +958,9 @@ __device__ __forceinline__ void stage_o(const Params& P, int l, int wg, int nwg,
                                              [](int, int) {}, wg, nwg, smem, sk, false, P.K.ss_b,
                                              D.Ht);
   } else {
-    gemv_stage<NR, UC, NB, kPfO>(rowfn, (rows_total + NR - 1) / NR, K, Wm, wbytes, src, nullptr,
-                                 false, D.eps, B, batch_tile(P, K, NB), wait, epi, wg, nwg, smem);
+    gemv_stage<NR, UC, NB, kPfO, 1, kKcMode<NB, MR>>(rowfn, (rows_total + NR - 1) / NR, K, Wm, wbytes, src, nullptr,
+                                 false, D.eps, B, batch_tile(P, K, NB), wait, epi, wg, nwg, smem,
+                                 (uint32_t)min((size_t)P.S.x_cap, row_stage_bytes<NB>(P)));
     held.flush();
   }
   trace_ev(P, l, kSO, 2, wg);
@@ -992,8 +1013,7 @@ constexpr int kGuBlockBytes = kBlockLdsBytes<2 * kPairsGu, kUcGu>;
 
 template <int NB>
 __device__ __forceinline__ int gu_lds_blocks(const Params& P) {
-  const Dims& D = P.D;
-  const size_t need = max((size_t)batch_tile(P, D.H, NB) * D.H, (size_t)batch_tile(P, D.qd, NB) * D.qd) * 4;
+  const size_t need = row_stage_bytes<NB>(P);
   const size_t room = P.S.x_cap > need ? P.S.x_cap - need : 0;
   return min(kGuLdsBlocks, (int)(room / ((size_t)kGuBlockBytes * nwaves())));
 }
@@ -1322,10 +1342,10 @@ __device__ __forceinline__ void stage_d(const Params& P, int l, int wg, int nwg,
                                              [](int, int) {}, wg, nwg, smem, sk, false, P.K.ss_a,
                                              D.Ht);
   } else {
-    gemv_stage<NR, UC, NB, kPfD, kStageGroupsD<NB>>(rowfn, (rows_total + NR - 1) / NR, K, Wm,
+    gemv_stage<NR, UC, NB, kPfD, kStageGroupsD<NB>, kKcMode<NB, MR>>(rowfn, (rows_total + NR - 1) / NR, K, Wm,
                                                      wbytes, src, nullptr, false, D.eps, B,
                                                      batch_tile(P, K, NB), wait, epi, wg, nwg,
-                                                     smem);
+                                                     smem, P.S.x_cap);
     held.flush();
   }
   trace_ev(P, l, kSD, 2, wg);

@@ -349,19 +349,19 @@ def test_wide_shapes_two_layers(ld, orc, name, w_std, batches):
     # mid-stream) and the MFMA engine's 16-row builds and 64-row builds (the
     # whole-kernel-wait and graph modes run their two-waves-per-SIMD split-K
     # builds there, the tile-flag mode its 32-row passes).  At the 70B width
-    # the tile-flag mode is refused (the Down stage's staged input row, 28672
-    # fp32, does not fit in half the LDS, so two stage kernels cannot share a
-    # CU): that refusal is checked instead.
+    # the tile-flag mode's half of the LDS cannot hold the Down stage's input
+    # row (28672 fp32, which two stage kernels side by side on a
+    # CU): the O and Down stages then take their input in column chunks, each
+    # task's per-lane sums kept across chunks, which is also the path of every
+    # mode wherever a batch's rows do not fit the staging area whole (here
+    # the 70B Down stage from 2 rows, its O stage from 5 and the 8B Down
+    # stage from 3).
     shape = dict(W.SHAPES[name], n_layers=2)
-    modes = MODES if name != "llama70b" else ("wait", "mega", "graph")
+    modes = MODES
     om = _wide_oracle(orc, name, w_std)
     Bmax = max(batches)
     print(f"{name} x2 layers: GPU model", flush=True)
     m = gpu_model(ld, shape, Bmax, 1040, [1024] * Bmax, w_std=w_std)
-    if "flags" not in modes:
-        with pytest.raises(ld.LdError) as ei:
-            m.set_mode("flags")
-        assert ei.value.status == ld.LD_EINVAL
     for B in batches:
         seqs = (0,) if B == 1 else (0, B - 1)
         _check_sampled(ld, orc, m, om, shape, B, [1024] * B, modes, seqs, f"{name} x2", 1040)
@@ -387,8 +387,24 @@ def test_long_context_70b_width(ld, orc):
     m.free()
 
 
+def _flags_splits_match(ld, m, shape, B, pos):
+    """Whether the tile-flag mode's attention splits equal the other modes'
+    for this step.  Below 16 rows every mode starts from the same split
+    length, but the long-context rule (far more items than workgroups) may
+    lengthen it up to each mode's tile area, which is half the LDS in the
+    tile-flag mode: the modes then add different partial sums."""
+    info = ld.ld_launch_info(m.h)
+    half = info["split_len"]
+    T = 64
+    while T < 32 * B and T < half:
+        T *= 2
+    T = min(T, half)
+    need = -(-(sum(p + 1 for p in pos) * shape["n_kv_heads"]) // info["grid_flags"])
+    return need <= T or (need + 31) // 32 * 32 <= half
+
+
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("name,w_std,batches", [("llama8b", 0.02, (1, 2, 16, 64)),
+@pytest.mark.parametrize("name,w_std,batches", [("llama8b", 0.02, (1, 2, 8, 16, 64)),
                                                 ("llama70b", 0.01, (1, 4, 16))])
 def test_full_depth_properties(ld, name, w_std, batches):
     # The Llama-8B (32 layers) and Llama-70B (80 layers, about 141 GB of bf16
@@ -398,7 +414,11 @@ def test_full_depth_properties(ld, name, w_std, batches):
     # argmax of its row with the lowest index on ties, and the modes agree.
     # Below batch 16 (VALU engine: each row's dot product stays in one wave)
     # every mode adds the same numbers in the same order, so they agree
-    # bitwise.  From batch 16 the MFMA engine splits each tile's K steps over
+    # bitwise, except the tile-flag mode where the long-context split rule
+    # gives it shorter attention splits (half the LDS; at KV 1024 from 4 rows
+    # of head_dim 128), which agrees to rounding.  (The batch tiles and the
+    # column chunks of the staged inputs differ between the modes and change
+    # nothing.)  From batch 16 the MFMA engine splits each tile's K steps over
     # a number of waves chosen from the tiles per workgroup, which depends on
     # the mode's grid, so the modes agree to rounding only (relative L2 within
     # 1e-4, a tenth of the bar against the oracle).
@@ -407,7 +427,7 @@ def test_full_depth_properties(ld, name, w_std, batches):
     print(f"{name}: GPU model ({Bmax} sequences)", flush=True)
     m = gpu_model(ld, shape, Bmax, 1040, [1024] * Bmax, w_std=w_std)
     run = GpuRunner(m, shape["vocab"], Bmax)
-    modes = MODES if name != "llama70b" else ("wait", "mega", "graph")
+    modes = MODES
     for B in batches:
         toks = W.first_tokens(B, shape["vocab"])
         outs = {}
@@ -421,14 +441,16 @@ def test_full_depth_properties(ld, name, w_std, batches):
             assert np.array_equal(nx, first), f"{name} B={B} mode={mode}: next token is not the argmax"
             outs[mode] = (lg, nx)
         ref_lg = outs[modes[0]][0]
+        same_splits = _flags_splits_match(ld, m, shape, B, [1024] * B)
         for mode in modes[1:]:
             lg = outs[mode][0]
-            if B < 16:
+            if B < 16 and (mode != "flags" or same_splits):
                 assert np.array_equal(ref_lg, lg), f"{name} B={B}: {mode} differs"
             else:
                 rel = np.linalg.norm(lg - ref_lg) / np.linalg.norm(ref_lg)
                 assert rel <= 1e-4, f"{name} B={B}: {mode} differs (rel L2 {rel:.2e})"
-        how = "bitwise equal" if B < 16 else "equal to rounding"
+        how = ("bitwise equal" if same_splits else "bitwise equal but flags (its splits) to rounding") \
+            if B < 16 else "equal to rounding"
         print(f"{name} B={B}: {'/'.join(modes)} {how}, next = argmax", flush=True)
     m.free()
 
