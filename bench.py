@@ -288,7 +288,7 @@ def tune_tables(shape_name, batches, modes):
     return out
 
 
-def long_generation(batches=(1, 4, 16), prefills=(1024, 16384), modes=("wait", "mega"),
+def long_generation(batches=(1, 4, 16), prefills=(1024, 16384), modes=("wait", "flags", "mega"),
                     steps=4, warmup=2):
     """Long generation at the Llama-70B shape (80 layers, about 141 GB of
     bf16 weights, N(0, 0.01)) on one GPU: every sequence of the batch at KV
