@@ -45,6 +45,11 @@ constexpr int kMfmaTileMats = 2;   // 16-row tiles x matrices a wave accumulates
 // K steps of weight fragments in flight per wave: the persistent kernel has
 // 256 VGPRs per wave, the stage kernels 128
 constexpr int kMfmaRingBig = 8, kMfmaRingSmall = 4;
+// ... but 6 when a wave accumulates 4 batch tiles (64 rows) from LDS
+// fragments: with 8 the 64-row builds spilled (the persistent kernel 50
+// VGPRs, the O stage kernel 19); with 6 they spill 5 and 0, and batch 64 went
+// 3.94 -> 3.79 ms (MEGA) and 4.49 -> 4.35 ms (WAIT) at the Llama-1B shape
+constexpr int kMfmaRing64 = 6;
 constexpr int kMfmaPad = 4;        // 4-byte elements of padding per staged row (16 bytes)
 // Tiles per workgroup at least: a stage with fewer tiles than this many per
 // workgroup runs on ntile / kMfmaMinTiles workgroups, the others skip it.
@@ -213,7 +218,8 @@ __device__ __forceinline__ void mfma_stage(const MatRows& mr, int ntile, int K, 
                                            int ss_ld = 0) {
   constexpr int MT = kMfmaTileMats / NT;  // tiles per wave per tile pass
   constexpr bool DIRECT = SRC == kSrcDirect, FRAG = SRC != kSrcConvert;
-  constexpr int RR = DIRECT ? kDirectRing<NBT, RING> : RING;  // K steps in flight per wave
+  constexpr int RR = DIRECT ? kDirectRing<NBT, RING>                // K steps in flight per wave
+                            : (NBT >= 4 && RING > kMfmaRing64 ? kMfmaRing64 : RING);
   Scratch& sc = *reinterpret_cast<Scratch*>(smem);
   char* xbase = smem + kScratchBytes;
   const int lane = lane_id(), wave = wave_id(), nw = nwaves(), t = tid(), nth = blockDim.x;
