@@ -24,6 +24,11 @@ MFMA engine's tiles per workgroup and K ranges (split K), and the attention
 items per (row, kv head, split) with the split length's long-context rule
 and, past 16 splits per head, the combine phase (every workgroup waits for
 all items, then the combines are dealt to the grid).
+
+The column-chunked staging of the VALU engine's norm-free stages (O, Down)
+is mirrored too: its choice of batch tile and chunk, and the stream of
+(group, chunk) segments, which must consume every block of every task once,
+in column order and inside the staged chunk.
 """
 import random
 
@@ -452,3 +457,86 @@ def test_attention_items_cover_every_position_once(B, lo, hi, max_seq):
                 assert spans[0][0] == 0 and spans[-1][1] == p + 1
                 assert all(a[1] == c[0] for a, c in zip(spans, spans[1:]))
                 assert all(0 < n1 - n0 <= T for n0, n1 in spans)  # fits the LDS tiles
+
+
+# ------------------------------------------- column-chunked GEMV staging
+
+def kc_choice(K, B, NB, xcap, UC, PF):
+    """(batch tile, chunk columns) of the VALU engine's column-chunked staging
+    for a norm-free stage, or None for whole rows (gemv_stage)."""
+    rows = min(B, NB)
+    if K * 4 * rows <= xcap:
+        return None
+    CB = UC * 512
+
+    def passes(w):
+        return -(-rows // w) if w > 0 else 0x7FFF
+    fitw = xcap // (K * 4)
+    w2 = min(rows, xcap // (PF * CB * 4))
+    w1 = min(rows, xcap // (CB * 4))
+    choice = None
+    if passes(w2) < passes(fitw):
+        choice = (w2, min(-(-K // (PF * CB)), xcap // (w2 * PF * CB * 4)) * PF * CB)
+    if passes(w1) < min(passes(fitw), passes(w2)):
+        choice = (w1, min(-(-K // CB), xcap // (w1 * CB * 4)) * CB)
+    return choice
+
+
+def kc_sequence(K, KC, UC, PF, G, ntask, ntask0):
+    """The blocks a wave consumes per (group, chunk) segment, mirroring
+    gemv_run_kc: element e -> (task, block) or None (masked)."""
+    CB = UC * 512
+    bpt = -(-K // CB)
+    bpc = KC // CB
+    nkc = -(-K // KC)
+    nbp = -(-bpc // PF) * PF
+    ngr = -(-ntask0 // G)
+    seg = G * nbp
+    nseq = ngr * nkc * seg
+
+    def block_of(e):
+        if e >= nseq:
+            return None
+        gk, r = divmod(e, seg)
+        g, kc = divmod(gk, nkc)
+        t, cb = divmod(r, nbp)
+        q, bk = g * G + t, kc * bpc + cb
+        return (q, bk, kc) if q < ntask and cb < bpc and bk < bpt else None
+    return [block_of(e) for e in range(nseq)], nseq, seg, bpt
+
+
+@pytest.mark.parametrize("K,UC", [(28672, 8), (14336, 8), (8192, 8), (8192, 4), (4096, 4), (2048, 4)])
+@pytest.mark.parametrize("B", [1, 2, 3, 4, 5, 8, 12, 15])
+@pytest.mark.parametrize("xcap", [74 * 1024, 155 * 1024])
+def test_column_chunks_consume_every_block_once_in_order(K, UC, B, xcap):
+    # every task's blocks once, in increasing column order (the per-lane
+    # addition order of whole-row staging), each within the chunk that is
+    # staged while it is consumed; every wave runs the same number of
+    # elements (the restaging barriers line up) and segments are whole ring
+    # turns (the ring slot of element e is e mod PF)
+    PF = 2
+    NB = 1 if B == 1 else 2 if B == 2 else 4 if B <= 4 else 8
+    ch = kc_choice(K, B, NB, xcap, UC, PF)
+    if ch is None:
+        return
+    bw, KC = ch
+    assert bw >= 1 and KC % (UC * 512) == 0 and bw * KC * 4 <= xcap
+    assert -(-min(B, NB) // bw) < (-(-min(B, NB) // (xcap // (K * 4))) if xcap >= K * 4 else 1 << 30)
+    for G in (1, 2):
+        for ntask0 in (1, 2, 3, 4, 7):
+            lens = set()
+            for ntask in {ntask0, max(0, ntask0 - 1)}:   # waves of a workgroup differ by at most one task
+                seq, nseq, seg, bpt = kc_sequence(K, KC, UC, PF, G, ntask, ntask0)
+                lens.add(nseq)
+                assert seg % PF == 0
+                per_task = {}
+                for e, x in enumerate(seq):
+                    if x is None:
+                        continue
+                    q, bk, kc = x
+                    assert kc * KC <= bk * UC * 512 < (kc + 1) * KC   # inside the staged chunk
+                    per_task.setdefault(q, []).append(bk)
+                assert sorted(per_task) == list(range(ntask))
+                for q, blocks in per_task.items():
+                    assert blocks == list(range(bpt)), (q, blocks)
+            assert len(lens) == 1
