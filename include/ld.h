@@ -16,10 +16,12 @@
  * Kernel Fusion for Transformers", Key points, "Fusion scope").
  *
  * Execution modes (all share the same stage code; below batch 16 they give
- * bitwise-equal results.  From 16 on they agree to rounding: the MFMA
- * engine's split of each tile's K steps over waves depends on the mode's
- * grid, and the tile-flag mode splits attention into shorter KV ranges,
- * since two of its stage kernels share a CU's LDS):
+ * bitwise-equal results, except the tile-flag mode where a long context
+ * lengthens the attention splits past half a CU's tile area.  From 16 on
+ * they agree to rounding: the MFMA engine's split of each tile's K steps
+ * over waves depends on the mode's grid, and the tile-flag mode splits
+ * attention into shorter KV ranges, since two of its stage kernels share a
+ * CU's LDS):
  *   LD_MODE_WAIT  - one kernel per stage on one stream; each kernel starts
  *                   when the previous one has finished (the conventional
  *                   whole-kernel wait of the MegaOps summary, "In plain
@@ -141,6 +143,11 @@ ld_status ld_fill_kv(ld_model* m, uint64_t seed, float kv_std, const int32_t* pr
 ld_status ld_fill_kv_static(ld_model* m, uint64_t seed, float kv_std, const int32_t* prefill_len,
                             void* stream);
 
+/* Select the execution mode for later steps (see the list above).  Returns
+ * LD_EINVAL for an unknown mode, and for LD_MODE_FLAGS when two of its stage
+ * kernels cannot share a CU for this shape (a hidden-size input row, or two
+ * weight blocks' columns of the O and Down stages' column chunks, must fit
+ * half a CU's LDS; no Llama-1B, 8B or 70B configuration is refused). */
 ld_status ld_set_mode(ld_model* m, ld_mode mode);
 
 /* One decode step for `batch` sequences (1 <= batch <= max_batch).
