@@ -138,10 +138,14 @@ __host__ __device__ constexpr int mfma_splits(int ntile, int K, int nwg) {
 // weight fragments (4 VGPRs each) and NBT pairs of 16-byte activation loads
 // (8 VGPRs per batch tile), within kDirectRingVgprs of the 256-VGPR builds
 // and kDirectRingVgprsSmall of the 128-VGPR ones (more spilled registers).
-constexpr int kDirectRingVgprs = 96, kDirectRingVgprsSmall = 56;
+// With one batch tile (16 rows) the 256-VGPR builds take 128, a ring of 8
+// steps: 1-2% faster than 6 at batch 16 (Llama-1B 1.670 -> 1.649 ms MEGA, 8B
+// and 70B likewise), the persistent kernel then spilling one VGPR.
+constexpr int kDirectRingVgprs = 96, kDirectRingVgprs16 = 128, kDirectRingVgprsSmall = 56;
 template <int NBT, int RING>
-constexpr int kDirectRingRaw = (RING == kMfmaRingBig ? kDirectRingVgprs : kDirectRingVgprsSmall) /
-                               (4 * kMfmaTileMats + 8 * NBT);
+constexpr int kDirectRingRaw =
+    (RING == kMfmaRingBig ? (NBT == 1 ? kDirectRingVgprs16 : kDirectRingVgprs) : kDirectRingVgprsSmall) /
+    (4 * kMfmaTileMats + 8 * NBT);
 template <int NBT, int RING>
 constexpr int kDirectRing =
     kDirectRingRaw<NBT, RING> < 2 ? 2 : (kDirectRingRaw<NBT, RING> > RING ? RING : kDirectRingRaw<NBT, RING>);
