@@ -592,8 +592,8 @@ __device__ __forceinline__ void gemv_run_kc(const WStream<NR, UC, RowFn>& ws, in
 // whole rows in batch tiles (ties keep whole rows).  A chunk of PF blocks
 // per task keeps the ring full; a chunk of one block (half the ring's slots
 // then masked padding) is used only where it saves a further pass.  KCM = 1
-// (stage kernels held to 128 VGPRs): at most 2 tasks and 2 staged groups in
-// registers; KCM = 2: up to 4 of each.
+// (the register-lean form every build with the path uses): at most 2 tasks
+// and 2 staged groups in registers; KCM = 2: up to 4 of each.
 template <int NR, int UC, int NB, int PF, int SU = 1, int KCM = 0, class RowFn, class WaitFn,
           class Epi>
 __device__ __forceinline__ void gemv_stage(const RowFn& rowfn, int ntile, int K,
